@@ -1,0 +1,208 @@
+"""Python binding of libgdn.so: the Gated DeltaNet recurrence on MI355X (gfx950).
+
+Thin ctypes wrappers with the same names as the C ABI in include/gdn.h. They check that
+tensors are contiguous CUDA (HIP) tensors of the right dtype, allocate outputs and the
+workspace with torch when the caller does not pass them, and hand raw device pointers and
+the current stream to the library. Every step of the computation runs in the library's
+HIP kernels; there is no Python or CPU fallback, and a missing libgdn.so is an error.
+
+Layouts (see include/gdn.h): q, k [n, t, h_qk, d]; v [n, t, h_v, d]; g, beta [n, t, h_v]
+fp32; state [n, h_v, d, d] fp32 with element [i][j] = S[j][i]; out [n, t, h_v, d] fp32.
+"""
+import ctypes
+import os
+
+import torch
+
+__all__ = [
+    "GdnError", "gdn_abi_version", "gdn_status_str", "gdn_workspace_bytes",
+    "gdn_prefill_chunked", "gdn_prefill_scan", "gdn_decode_step", "gdn_prefill_choose",
+    "gdn_prefill", "gdn_prefill_workspace_bytes", "library_path", "Dims",
+]
+
+GDN_F32, GDN_BF16 = 0, 1
+_DTYPES = {torch.float32: GDN_F32, torch.bfloat16: GDN_BF16}
+_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libgdn.so")
+_lib = None
+
+
+class Dims(ctypes.Structure):
+    """gdn_dims from include/gdn.h."""
+    _fields_ = [("n", ctypes.c_int64), ("t", ctypes.c_int64), ("h_qk", ctypes.c_int32),
+                ("h_v", ctypes.c_int32), ("d_k", ctypes.c_int32), ("d_v", ctypes.c_int32),
+                ("qkv_dtype", ctypes.c_int32), ("l2_eps", ctypes.c_float)]
+
+
+class GdnError(RuntimeError):
+    def __init__(self, status: int, where: str):
+        self.status = status
+        super().__init__(f"{where}: {gdn_status_str(status)}")
+
+
+def library_path() -> str:
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError(f"{_LIB_PATH} is not built; run __graft_entry__.build() "
+                           "(the HIP library is required, there is no fallback)")
+    lib = ctypes.CDLL(_LIB_PATH)
+    P, D = ctypes.c_void_p, ctypes.POINTER(Dims)
+    i32, sz = ctypes.c_int32, ctypes.c_size_t
+    sig = {
+        "gdn_abi_version": (i32, []),
+        "gdn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "gdn_workspace_bytes": (sz, [D, i32]),
+        "gdn_prefill_chunked": (ctypes.c_int, [D, i32] + [P] * 9 + [sz, P]),
+        "gdn_prefill_scan": (ctypes.c_int, [D] + [P] * 9 + [sz, P]),
+        "gdn_decode_step": (ctypes.c_int, [D] + [P] * 9),
+        "gdn_prefill_choose": (ctypes.c_int, [D, ctypes.POINTER(i32)]),
+        "gdn_prefill_workspace_bytes": (sz, [D]),
+        "gdn_prefill": (ctypes.c_int, [D] + [P] * 9 + [sz, P]),
+    }
+    for name, (res, args) in sig.items():
+        f = getattr(lib, name)
+        f.restype, f.argtypes = res, args
+    _lib = lib
+    return lib
+
+
+def gdn_abi_version() -> int:
+    return _load().gdn_abi_version()
+
+
+def gdn_status_str(status: int) -> str:
+    return _load().gdn_status_str(int(status)).decode()
+
+
+def _check(status: int, where: str):
+    if status != 0:
+        raise GdnError(status, where)
+
+
+def make_dims(n, t, h_qk, h_v, d, dtype=torch.bfloat16, l2_eps=1e-6) -> Dims:
+    return Dims(int(n), int(t), int(h_qk), int(h_v), int(d), int(d),
+                _DTYPES.get(dtype, -1), float(l2_eps))
+
+
+def _dims_of(q, v, l2_eps) -> Dims:
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [n, t, h_qk, d] and v [n, t, h_v, d]")
+    n, t, h_qk, d_k = q.shape
+    d = Dims(n, t, h_qk, v.shape[2], d_k, v.shape[3], _DTYPES.get(q.dtype, -1), float(l2_eps))
+    return d
+
+
+def _ptr(x):
+    return None if x is None else ctypes.c_void_p(x.data_ptr())
+
+
+def _stream(device, stream):
+    s = stream if stream is not None else torch.cuda.current_stream(device)
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps):
+    tensors = [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)]
+    if state_in is not None:
+        tensors.append(("state_in", state_in))
+    dev = q.device
+    for name, x in tensors:
+        if not x.is_cuda or x.device != dev:
+            raise ValueError(f"{name} must be a CUDA (HIP) tensor on {dev}")
+        if not x.is_contiguous():
+            raise ValueError(f"{name} must be contiguous")
+    if k.dtype != q.dtype or v.dtype != q.dtype or q.dtype not in _DTYPES:
+        raise ValueError("q, k, v must share one dtype, bfloat16 or float32")
+    for name, x in (("g", g), ("beta", beta), ("state_in", state_in)):
+        if x is not None and x.dtype != torch.float32:
+            raise ValueError(f"{name} must be float32")
+    dims = _dims_of(q, v, l2_eps)
+    n, t, _, d = q.shape
+    h_v = v.shape[2]
+    if out is None:
+        out = torch.empty((n, t, h_v, d), device=dev, dtype=torch.float32)
+    if state_out is None:
+        state_out = torch.empty((n, h_v, d, d), device=dev, dtype=torch.float32)
+    return dims, out, state_out
+
+
+def _workspace(dims, chunk, workspace, dev):
+    need = _load().gdn_workspace_bytes(ctypes.byref(dims), int(chunk))
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, device=dev, dtype=torch.uint8)
+    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    return workspace, nbytes
+
+
+def gdn_workspace_bytes(n, t, h_qk, h_v, d, dtype=torch.bfloat16, chunk=64) -> int:
+    """Workspace bytes for gdn_prefill_chunked (chunk > 0) or gdn_prefill_scan (chunk 0)."""
+    return _load().gdn_workspace_bytes(ctypes.byref(make_dims(n, t, h_qk, h_v, d, dtype)),
+                                       int(chunk))
+
+
+def gdn_prefill_chunked(q, k, v, g, beta, state_in=None, *, chunk=64, l2_eps=1e-6, out=None,
+                        state_out=None, workspace=None, stream=None):
+    """Chunked prefill. Returns (out, state_out)."""
+    dims, out, state_out = _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps)
+    workspace, wbytes = _workspace(dims, chunk, workspace, q.device)
+    _check(_load().gdn_prefill_chunked(
+        ctypes.byref(dims), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace), wbytes,
+        _stream(q.device, stream)), "gdn_prefill_chunked")
+    return out, state_out
+
+
+def gdn_prefill_scan(q, k, v, g, beta, state_in=None, *, l2_eps=1e-6, out=None,
+                     state_out=None, workspace=None, stream=None):
+    """Direct-scan prefill. Returns (out, state_out)."""
+    dims, out, state_out = _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps)
+    workspace, wbytes = _workspace(dims, 0, workspace, q.device)
+    _check(_load().gdn_prefill_scan(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+        _ptr(out), _ptr(state_out), _ptr(workspace), wbytes, _stream(q.device, stream)),
+        "gdn_prefill_scan")
+    return out, state_out
+
+
+def gdn_decode_step(q, k, v, g, beta, state_in=None, *, l2_eps=1e-6, out=None,
+                    state_out=None, stream=None):
+    """One decode token per sequence (t == 1). Returns (out, state_out); pass
+    state_out=state_in to update the state in place."""
+    dims, out, state_out = _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps)
+    _check(_load().gdn_decode_step(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+        _ptr(out), _ptr(state_out), _stream(q.device, stream)), "gdn_decode_step")
+    return out, state_out
+
+
+def gdn_prefill_choose(t, h_qk=16, h_v=32, d=128, n=1, dtype=torch.bfloat16) -> int:
+    """The measured scan/chunk choice: 0 for the direct scan, else a chunk size."""
+    res = ctypes.c_int32(-1)
+    _check(_load().gdn_prefill_choose(ctypes.byref(make_dims(n, t, h_qk, h_v, d, dtype)),
+                                      ctypes.byref(res)), "gdn_prefill_choose")
+    return res.value
+
+
+def gdn_prefill_workspace_bytes(n, t, h_qk, h_v, d, dtype=torch.bfloat16) -> int:
+    return _load().gdn_prefill_workspace_bytes(ctypes.byref(make_dims(n, t, h_qk, h_v, d, dtype)))
+
+
+def gdn_prefill(q, k, v, g, beta, state_in=None, *, l2_eps=1e-6, out=None, state_out=None,
+                workspace=None, stream=None):
+    """Prefill with the method gdn_prefill_choose picks. Returns (out, state_out)."""
+    dims, out, state_out = _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps)
+    if workspace is None:
+        need = _load().gdn_prefill_workspace_bytes(ctypes.byref(dims))
+        if need > 0:
+            workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
+    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check(_load().gdn_prefill(
+        ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+        _ptr(out), _ptr(state_out), _ptr(workspace), wbytes, _stream(q.device, stream)),
+        "gdn_prefill")
+    return out, state_out

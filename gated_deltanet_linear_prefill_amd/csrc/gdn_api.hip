@@ -1,0 +1,283 @@
+// gdn_api.hip -- the C ABI of libgdn.so (declared and documented in include/gdn.h):
+// host-side validation, workspace sizing, method choice and kernel dispatch.
+//
+// Every check runs on the host before the first HIP call, so each error path is testable
+// without a GPU, and on error nothing is enqueued.
+#include <math.h>
+#include <string.h>
+
+#include "gdn_internal.hpp"
+
+namespace gdn {
+namespace {
+
+#include "gdn_crossover.inc"  // kCrossover[]: measured scan/chunk choice by length
+
+struct Range {
+    uintptr_t lo, hi;  // [lo, hi); empty when lo == hi
+};
+
+bool overlap(Range a, Range b)
+{
+    return a.lo < a.hi && b.lo < b.hi && a.lo < b.hi && b.lo < a.hi;
+}
+
+bool mul_ok(int64_t a, int64_t b, int64_t* r)
+{
+    return !__builtin_mul_overflow(a, b, r);
+}
+
+bool supported_d(int32_t d)
+{
+    return d == 16 || d == 32 || d == 64 || d == 128;
+}
+
+bool supported_chunk(int32_t c)
+{
+    return c == 16 || c == 32 || c == 64 || c == 128;
+}
+
+// Element counts of every tensor, or false on overflow. Sizes are bounded so that every
+// byte offset fits in int64 and every grid dimension in 31 bits.
+struct Sizes {
+    int64_t qk, v, gb, state, out;  // elements
+    size_t esize;                   // bytes per q/k/v element
+};
+
+gdn_status check_dims(const gdn_dims* d, Sizes* s)
+{
+    if (!d) return GDN_ERR_NULL;
+    if (d->n < 0 || d->t < 0 || d->h_qk <= 0 || d->h_v <= 0 || d->d_k <= 0 || d->d_v <= 0)
+        return GDN_ERR_SHAPE;
+    if (d->h_v % d->h_qk != 0) return GDN_ERR_SHAPE;
+    if (!(d->l2_eps >= 0.0f) || !isfinite(d->l2_eps)) return GDN_ERR_SHAPE;
+    if (d->qkv_dtype != GDN_F32 && d->qkv_dtype != GDN_BF16) return GDN_ERR_UNSUPPORTED;
+    if (d->d_k != d->d_v || !supported_d(d->d_k)) return GDN_ERR_UNSUPPORTED;
+    const int64_t D = d->d_k;
+    int64_t nt, a;
+    if (!mul_ok(d->n, d->t, &nt)) return GDN_ERR_SHAPE;
+    if (!mul_ok(nt, d->h_qk, &a) || !mul_ok(a, D, &s->qk)) return GDN_ERR_SHAPE;
+    if (!mul_ok(nt, d->h_v, &s->gb) || !mul_ok(s->gb, D, &s->v)) return GDN_ERR_SHAPE;
+    s->out = s->v;
+    if (!mul_ok(d->n, d->h_v, &a) || !mul_ok(a, D * D, &s->state)) return GDN_ERR_SHAPE;
+    // Keep every byte count (fp32 outputs are the largest) and grid size well inside range.
+    const int64_t lim = INT64_C(1) << 60;
+    if (s->out > lim / 4 || s->state > lim / 4 || s->qk > lim / 4) return GDN_ERR_SHAPE;
+    if (d->n * (int64_t)d->h_v >= (INT64_C(1) << 31)) return GDN_ERR_SHAPE;
+    if (d->t >= (INT64_C(1) << 40)) return GDN_ERR_SHAPE;
+    s->esize = d->qkv_dtype == GDN_BF16 ? 2 : 4;
+    return GDN_OK;
+}
+
+Range range_of(const void* p, int64_t elems, size_t esize)
+{
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, p ? lo + (uintptr_t)elems * esize : lo};
+}
+
+bool aligned(const void* p, uintptr_t a)
+{
+    return (reinterpret_cast<uintptr_t>(p) & (a - 1)) == 0;
+}
+
+size_t workspace_for(const gdn_dims* d, int32_t chunk)
+{
+    if (d->t == 0 || d->n == 0) return 0;
+    return chunk == 0 ? scan_workspace_bytes(d->n, d->t, d->h_qk, d->h_v, d->d_k)
+                      : chunked_workspace_bytes(d->n, d->t, d->h_qk, d->h_v, d->d_k, chunk);
+}
+
+// Validate one call; `mode` 0 = scan, >0 = chunk size, -1 = decode (no workspace).
+gdn_status validate(const gdn_dims* d, int32_t mode, const void* q, const void* k,
+                    const void* v, const float* g, const float* beta, const float* state_in,
+                    float* out, float* state_out, void* ws, size_t ws_bytes, Call* call)
+{
+    Sizes s;
+    gdn_status st = check_dims(d, &s);
+    if (st != GDN_OK) return st;
+    if (mode > 0 && !supported_chunk(mode)) return GDN_ERR_UNSUPPORTED;
+    if (mode == -1 && d->t != 1) return GDN_ERR_SHAPE;
+
+    const bool work = d->n > 0;
+    const bool tokens = work && d->t > 0;
+    if (work && !state_out) return GDN_ERR_NULL;
+    if (tokens && (!q || !k || !v || !g || !beta || !out)) return GDN_ERR_NULL;
+
+    const void* al16[] = {q, k, v, state_in, out, state_out, ws};
+    for (const void* p : al16)
+        if (p && !aligned(p, 16)) return GDN_ERR_ALIGN;
+    if ((g && !aligned(g, 4)) || (beta && !aligned(beta, 4))) return GDN_ERR_ALIGN;
+
+    size_t need = 0;
+    if (mode >= 0 && tokens) need = workspace_for(d, mode);
+    if (need > 0 && (!ws || ws_bytes < need)) return GDN_ERR_WORKSPACE;
+
+    if (work) {
+        const int64_t tq = tokens ? s.qk : 0, tv = tokens ? s.v : 0, tg = tokens ? s.gb : 0;
+        const Range r_q = range_of(q, tq, s.esize), r_k = range_of(k, tq, s.esize);
+        const Range r_v = range_of(v, tv, s.esize);
+        const Range r_g = range_of(g, tg, 4), r_b = range_of(beta, tg, 4);
+        const Range r_si = range_of(state_in, state_in ? s.state : 0, 4);
+        const Range r_o = range_of(out, tv, 4), r_so = range_of(state_out, s.state, 4);
+        const Range r_w = range_of(ws, (int64_t)need, 1);
+        const Range inputs[] = {r_q, r_k, r_v, r_g, r_b};
+        const Range outputs[] = {r_o, r_so, r_w};
+        for (int i = 0; i < 3; ++i) {
+            for (const Range& in : inputs)
+                if (overlap(outputs[i], in)) return GDN_ERR_ALIAS;
+            for (int j = i + 1; j < 3; ++j)
+                if (overlap(outputs[i], outputs[j])) return GDN_ERR_ALIAS;
+            // state_in may be state_out exactly (in place); any other overlap is an alias.
+            if (overlap(outputs[i], r_si) && !(i == 1 && state_in == state_out))
+                return GDN_ERR_ALIAS;
+        }
+    }
+
+    *call = Call{d->n, d->t, d->h_qk, d->h_v, d->d_k, d->qkv_dtype, d->l2_eps,
+                 q, k, v, g, beta, state_in, out, state_out, ws, ws_bytes, nullptr};
+    return GDN_OK;
+}
+
+gdn_status finish(hipError_t e)
+{
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
+}
+
+// Copy (or zero) the state for an empty segment, t == 0.
+__global__ void state_passthrough_kernel(const float4* __restrict__ src, float4* __restrict__ dst,
+                                         int64_t n4)
+{
+    for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n4;
+         i += (int64_t)gridDim.x * blockDim.x)
+        dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
+}
+
+int32_t choose_chunk(const gdn_dims* d)
+{
+    int32_t pick = kCrossover[0].chunk;
+    for (const auto& e : kCrossover)
+        if (d->t >= e.min_t) pick = e.chunk;
+    return pick;
+}
+
+}  // namespace
+
+hipError_t launch_state_passthrough(const Call& c)
+{
+    if (c.state_in == c.state_out) return hipSuccess;
+    const int64_t n4 = c.n * c.h_v * (int64_t)c.d * c.d / 4;
+    int64_t blocks = (n4 + 255) / 256;
+    if (blocks > 4096) blocks = 4096;
+    hipLaunchKernelGGL(state_passthrough_kernel, dim3((unsigned)blocks), dim3(256), 0, c.stream,
+                       reinterpret_cast<const float4*>(c.state_in),
+                       reinterpret_cast<float4*>(c.state_out), n4);
+    return hipGetLastError();
+}
+
+}  // namespace gdn
+
+using namespace gdn;
+
+extern "C" {
+
+int32_t gdn_abi_version(void)
+{
+    return GDN_ABI_VERSION;
+}
+
+const char* gdn_status_str(gdn_status s)
+{
+    switch (s) {
+        case GDN_OK: return "GDN_OK: success";
+        case GDN_ERR_NULL: return "GDN_ERR_NULL: a required pointer is NULL";
+        case GDN_ERR_SHAPE: return "GDN_ERR_SHAPE: invalid sizes or scalar arguments";
+        case GDN_ERR_UNSUPPORTED: return "GDN_ERR_UNSUPPORTED: head dim, chunk size or dtype not supported";
+        case GDN_ERR_ALIGN: return "GDN_ERR_ALIGN: a pointer is misaligned";
+        case GDN_ERR_ALIAS: return "GDN_ERR_ALIAS: an output overlaps another buffer";
+        case GDN_ERR_WORKSPACE: return "GDN_ERR_WORKSPACE: workspace missing or too small";
+        case GDN_ERR_HIP: return "GDN_ERR_HIP: the HIP runtime reported an error";
+    }
+    return "GDN_ERR_?: unknown status";
+}
+
+size_t gdn_workspace_bytes(const gdn_dims* d, int32_t chunk)
+{
+    Sizes s;
+    if (check_dims(d, &s) != GDN_OK) return 0;
+    if (chunk != 0 && !supported_chunk(chunk)) return 0;
+    return workspace_for(d, chunk);
+}
+
+gdn_status gdn_prefill_chunked(const gdn_dims* d, int32_t chunk, const void* q, const void* k,
+                               const void* v, const float* g, const float* beta,
+                               const float* state_in, float* out, float* state_out,
+                               void* ws, size_t ws_bytes, void* stream)
+{
+    if (d && !supported_chunk(chunk)) return GDN_ERR_UNSUPPORTED;
+    Call c;
+    gdn_status st = validate(d, chunk, q, k, v, g, beta, state_in, out, state_out, ws, ws_bytes, &c);
+    if (st != GDN_OK) return st;
+    if (c.n == 0) return GDN_OK;
+    c.stream = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();  // report only errors raised by this call's launches
+    return finish(c.t == 0 ? launch_state_passthrough(c) : launch_chunked(c, chunk));
+}
+
+gdn_status gdn_prefill_scan(const gdn_dims* d, const void* q, const void* k, const void* v,
+                            const float* g, const float* beta, const float* state_in,
+                            float* out, float* state_out, void* ws, size_t ws_bytes,
+                            void* stream)
+{
+    Call c;
+    gdn_status st = validate(d, 0, q, k, v, g, beta, state_in, out, state_out, ws, ws_bytes, &c);
+    if (st != GDN_OK) return st;
+    if (c.n == 0) return GDN_OK;
+    c.stream = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return finish(c.t == 0 ? launch_state_passthrough(c) : launch_scan(c));
+}
+
+gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, const void* v,
+                           const float* g, const float* beta, const float* state_in,
+                           float* out, float* state_out, void* stream)
+{
+    Call c;
+    gdn_status st = validate(d, -1, q, k, v, g, beta, state_in, out, state_out, nullptr, 0, &c);
+    if (st != GDN_OK) return st;
+    if (c.n == 0) return GDN_OK;
+    c.stream = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return finish(launch_decode(c));
+}
+
+gdn_status gdn_prefill_choose(const gdn_dims* d, int32_t* chunk_or_zero)
+{
+    Sizes s;
+    if (!chunk_or_zero) return GDN_ERR_NULL;
+    gdn_status st = check_dims(d, &s);
+    if (st != GDN_OK) return st;
+    *chunk_or_zero = choose_chunk(d);
+    return GDN_OK;
+}
+
+size_t gdn_prefill_workspace_bytes(const gdn_dims* d)
+{
+    Sizes s;
+    if (check_dims(d, &s) != GDN_OK) return 0;
+    return workspace_for(d, choose_chunk(d));
+}
+
+gdn_status gdn_prefill(const gdn_dims* d, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const float* state_in, float* out,
+                       float* state_out, void* ws, size_t ws_bytes, void* stream)
+{
+    int32_t chunk = 0;
+    gdn_status st = gdn_prefill_choose(d, &chunk);
+    if (st != GDN_OK) return st;
+    return chunk == 0 ? gdn_prefill_scan(d, q, k, v, g, beta, state_in, out, state_out, ws,
+                                         ws_bytes, stream)
+                      : gdn_prefill_chunked(d, chunk, q, k, v, g, beta, state_in, out,
+                                            state_out, ws, ws_bytes, stream);
+}
+
+}  // extern "C"

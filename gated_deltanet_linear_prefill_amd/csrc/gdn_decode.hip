@@ -1,0 +1,168 @@
+// gdn_decode.hip -- batch-1 decode step of the Gated DeltaNet recurrence (t == 1).
+//
+// "Optimizing on-device inference for Apple Silicon", section "Decode: minimise bytes
+// moved per token": at batch 1 the step is bound by the bytes it moves, and the recurrent
+// update is fused with its normalisation (here the L2 normalisation of q and k). On
+// MI355X the bytes are the fp32 state: every (sequence, V head) state is read from HBM
+// once and written back once, with 128-bit coalesced accesses.
+//
+// One workgroup per (sequence, V head). With the state stored d_k-major (M = S^T,
+// M[i][j] = S[j][i]), value channel j is column j of M and evolves on its own:
+//   s_k = khat . m_j,  s_q = qhat . m_j,  c_j = beta (v_j - alpha s_k)
+//   o_j = alpha s_q + c_j (qhat . khat),   m_j <- alpha m_j + c_j khat
+// which is S_t = alpha S_{t-1}(I - beta khat khat^T) + beta v khat^T and o = S_t qhat
+// written per column. Thread (rg, cg) holds columns 4cg..4cg+3 of rows rg, rg+RG, ...:
+// each load/store instruction of a wave covers whole contiguous rows of M.
+#include "gdn_internal.hpp"
+
+namespace gdn {
+namespace {
+
+template <int D>
+struct DecodeCfg {
+    static constexpr int NT = (D * D / 4 >= 256) ? 256 : D * D / 4;  // threads
+    static constexpr int CG = D / 4;                                 // float4 per row
+    static constexpr int RG = NT / CG;                               // row groups
+    static constexpr int RPT = D / RG;                               // rows per thread
+    static_assert(RG * RPT == D && CG * RG == NT, "decode tiling");
+};
+
+template <int D, typename TIn>
+__global__ void __launch_bounds__(DecodeCfg<D>::NT)
+decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+              const float* __restrict__ g, const float* __restrict__ beta,
+              const float* state_in, float* __restrict__ out, float* state_out, int h_qk,
+              int h_v, float eps)
+{
+    using Cfg = DecodeCfg<D>;
+    constexpr int CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT;
+    __shared__ float s_q[D], s_k[D], s_norm[3];
+    __shared__ float4 s_part[RG][CG][2];
+
+    const int64_t nh = blockIdx.x;  // sequence * h_v + V head
+    const int64_t seq = nh / h_v;
+    const int h = (int)(nh - seq * h_v);
+    const int hq = h / (h_v / h_qk);
+    const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
+    const int64_t sbase = nh * (int64_t)D * D;
+
+    // 1. Issue the state loads first: they are the bytes that bound the step.
+    float4 m[RPT];
+    if (state_in) {
+#pragma unroll
+        for (int r = 0; r < RPT; ++r)
+            m[r] = *reinterpret_cast<const float4*>(state_in + sbase + (int64_t)(rg + RG * r) * D + 4 * cg);
+    } else {
+#pragma unroll
+        for (int r = 0; r < RPT; ++r) m[r] = make_float4(0.f, 0.f, 0.f, 0.f);
+    }
+
+    // 2. This token's q, k (shared QK head), v slice, gate and write strength.
+    const int64_t qk_off = (seq * h_qk + hq) * (int64_t)D;
+    if (tid < D) {
+        s_q[tid] = load1_f32(q + qk_off + tid);
+        s_k[tid] = load1_f32(k + qk_off + tid);
+    }
+    const float4 vv = load4_f32(v + nh * (int64_t)D + 4 * cg);
+    const float alpha = expf(g[nh]);
+    const float b = beta[nh];
+    __syncthreads();
+
+    // 3. L2 norms and qhat . khat (wave 0), fused here instead of a separate pass.
+    if (tid < 64) {
+        float qq = 0.f, kk = 0.f, qk = 0.f;
+        for (int i = tid; i < D; i += 64) {
+            qq += s_q[i] * s_q[i];
+            kk += s_k[i] * s_k[i];
+            qk += s_q[i] * s_k[i];
+        }
+        qq = wave_sum(qq);
+        kk = wave_sum(kk);
+        qk = wave_sum(qk);
+        if (tid == 0) {
+            const float rq = 1.0f / sqrtf(qq + eps), rk = 1.0f / sqrtf(kk + eps);
+            s_norm[0] = rq;
+            s_norm[1] = rk;
+            s_norm[2] = qk * rq * rk;
+        }
+    }
+
+    // 4. Partial k . m_j and q . m_j over this thread's rows (raw q, k; scaled below).
+    __syncthreads();
+    float4 pk = make_float4(0.f, 0.f, 0.f, 0.f), pq = pk;
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const float ki = s_k[rg + RG * r], qi = s_q[rg + RG * r];
+        pk.x += ki * m[r].x; pk.y += ki * m[r].y; pk.z += ki * m[r].z; pk.w += ki * m[r].w;
+        pq.x += qi * m[r].x; pq.y += qi * m[r].y; pq.z += qi * m[r].z; pq.w += qi * m[r].w;
+    }
+    s_part[rg][cg][0] = pk;
+    s_part[rg][cg][1] = pq;
+    __syncthreads();
+
+    // 5. Column sums (fixed order, so the result is deterministic), output, update.
+    float4 tk = make_float4(0.f, 0.f, 0.f, 0.f), tq = tk;
+#pragma unroll
+    for (int j = 0; j < RG; ++j) {
+        const float4 a = s_part[j][cg][0], c = s_part[j][cg][1];
+        tk.x += a.x; tk.y += a.y; tk.z += a.z; tk.w += a.w;
+        tq.x += c.x; tq.y += c.y; tq.z += c.z; tq.w += c.w;
+    }
+    const float rq = s_norm[0], rk = s_norm[1], qkh = s_norm[2];
+    const float ak = alpha * rk, aq = alpha * rq;
+    float4 c;
+    c.x = b * (vv.x - ak * tk.x);
+    c.y = b * (vv.y - ak * tk.y);
+    c.z = b * (vv.z - ak * tk.z);
+    c.w = b * (vv.w - ak * tk.w);
+    if (rg == 0) {
+        float4 o;
+        o.x = aq * tq.x + c.x * qkh;
+        o.y = aq * tq.y + c.y * qkh;
+        o.z = aq * tq.z + c.z * qkh;
+        o.w = aq * tq.w + c.w * qkh;
+        *reinterpret_cast<float4*>(out + nh * (int64_t)D + 4 * cg) = o;
+    }
+#pragma unroll
+    for (int r = 0; r < RPT; ++r) {
+        const float khi = s_k[rg + RG * r] * rk;
+        float4 u;
+        u.x = alpha * m[r].x + c.x * khi;
+        u.y = alpha * m[r].y + c.y * khi;
+        u.z = alpha * m[r].z + c.z * khi;
+        u.w = alpha * m[r].w + c.w * khi;
+        *reinterpret_cast<float4*>(state_out + sbase + (int64_t)(rg + RG * r) * D + 4 * cg) = u;
+    }
+}
+
+template <int D, typename TIn>
+hipError_t launch_decode_t(const Call& c)
+{
+    const int64_t blocks = c.n * c.h_v;
+    hipLaunchKernelGGL((decode_kernel<D, TIn>), dim3((unsigned)blocks), dim3(DecodeCfg<D>::NT), 0,
+                       c.stream, static_cast<const TIn*>(c.q), static_cast<const TIn*>(c.k),
+                       static_cast<const TIn*>(c.v), c.g, c.beta, c.state_in, c.out,
+                       c.state_out, c.h_qk, c.h_v, c.eps);
+    return hipGetLastError();
+}
+
+template <typename TIn>
+hipError_t dispatch_d(const Call& c)
+{
+    switch (c.d) {
+        case 16: return launch_decode_t<16, TIn>(c);
+        case 32: return launch_decode_t<32, TIn>(c);
+        case 64: return launch_decode_t<64, TIn>(c);
+        case 128: return launch_decode_t<128, TIn>(c);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+}  // namespace
+
+hipError_t launch_decode(const Call& c)
+{
+    return c.dtype == GDN_BF16 ? dispatch_d<uint16_t>(c) : dispatch_d<float>(c);
+}
+
+}  // namespace gdn

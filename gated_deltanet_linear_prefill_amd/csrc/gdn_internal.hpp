@@ -1,0 +1,83 @@
+// gdn_internal.hpp -- shared host/device pieces of libgdn.so (not part of the C ABI).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stddef.h>
+#include <stdint.h>
+
+#include "gdn.h"
+
+namespace gdn {
+
+// A validated call: sizes checked, pointers non-null where required, aligned, disjoint.
+struct Call {
+    int64_t n, t;
+    int32_t h_qk, h_v, d;
+    int32_t dtype;  // gdn_dtype of q, k, v
+    float eps;
+    const void *q, *k, *v;
+    const float *g, *beta, *state_in;
+    float *out, *state_out;
+    void* ws;
+    size_t ws_bytes;
+    hipStream_t stream;
+};
+
+// Kernel launchers, one per translation unit. Each returns hipGetLastError() after its
+// launches. The caller has validated everything the kernels assume.
+hipError_t launch_decode(const Call& c);
+hipError_t launch_scan(const Call& c);
+hipError_t launch_chunked(const Call& c, int chunk);
+hipError_t launch_state_passthrough(const Call& c);  // t == 0: state_out = state_in or 0
+
+size_t scan_workspace_bytes(int64_t n, int64_t t, int32_t h_qk, int32_t h_v, int32_t d);
+size_t chunked_workspace_bytes(int64_t n, int64_t t, int32_t h_qk, int32_t h_v, int32_t d,
+                               int chunk);
+
+// ---------------------------------------------------------------- device helpers
+__device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16)
+{
+    return __uint_as_float(bits16 << 16);
+}
+
+// Four consecutive q/k/v elements as fp32 (an 8-byte load for bf16, 16 bytes for fp32).
+template <typename TIn>
+__device__ __forceinline__ float4 load4_f32(const TIn* p);
+
+template <>
+__device__ __forceinline__ float4 load4_f32<float>(const float* p)
+{
+    return *reinterpret_cast<const float4*>(p);
+}
+
+template <>
+__device__ __forceinline__ float4 load4_f32<uint16_t>(const uint16_t* p)
+{
+    const uint2 u = *reinterpret_cast<const uint2*>(p);
+    return make_float4(bf16_bits_to_f32(u.x & 0xffffu), bf16_bits_to_f32(u.x >> 16),
+                       bf16_bits_to_f32(u.y & 0xffffu), bf16_bits_to_f32(u.y >> 16));
+}
+
+template <typename TIn>
+__device__ __forceinline__ float load1_f32(const TIn* p);
+
+template <>
+__device__ __forceinline__ float load1_f32<float>(const float* p)
+{
+    return *p;
+}
+
+template <>
+__device__ __forceinline__ float load1_f32<uint16_t>(const uint16_t* p)
+{
+    return bf16_bits_to_f32(*p);
+}
+
+__device__ __forceinline__ float wave_sum(float x)
+{
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
+    return x;
+}
+
+}  // namespace gdn

@@ -1,0 +1,171 @@
+/*
+ * gdn.h -- C ABI of libgdn.so: the Gated DeltaNet layer recurrence on AMD Instinct
+ * MI355X (gfx950), prefill and batch-1 decode.
+ *
+ * Source of the operation: "Optimizing on-device inference for Apple Silicon"
+ * (Perplexity, 2026).
+ *   - Section "Qwen creates three distinct workload shapes": each Gated DeltaNet layer
+ *     keeps a fixed-size recurrent state; a learned gate decides how much of the old
+ *     state to keep and a delta update writes the current token in; every token depends
+ *     on the state after the previous token. Prefill may either scan the tokens directly
+ *     or re-block the updates into chunks that expose matrix work; which is faster depends
+ *     on the model dimensions, the workload and the hardware.
+ *   - Section "Keep the recurrent state on-chip": the state and its gate are 32-bit
+ *     floats (rounding compounds over sequential updates); queries and keys stay bf16;
+ *     the state is loaded once, carried through the scan and written back once.
+ *   - Section "Bound temporary memory with prompt chunking": a long prompt runs as
+ *     bounded segments whose recurrent state carries the context forward, without
+ *     changing the result. Here: pass one call's state_out as the next call's state_in.
+ *   - Section "Decode: minimise bytes moved per token" and its fused-chain list: decode
+ *     is bound by bytes moved per token; the recurrent update is fused with its
+ *     normalisation (here: the L2 normalisation of q and k).
+ *
+ * The recurrence (the gated delta rule; the page states it only in words). Per sequence,
+ * per V head h, for tokens t = 1..T:
+ *
+ *     S_t = exp(g_t) * S_{t-1} * (I - beta_t * khat_t * khat_t^T) + beta_t * v_t * khat_t^T
+ *     o_t = S_t * qhat_t                     (the state after token t's own update)
+ *
+ * with S_t of shape d_v x d_k, qhat = q / sqrt(sum(q^2) + l2_eps) and likewise khat, per
+ * token and QK head, and V head h reading QK head h / (h_v / h_qk) (consecutive V heads
+ * share a QK head). No 1/sqrt(d_k) query scale is applied; o is linear in q, so a caller
+ * that wants one scales `out`.
+ *
+ * Layouts. Every tensor is dense, row-major (C order), with no padding:
+ *   q, k        [n][t][h_qk][d_k]   qkv_dtype (bf16 or fp32)
+ *   v           [n][t][h_v][d_v]    qkv_dtype
+ *   g, beta     [n][t][h_v]         fp32; g is the log of the per-token decay (exp(g) is
+ *                                   applied), beta the write strength. Neither is clamped.
+ *   state_in,   [n][h_v][d_k][d_v]  fp32; element [i][j] holds S[j][i] (the state is stored
+ *   state_out                        transposed, d_k-major, so a value channel j is a
+ *                                   strided column and a key row i is contiguous)
+ *   out         [n][t][h_v][d_v]    fp32
+ * n counts independent sequences; for the stacked decode step it counts layers.
+ *
+ * Pointers and ownership. Every data pointer is a DEVICE pointer on the current HIP
+ * device. The caller allocates and owns every buffer, including the workspace. The
+ * library never allocates, frees or synchronises, keeps no mutable global state, and is
+ * safe to call from several host threads. Every compute call only enqueues work on
+ * `stream` (a hipStream_t; NULL is the default stream) and returns; results are ready
+ * when the stream reaches that point.
+ *
+ * Alignment. q, k, v, state_in, state_out, out and workspace must be 16-byte aligned;
+ * g and beta 4-byte aligned.
+ *
+ * Aliasing. state_in == state_out is allowed (update in place). Any other overlap of an
+ * output (out, state_out, workspace) with any other buffer is GDN_ERR_ALIAS. Inputs may
+ * overlap each other (for example q == k).
+ *
+ * Errors. All arguments are validated on the host before any HIP call. On any error
+ * nothing is enqueued and out/state_out are untouched. A launch failure reported by
+ * hipGetLastError returns GDN_ERR_HIP. Faults inside a kernel surface at the caller's next
+ * stream synchronisation, as for any HIP kernel.
+ *
+ * Supported: d_k == d_v in {16, 32, 64, 128}; chunk in {16, 32, 64, 128}; h_v a multiple
+ * of h_qk; n >= 0 (n == 0 is a no-op); t >= 0 for prefill (t == 0 copies state_in to
+ * state_out, or zeroes state_out when state_in is NULL); t == 1 for decode.
+ */
+#ifndef GDN_H
+#define GDN_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define GDN_ABI_VERSION 1
+
+typedef enum {
+    GDN_OK = 0,
+    GDN_ERR_NULL = 1,        /* a required pointer is NULL                               */
+    GDN_ERR_SHAPE = 2,       /* negative or inconsistent sizes, size overflow            */
+    GDN_ERR_UNSUPPORTED = 3, /* valid but not built: head dim, chunk size, dtype          */
+    GDN_ERR_ALIGN = 4,       /* pointer misaligned                                       */
+    GDN_ERR_ALIAS = 5,       /* an output overlaps another buffer (see Aliasing)          */
+    GDN_ERR_WORKSPACE = 6,   /* workspace NULL or smaller than gdn_workspace_bytes()      */
+    GDN_ERR_HIP = 7          /* the HIP runtime reported an error at launch               */
+} gdn_status;
+
+typedef enum { GDN_F32 = 0, GDN_BF16 = 1 } gdn_dtype;
+
+typedef struct {
+    int64_t n;         /* independent sequences (or stacked layers for decode)     */
+    int64_t t;         /* tokens in this call                                      */
+    int32_t h_qk;      /* query/key heads                                          */
+    int32_t h_v;       /* value heads, a multiple of h_qk                          */
+    int32_t d_k;       /* key head dimension                                       */
+    int32_t d_v;       /* value head dimension (must equal d_k)                    */
+    int32_t qkv_dtype; /* gdn_dtype of q, k and v                                  */
+    float l2_eps;      /* added to sum(x^2) under the square root; 1e-6 is typical */
+} gdn_dims;
+
+/* Version of this header the library was built from (GDN_ABI_VERSION). */
+int32_t gdn_abi_version(void);
+
+/* Static string for a status code; never NULL. */
+const char* gdn_status_str(gdn_status status);
+
+/*
+ * Workspace bytes a call needs: chunk in {16,32,64,128} for gdn_prefill_chunked, chunk 0
+ * for gdn_prefill_scan. Returns 0 for invalid or unsupported dims (and for t == 0).
+ * gdn_decode_step needs no workspace.
+ */
+size_t gdn_workspace_bytes(const gdn_dims* dims, int32_t chunk);
+
+/*
+ * Chunked prefill: the recurrence re-blocked into chunks of `chunk` tokens (the chunked
+ * evaluation of "Qwen creates three distinct workload shapes"). Within a chunk the
+ * updates are solved jointly (UT transform of the delta-rule updates, WY form) with bf16
+ * matrix-core products; the state is carried across chunks on chip. t need not be a
+ * multiple of chunk. Needs gdn_workspace_bytes(dims, chunk) bytes of workspace.
+ */
+gdn_status gdn_prefill_chunked(const gdn_dims* dims, int32_t chunk, const void* q,
+                               const void* k, const void* v, const float* g,
+                               const float* beta, const float* state_in, float* out,
+                               float* state_out, void* workspace, size_t workspace_bytes,
+                               void* stream);
+
+/*
+ * Direct-scan prefill: tokens in order, the state held in registers for the whole call
+ * and written back once ("Keep the recurrent state on-chip"). Needs
+ * gdn_workspace_bytes(dims, 0) bytes of workspace.
+ */
+gdn_status gdn_prefill_scan(const gdn_dims* dims, const void* q, const void* k,
+                            const void* v, const float* g, const float* beta,
+                            const float* state_in, float* out, float* state_out,
+                            void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Batch-1 decode step (dims->t must be 1): one token per sequence; each (sequence, V
+ * head) state streams from HBM through registers back to HBM once, with the q/k
+ * normalisation fused in. No workspace.
+ */
+gdn_status gdn_decode_step(const gdn_dims* dims, const void* q, const void* k,
+                           const void* v, const float* g, const float* beta,
+                           const float* state_in, float* out, float* state_out,
+                           void* stream);
+
+/*
+ * Prefill method for these dims, from the measured scan-versus-chunk crossover on
+ * MI355X: *chunk_or_zero receives 0 for the direct scan or the chunk size to pass to
+ * gdn_prefill_chunked.
+ */
+gdn_status gdn_prefill_choose(const gdn_dims* dims, int32_t* chunk_or_zero);
+
+/*
+ * Prefill with the method gdn_prefill_choose picks. The workspace must be at least
+ * gdn_workspace_bytes(dims, chosen chunk); gdn_prefill_workspace_bytes gives that size.
+ */
+size_t gdn_prefill_workspace_bytes(const gdn_dims* dims);
+gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const void* v,
+                       const float* g, const float* beta, const float* state_in,
+                       float* out, float* state_out, void* workspace,
+                       size_t workspace_bytes, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* GDN_H */

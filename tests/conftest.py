@@ -19,3 +19,13 @@ def pytest_configure(config):
 def oracle_run():
     import oracle
     return oracle.run
+
+
+@pytest.fixture(autouse=True)
+def _announce_gpu_case(request):
+    """Name each GPU case on the real stderr before it touches the GPU, so a run that
+    ends abruptly still shows which case was running."""
+    if request.node.get_closest_marker("gpu"):
+        sys.__stderr__.write(f"\n[gpu-case] {request.node.nodeid}\n")
+        sys.__stderr__.flush()
+    yield

@@ -1,0 +1,241 @@
+"""CPU tests of the C ABI: the library loads, exports every symbol include/gdn.h declares,
+and every validation path returns its error code before any HIP call (no GPU needed).
+
+Pointers below are fake device addresses: validation never dereferences them, and every
+call here fails validation, so nothing is launched.
+"""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import gated_deltanet_linear_prefill_amd as gdn
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "gdn.h")
+
+OK, NULL, SHAPE, UNSUP, ALIGN, ALIAS, WS, HIP = range(8)
+MB = 1 << 20
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(gdn_[a-z_]+)\s*\(", text)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return gdn._load()
+
+
+def test_library_exports_every_declared_function(lib):
+    names = declared_functions()
+    assert {"gdn_prefill_chunked", "gdn_prefill_scan", "gdn_decode_step",
+            "gdn_prefill_choose", "gdn_workspace_bytes", "gdn_status_str"} <= set(names)
+    for name in names:
+        assert hasattr(lib, name), name
+    dyn = subprocess.run(["nm", "-D", "--defined-only", gdn.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    exported = set(re.findall(r"\bT (gdn_\w+)", dyn))
+    assert set(names) <= exported, set(names) - exported
+
+
+def test_abi_version(lib):
+    m = re.search(r"#define GDN_ABI_VERSION (\d+)", open(HEADER).read())
+    assert gdn.gdn_abi_version() == int(m.group(1))
+
+
+def test_status_strings(lib):
+    for code in range(8):
+        s = gdn.gdn_status_str(code)
+        assert s.startswith("GDN_") and len(s) > 10
+    assert "unknown" in gdn.gdn_status_str(99)
+
+
+class Bufs:
+    """Disjoint, 256-byte aligned fake device ranges for one call."""
+
+    def __init__(self, n=1, t=64, h_qk=2, h_v=4, d=32, esize=2):
+        base = 0x7F0000000000
+        sizes = dict(q=n * t * h_qk * d * esize, k=n * t * h_qk * d * esize,
+                     v=n * t * h_v * d * esize, g=n * t * h_v * 4, beta=n * t * h_v * 4,
+                     state_in=n * h_v * d * d * 4, out=n * t * h_v * d * 4,
+                     state_out=n * h_v * d * d * 4, ws=64 * MB)
+        self.addr = {}
+        for key, size in sizes.items():
+            self.addr[key] = base
+            base += (size + 4095) // 4096 * 4096 + 4096
+        self.dims = gdn.make_dims(n, t, h_qk, h_v, d, gdn.torch.bfloat16 if esize == 2
+                                  else gdn.torch.float32)
+
+    def p(self, key, off=0):
+        return ctypes.c_void_p(self.addr[key] + off)
+
+
+def call_chunked(lib, b, chunk=64, dims=None, ws_bytes=64 * MB, **over):
+    a = {key: b.p(key) for key in ("q", "k", "v", "g", "beta", "state_in", "out",
+                                    "state_out", "ws")}
+    a.update(over)
+    d = ctypes.byref(dims if dims is not None else b.dims)
+    return lib.gdn_prefill_chunked(d, chunk, a["q"], a["k"], a["v"], a["g"], a["beta"],
+                                   a["state_in"], a["out"], a["state_out"], a["ws"],
+                                   ws_bytes, None)
+
+
+def call_scan(lib, b, dims=None, ws_bytes=64 * MB, **over):
+    a = {key: b.p(key) for key in ("q", "k", "v", "g", "beta", "state_in", "out",
+                                    "state_out", "ws")}
+    a.update(over)
+    d = ctypes.byref(dims if dims is not None else b.dims)
+    return lib.gdn_prefill_scan(d, a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"],
+                                a["out"], a["state_out"], a["ws"], ws_bytes, None)
+
+
+def call_decode(lib, b, dims=None, **over):
+    a = {key: b.p(key) for key in ("q", "k", "v", "g", "beta", "state_in", "out", "state_out")}
+    a.update(over)
+    d = ctypes.byref(dims if dims is not None else b.dims)
+    return lib.gdn_decode_step(d, a["q"], a["k"], a["v"], a["g"], a["beta"], a["state_in"],
+                               a["out"], a["state_out"], None)
+
+
+def with_dims(b, **kw):
+    d = gdn.Dims.from_buffer_copy(b.dims)
+    for key, val in kw.items():
+        setattr(d, key, val)
+    return d
+
+
+CALLS = [call_chunked, call_scan]
+
+
+@pytest.mark.parametrize("call", CALLS + [call_decode], ids=["chunked", "scan", "decode"])
+def test_null_dims(lib, call):
+    b = Bufs(t=1)
+    if call is call_decode:
+        st = lib.gdn_decode_step(None, *[b.p("q")] * 8, None)
+    elif call is call_scan:
+        st = lib.gdn_prefill_scan(None, *[b.p("q")] * 9, 0, None)
+    else:
+        st = lib.gdn_prefill_chunked(None, 64, *[b.p("q")] * 9, 0, None)
+    assert st == NULL
+
+
+@pytest.mark.parametrize("call", CALLS, ids=["chunked", "scan"])
+@pytest.mark.parametrize("field,value,code", [
+    ("n", -1, SHAPE), ("t", -5, SHAPE), ("h_qk", 0, SHAPE), ("h_v", 3, SHAPE),
+    ("h_v", -4, SHAPE), ("d_k", 48, UNSUP), ("d_v", 64, UNSUP), ("qkv_dtype", 7, UNSUP),
+    ("l2_eps", -1.0, SHAPE), ("l2_eps", float("nan"), SHAPE), ("t", 1 << 62, SHAPE),
+])
+def test_bad_dims(lib, call, field, value, code):
+    b = Bufs()
+    kw = {field: value}
+    if field == "d_k":
+        kw["d_v"] = value
+    assert call(lib, b, dims=with_dims(b, **kw)) == code
+
+
+def test_bad_chunk(lib):
+    b = Bufs()
+    for chunk in (0, 8, 48, 256, -64):
+        assert call_chunked(lib, b, chunk=chunk) == UNSUP
+
+
+def test_decode_needs_one_token(lib):
+    b = Bufs(t=2)
+    assert call_decode(lib, b) == SHAPE
+    b = Bufs(t=1)
+    assert call_decode(lib, b, dims=with_dims(b, t=0)) == SHAPE
+
+
+@pytest.mark.parametrize("call", CALLS + [call_decode], ids=["chunked", "scan", "decode"])
+@pytest.mark.parametrize("key", ["q", "k", "v", "g", "beta", "out", "state_out"])
+def test_missing_pointer(lib, call, key):
+    b = Bufs(t=1)
+    assert call(lib, b, **{key: None}) == NULL
+
+
+@pytest.mark.parametrize("call", CALLS + [call_decode], ids=["chunked", "scan", "decode"])
+@pytest.mark.parametrize("key,off", [("q", 2), ("k", 8), ("v", 4), ("state_in", 4),
+                                     ("out", 8), ("state_out", 12), ("g", 2), ("beta", 1)])
+def test_misaligned_pointer(lib, call, key, off):
+    b = Bufs(t=1)
+    assert call(lib, b, **{key: b.p(key, off)}) == ALIGN
+
+
+def test_misaligned_workspace(lib):
+    b = Bufs()
+    assert call_chunked(lib, b, ws=b.p("ws", 8)) == ALIGN
+    assert call_scan(lib, b, ws=b.p("ws", 4)) == ALIGN
+
+
+@pytest.mark.parametrize("call", CALLS, ids=["chunked", "scan"])
+def test_workspace_checks(lib, call):
+    b = Bufs()
+    need = lib.gdn_workspace_bytes(ctypes.byref(b.dims), 64 if call is call_chunked else 0)
+    assert need > 0
+    assert call(lib, b, ws=None) == WS
+    assert call(lib, b, ws_bytes=need - 1) == WS
+
+
+@pytest.mark.parametrize("call", CALLS + [call_decode], ids=["chunked", "scan", "decode"])
+def test_aliasing(lib, call):
+    b = Bufs(t=1)
+    # out overlapping an input, the state, or state_out
+    assert call(lib, b, out=b.p("v")) == ALIAS
+    assert call(lib, b, out=b.p("q", 16)) == ALIAS
+    assert call(lib, b, out=b.p("state_out")) == ALIAS
+    assert call(lib, b, state_out=b.p("g")) == ALIAS
+    # state_out partly overlapping state_in (equality is allowed; a shift is not)
+    assert call(lib, b, state_out=b.p("state_in", 16)) == ALIAS
+    assert call(lib, b, out=b.p("state_in")) == ALIAS
+
+
+def test_workspace_alias(lib):
+    b = Bufs()
+    assert call_chunked(lib, b, ws=b.p("out")) == ALIAS
+    assert call_scan(lib, b, ws=b.p("state_in")) == ALIAS
+    assert call_chunked(lib, b, ws=b.p("k")) == ALIAS
+
+
+def test_zero_sequences_is_a_noop(lib):
+    b = Bufs()
+    # n == 0 with no buffers at all: nothing to do, nothing launched.
+    z = with_dims(b, n=0)
+    none = {key: None for key in ("q", "k", "v", "g", "beta", "state_in", "out",
+                                   "state_out", "ws")}
+    assert call_chunked(lib, b, dims=z, ws_bytes=0, **none) == OK
+    assert call_scan(lib, b, dims=z, ws_bytes=0, **none) == OK
+    assert call_decode(lib, b, dims=with_dims(b, n=0, t=1),
+                       **{key: None for key in none if key != "ws"}) == OK
+
+
+def test_workspace_bytes_queries(lib):
+    b = Bufs(t=4096, h_qk=16, h_v=32, d=128)
+    for chunk in (0, 16, 32, 64, 128):
+        assert lib.gdn_workspace_bytes(ctypes.byref(b.dims), chunk) >= 0
+    assert lib.gdn_workspace_bytes(ctypes.byref(b.dims), 48) == 0
+    assert lib.gdn_workspace_bytes(None, 64) == 0
+    assert lib.gdn_workspace_bytes(ctypes.byref(with_dims(b, d_k=40, d_v=40)), 64) == 0
+    assert lib.gdn_workspace_bytes(ctypes.byref(with_dims(b, t=0)), 64) == 0
+
+
+def test_prefill_choose(lib):
+    for t in (1, 7, 64, 256, 4096, 131072):
+        c = gdn.gdn_prefill_choose(t)
+        assert c in (0, 16, 32, 64, 128)
+    res = ctypes.c_int32()
+    assert lib.gdn_prefill_choose(None, ctypes.byref(res)) == NULL
+    b = Bufs()
+    assert lib.gdn_prefill_choose(ctypes.byref(b.dims), None) == NULL
+    assert lib.gdn_prefill_choose(ctypes.byref(with_dims(b, h_v=3)), ctypes.byref(res)) == SHAPE
+
+
+def test_python_wrappers_reject_cpu_tensors():
+    import gdn_inputs
+    c = gdn_inputs.make_case(gdn_inputs.TINY, seed=1)
+    with pytest.raises(ValueError):
+        gdn.gdn_prefill_scan(c["q"], c["k"], c["v"], c["g"], c["beta"])
