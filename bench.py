@@ -1,0 +1,223 @@
+#!/usr/bin/env python3
+"""Benchmark of the Gated DeltaNet layer recurrence on one MI355X.
+
+One step is the whole hot path once:
+  * prefill: a 4096-token prompt through 30 GDN layers, one library prefill call per layer
+    (the method gdn_prefill_choose picks: the chunked kernels at this length), each layer
+    on its own synthetic inputs (16 QK heads, 32 V heads, d_k = d_v = 128, bf16 q/k/v,
+    fp32 gate and write strength, zero initial state), states written to a 30-layer stack;
+  * decode: one token through the same 30 layers (one stacked gdn_decode_step, n = 30),
+    continuing from the states the prefill produced, updated in place.
+`value` is prefill tokens per second for the 30 layers (4096 / prefill seconds per step);
+`decode_us_per_token` is the decode part. Inputs are resident in HBM before timing starts.
+
+The JSON line also carries
+  roofline:     the prefill call (its two kernels) against HBM: algorithmic bytes per call
+                (q, k, v, g, beta read once, out and state_out written once) divided by the
+                mean call duration from HIP events around every timed call, on the stream
+                the kernels run on; traffic from rocprofv3 counters when --traffic-json is
+                given;
+  cpu_baseline: the fp64 oracle timed on this host's cores on one layer of the same prefill.
+
+Modes for counter collection (no JSON line): --mode pmc-prefill runs the prefill calls of
+three layers; --mode pmc-copy runs a device copy of known size for counter calibration.
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+T_PROMPT, LAYERS, H_QK, H_V, D = 4096, 30, 16, 32, 128
+HBM_PEAK_GBS = 8000.0
+COPY_BYTES = 256 << 20
+METRIC = "GDN prefill tokens/s at T=4096 x30 layers; decode step us/token; % roofline"
+
+
+def parse():
+    ap = argparse.ArgumentParser(description=__doc__.split("\n")[0])
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--mode", choices=["bench", "pmc-prefill", "pmc-copy"], default="bench")
+    return ap.parse_args()
+
+
+def prefill_bytes():
+    """Algorithmic HBM bytes of one prefill call (S0 = 0, so no state read)."""
+    qk = T_PROMPT * H_QK * D * 2
+    v = T_PROMPT * H_V * D * 2
+    gb = T_PROMPT * H_V * 4
+    out = T_PROMPT * H_V * D * 4
+    st = H_V * D * D * 4
+    return 2 * qk + v + 2 * gb + out + st
+
+
+def decode_bytes():
+    st = LAYERS * H_V * D * D * 4
+    qk = LAYERS * H_QK * D * 2
+    v = LAYERS * H_V * D * 2
+    gb = LAYERS * H_V * 4
+    out = LAYERS * H_V * D * 4
+    return 2 * st + 2 * qk + v + 2 * gb + out
+
+
+TRAFFIC_PROFILE = os.path.join(ROOT, "profiles", "chunked_prefill_4k_traffic.md")
+KERNEL_SOURCE = os.path.join(ROOT, "gated_deltanet_linear_prefill_amd", "csrc", "gdn_chunked.hip")
+
+
+def measured_traffic():
+    """HBM bytes per prefill call from the committed rocprofv3 counter summary, or None when
+    the kernel source has changed since the counters were taken."""
+    import hashlib
+    if not os.path.exists(TRAFFIC_PROFILE):
+        return None
+    fields = {}
+    for line in open(TRAFFIC_PROFILE):
+        if ":" in line and line.split(":", 1)[0] in ("bytes_per_call", "source_sha256"):
+            key, val = line.split(":", 1)
+            fields[key] = val.strip()
+    sha = hashlib.sha256(open(KERNEL_SOURCE, "rb").read()).hexdigest()
+    if fields.get("source_sha256") != sha or "bytes_per_call" not in fields:
+        return None
+    return int(fields["bytes_per_call"])
+
+
+def cpu_baseline():
+    """The fp64 oracle on one layer of the prefill workload, all host threads it may use."""
+    import oracle
+    import gdn_inputs
+    c = gdn_inputs.make_case(gdn_inputs.PREFILL_4K, seed=100)
+    threads = oracle.default_threads()
+    t0 = time.perf_counter()
+    oracle.run(c["q"], c["k"], c["v"], c["g"], c["beta"], None, threads=threads)
+    dt = time.perf_counter() - t0
+    return {"value": T_PROMPT / (LAYERS * dt), "unit": "tokens/s", "cores": threads,
+            "kind": "oracle",
+            "sample": f"one layer of the prefill workload (T=4096, 32 V heads, d=128), "
+                      f"{dt:.2f} s; value = 4096 / (30 x layer time)"}
+
+
+def main():
+    args = parse()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}, WORLD_SIZE "
+              f"{world}); the recurrence shards by head with no communication, so the "
+              "whole-job figure is N times the one-GPU figure and is not measured here.",
+              file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    import gated_deltanet_linear_prefill_amd as gdn
+    import gdn_inputs
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+
+    if args.mode == "pmc-copy":
+        a = torch.empty(COPY_BYTES // 4, device=dev, dtype=torch.float32).fill_(1.0)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(f"copied {COPY_BYTES} bytes x3", flush=True)
+        return
+
+    # ---- inputs, all resident before timing
+    layers = [gdn_inputs.make_case(gdn_inputs.PREFILL_4K, seed=100 + l, device=dev)
+              for l in range(LAYERS)]
+    dec = gdn_inputs.make_case(gdn_inputs.DECODE_30L, seed=200, device=dev)
+    states = torch.zeros(LAYERS, H_V, D, D, device=dev)
+    outs = torch.empty(LAYERS, 1, T_PROMPT, H_V, D, device=dev)
+    dec_out = torch.empty(LAYERS, 1, H_V, D, device=dev)
+    chunk = gdn.gdn_prefill_choose(T_PROMPT, H_QK, H_V, D)
+    ws = torch.empty(max(1, gdn.gdn_workspace_bytes(1, T_PROMPT, H_QK, H_V, D, chunk=chunk)),
+                     device=dev, dtype=torch.uint8)
+    if chunk > 0:
+        bind = lambda c, l: gdn.bind_prefill_chunked(c["q"], c["k"], c["v"], c["g"], c["beta"], None,
+                                                     outs[l], states[l:l + 1], ws, chunk=chunk)
+    else:
+        bind = lambda c, l: gdn.bind_prefill_scan(c["q"], c["k"], c["v"], c["g"], c["beta"], None,
+                                                  outs[l], states[l:l + 1], ws)
+    calls = [bind(c, l) for l, c in enumerate(layers)]
+    decode = gdn.bind_decode_step(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], states,
+                                  dec_out, states)
+
+    if args.mode == "pmc-prefill":
+        for l in range(3):
+            calls[l]()
+        torch.cuda.synchronize()
+        print("prefill calls done", flush=True)
+        return
+
+    def step(evs=None):
+        if evs is None:
+            for c in calls:
+                c()
+            decode()
+            return
+        for l, c in enumerate(calls):
+            evs[l].record()
+            c()
+        evs[LAYERS].record()
+        decode()
+        evs[LAYERS + 1].record()
+
+    for _ in range(args.warmup):
+        step()
+    all_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(LAYERS + 2)]
+               for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        step(all_evs[s])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+
+    call_ms = [evs[l].elapsed_time(evs[l + 1]) for evs in all_evs for l in range(LAYERS)]
+    prefill_ms = [evs[0].elapsed_time(evs[LAYERS]) for evs in all_evs]
+    decode_ms = [evs[LAYERS].elapsed_time(evs[LAYERS + 1]) for evs in all_evs]
+    prefill_s = sum(prefill_ms) / len(prefill_ms) / 1e3
+    mean_call_s = sum(call_ms) / len(call_ms) / 1e3
+    achieved = prefill_bytes() / mean_call_s / 1e9
+
+    traffic = measured_traffic()
+
+    res = {
+        "metric": METRIC,
+        "value": T_PROMPT / prefill_s,
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": wall / args.steps * 1e3,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "GDN prefill, T=4096 tokens through 30 layers (16 QK + 32 V "
+                               "heads, d_k=d_v=128, bf16 q/k/v, fp32 g/beta/state, S0=0), "
+                               "then one decode token through the 30 layers",
+                   "method": f"chunked C={chunk}" if chunk else "direct scan",
+                   "global_batch": 1, "seq_len": T_PROMPT, "layers": LAYERS},
+        "decode_us_per_token": sum(decode_ms) / len(decode_ms) * 1e3,
+        "decode_GBps": decode_bytes() / (sum(decode_ms) / len(decode_ms) / 1e3) / 1e9,
+        "prefill_us_per_layer": mean_call_s * 1e6,
+        "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
+                     "kernel": "gdn_prefill_chunked call (chunk_prep_kernel + chunk_scan_kernel)",
+                     "algorithmic_bytes_per_call": prefill_bytes()},
+    }
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline()
+    print(json.dumps(res), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -17,7 +17,8 @@ import torch
 __all__ = [
     "GdnError", "gdn_abi_version", "gdn_status_str", "gdn_workspace_bytes",
     "gdn_prefill_chunked", "gdn_prefill_scan", "gdn_decode_step", "gdn_prefill_choose",
-    "gdn_prefill", "gdn_prefill_workspace_bytes", "library_path", "Dims",
+    "gdn_prefill", "gdn_prefill_workspace_bytes", "library_path", "Dims", "BoundCall",
+    "bind_prefill_chunked", "bind_prefill_scan", "bind_decode_step",
 ]
 
 GDN_F32, GDN_BF16 = 0, 1
@@ -206,3 +207,47 @@ def gdn_prefill(q, k, v, g, beta, state_in=None, *, l2_eps=1e-6, out=None, state
         _ptr(out), _ptr(state_out), _ptr(workspace), wbytes, _stream(q.device, stream)),
         "gdn_prefill")
     return out, state_out
+
+
+class BoundCall:
+    """One library call with its arguments marshalled once (for loops that replay the same
+    call, such as benchmarks or a layer stack). Calling it enqueues the kernels on the
+    stream that was current at bind time and raises GdnError on a non-OK status."""
+
+    def __init__(self, fn, args, where, keep):
+        self._fn, self._args, self._where, self._keep = fn, args, where, keep
+
+    def __call__(self):
+        st = self._fn(*self._args)
+        if st != 0:
+            raise GdnError(st, self._where)
+
+
+def bind_prefill_chunked(q, k, v, g, beta, state_in, out, state_out, workspace, *, chunk=64,
+                         l2_eps=1e-6, stream=None) -> BoundCall:
+    dims, out, state_out = _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps)
+    nbytes = workspace.numel() * workspace.element_size()
+    args = (ctypes.byref(dims), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+            _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace), nbytes,
+            _stream(q.device, stream))
+    return BoundCall(_load().gdn_prefill_chunked, args, "gdn_prefill_chunked",
+                     (dims, q, k, v, g, beta, state_in, out, state_out, workspace))
+
+
+def bind_prefill_scan(q, k, v, g, beta, state_in, out, state_out, workspace, *, l2_eps=1e-6,
+                      stream=None) -> BoundCall:
+    dims, out, state_out = _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps)
+    nbytes = workspace.numel() * workspace.element_size()
+    args = (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+            _ptr(out), _ptr(state_out), _ptr(workspace), nbytes, _stream(q.device, stream))
+    return BoundCall(_load().gdn_prefill_scan, args, "gdn_prefill_scan",
+                     (dims, q, k, v, g, beta, state_in, out, state_out, workspace))
+
+
+def bind_decode_step(q, k, v, g, beta, state_in, out, state_out, *, l2_eps=1e-6,
+                     stream=None) -> BoundCall:
+    dims, out, state_out = _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps)
+    args = (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
+            _ptr(out), _ptr(state_out), _stream(q.device, stream))
+    return BoundCall(_load().gdn_decode_step, args, "gdn_decode_step",
+                     (dims, q, k, v, g, beta, state_in, out, state_out))

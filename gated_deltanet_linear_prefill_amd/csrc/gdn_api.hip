@@ -84,7 +84,8 @@ size_t workspace_for(const gdn_dims* d, int32_t chunk)
 {
     if (d->t == 0 || d->n == 0) return 0;
     return chunk == 0 ? scan_workspace_bytes(d->n, d->t, d->h_qk, d->h_v, d->d_k)
-                      : chunked_workspace_bytes(d->n, d->t, d->h_qk, d->h_v, d->d_k, chunk);
+                      : chunked_workspace_bytes(d->n, d->t, d->h_qk, d->h_v, d->d_k, chunk,
+                                                d->qkv_dtype);
 }
 
 // Validate one call; `mode` 0 = scan, >0 = chunk size, -1 = decode (no workspace).
@@ -97,6 +98,11 @@ gdn_status validate(const gdn_dims* d, int32_t mode, const void* q, const void* 
     if (st != GDN_OK) return st;
     if (mode > 0 && !supported_chunk(mode)) return GDN_ERR_UNSUPPORTED;
     if (mode == -1 && d->t != 1) return GDN_ERR_SHAPE;
+    // Every grid must fit in 31 bits: chunk workgroups (n * chunks * h_qk) and the scan's
+    // normalisation rows (n * t * h_qk / 16).
+    if (mode > 0 && d->n * ((d->t + mode - 1) / mode) * (int64_t)d->h_qk >= (INT64_C(1) << 31))
+        return GDN_ERR_SHAPE;
+    if (mode == 0 && s.qk / d->d_k / 16 >= (INT64_C(1) << 31)) return GDN_ERR_SHAPE;
 
     const bool work = d->n > 0;
     const bool tokens = work && d->t > 0;

@@ -32,7 +32,7 @@ hipError_t launch_state_passthrough(const Call& c);  // t == 0: state_out = stat
 
 size_t scan_workspace_bytes(int64_t n, int64_t t, int32_t h_qk, int32_t h_v, int32_t d);
 size_t chunked_workspace_bytes(int64_t n, int64_t t, int32_t h_qk, int32_t h_v, int32_t d,
-                               int chunk);
+                               int chunk, int32_t dtype);
 
 // ---------------------------------------------------------------- device helpers
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t bits16)
@@ -78,6 +78,37 @@ __device__ __forceinline__ float wave_sum(float x)
 #pragma unroll
     for (int off = 32; off >= 1; off >>= 1) x += __shfl_xor(x, off, 64);
     return x;
+}
+
+template <int CTRL>
+__device__ __forceinline__ float dpp_f(float x)
+{
+    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
+}
+
+// Sum over the 16 lanes of a DPP row; every lane receives the same (bitwise) total.
+__device__ __forceinline__ float row16_sum(float x)
+{
+    x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
+    x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
+    x += dpp_f<0x141>(x);  // row_half_mirror: lane i <-> 7 - i within 8
+    x += dpp_f<0x140>(x);  // row_mirror: lane i <-> 15 - i within 16
+    return x;
+}
+
+template <int N, typename TIn>
+__device__ __forceinline__ void load_n(const TIn* p, float* x)
+{
+    if constexpr (N % 4 == 0) {
+#pragma unroll
+        for (int i = 0; i < N; i += 4) {
+            const float4 a = load4_f32(p + i);
+            x[i] = a.x; x[i + 1] = a.y; x[i + 2] = a.z; x[i + 3] = a.w;
+        }
+    } else {
+#pragma unroll
+        for (int i = 0; i < N; ++i) x[i] = load1_f32(p + i);
+    }
 }
 
 }  // namespace gdn

@@ -21,37 +21,6 @@
 namespace gdn {
 namespace {
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_f(float x)
-{
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(x), CTRL, 0xF, 0xF, false));
-}
-
-// Sum over the 16 lanes of a DPP row; every lane receives the same (bitwise) total.
-__device__ __forceinline__ float row16_sum(float x)
-{
-    x += dpp_f<0xB1>(x);   // quad_perm [1,0,3,2]: lane ^ 1
-    x += dpp_f<0x4E>(x);   // quad_perm [2,3,0,1]: lane ^ 2
-    x += dpp_f<0x141>(x);  // row_half_mirror: lane i <-> 7 - i within 8
-    x += dpp_f<0x140>(x);  // row_mirror: lane i <-> 15 - i within 16
-    return x;
-}
-
-template <int N, typename TIn>
-__device__ __forceinline__ void load_n(const TIn* p, float* x)
-{
-    if constexpr (N % 4 == 0) {
-#pragma unroll
-        for (int i = 0; i < N; i += 4) {
-            const float4 a = load4_f32(p + i);
-            x[i] = a.x; x[i + 1] = a.y; x[i + 2] = a.z; x[i + 3] = a.w;
-        }
-    } else {
-#pragma unroll
-        for (int i = 0; i < N; ++i) x[i] = load1_f32(p + i);
-    }
-}
-
 size_t align256(size_t x)
 {
     return (x + 255) & ~size_t(255);

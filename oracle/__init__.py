@@ -47,10 +47,16 @@ def _ptr(a):
 
 
 def default_threads() -> int:
+    """Host threads to use: the CPUs this process may run on, capped by OMP_NUM_THREADS
+    when set and at 16 (the CPU share of one GPU on a shared host)."""
     try:
-        return max(1, len(os.sched_getaffinity(0)))
+        n = len(os.sched_getaffinity(0))
     except AttributeError:
-        return max(1, os.cpu_count() or 1)
+        n = os.cpu_count() or 1
+    env = os.environ.get("OMP_NUM_THREADS", "")
+    if env.isdigit() and int(env) > 0:
+        n = min(n, int(env))
+    return max(1, min(n, 16))
 
 
 def run(q, k, v, g, beta, state_in=None, l2_eps=1e-6, heads=None, threads=None):
