@@ -15,8 +15,8 @@ The JSON line also carries
   roofline:     the prefill call (its two kernels) against HBM: algorithmic bytes per call
                 (q, k, v, g, beta read once, out and state_out written once) divided by the
                 mean call duration from HIP events around every timed call, on the stream
-                the kernels run on; traffic from rocprofv3 counters when --traffic-json is
-                given;
+                the kernels run on; traffic = HBM bytes per call from the committed
+                rocprofv3 counter summary (null once the kernel source has changed);
   cpu_baseline: the fp64 oracle timed on this host's cores on one layer of the same prefill.
 
 Modes for counter collection (no JSON line): --mode pmc-prefill runs the prefill calls of
