@@ -31,6 +31,10 @@
 //    sequential over chunks): the state block stays in MFMA accumulators for the whole
 //    call; per chunk K M0 and Q M0, X, U = T X, O and the state update run on MFMA.
 //
+// Decay factors exp(gamma_r - gamma_s) <= 1 inside the C x C matrices use the hardware
+// exponential (__expf); its relative error, a few 1e-6 at these arguments, is far below the
+// split-bf16 operand precision.
+//
 // Precision: an MFMA operand that is not an exact bf16 input (the state, X, U, T, Ptil) is
 // split into hi = bf16(x) and lo = bf16(x - hi) and multiplied as hi*hi + hi*lo + lo*hi
 // (or hi + lo against an exact operand), which keeps about 16 significant bits per
@@ -47,6 +51,7 @@ namespace {
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ floatx4 mfma_bf16(bf16x8 a, bf16x8 b, floatx4 c)
 {
@@ -201,6 +206,63 @@ __device__ __forceinline__ float raw_to_f32(float x)
     return x;
 }
 
+// Buffer resources: a base address and byte range in scalar registers, re-based once per
+// chunk with scalar adds, while each lane keeps one fixed byte offset. Lanes whose offset
+// falls outside the range read zero (and their stores are dropped), which handles the rows
+// past the end of a sequence without per-lane branches. The 0x00020000 word is the raw
+// (untyped, unswizzled) descriptor format of the gfx9 family.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes)
+{
+    const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+__device__ __forceinline__ bf16x8 buf_bf16x8(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ u32x4 buf_u32x4(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+__device__ __forceinline__ floatx4 buf_floatx4(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(floatx4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
+}
+
+template <typename TIn>
+__device__ __forceinline__ TIn buf_elem(__amdgpu_buffer_rsrc_t r, int off);
+
+template <>
+__device__ __forceinline__ uint16_t buf_elem<uint16_t>(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
+}
+
+template <>
+__device__ __forceinline__ float buf_elem<float>(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return __builtin_bit_cast(float, __builtin_amdgcn_raw_buffer_load_b32(r, off, 0, 0));
+}
+
+template <typename TIn>
+__device__ __forceinline__ typename RawFrag<TIn>::type buf_raw_frag(__amdgpu_buffer_rsrc_t r, int off);
+
+template <>
+__device__ __forceinline__ bf16x8 buf_raw_frag<uint16_t>(__amdgpu_buffer_rsrc_t r, int off)
+{
+    return buf_bf16x8(r, off);
+}
+
+template <>
+__device__ __forceinline__ floatx8 buf_raw_frag<float>(__amdgpu_buffer_rsrc_t r, int off)
+{
+    const floatx4 a = buf_floatx4(r, off), b = buf_floatx4(r, off + 16);
+    return floatx8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+}
+
 // acc += A * B with A given as NA bf16 pieces and B as NB pieces, skipping lo*lo.
 template <int NA, int NB>
 __device__ __forceinline__ floatx4 mfma_split(const bf16x8* a, const bf16x8* b, floatx4 acc)
@@ -209,6 +271,16 @@ __device__ __forceinline__ floatx4 mfma_split(const bf16x8* a, const bf16x8* b, 
     if constexpr (NB > 1) acc = mfma_bf16(a[0], b[1], acc);
     if constexpr (NA > 1) acc = mfma_bf16(a[1], b[0], acc);
     return acc;
+}
+
+// The same product with each split pass in its own accumulator (acc[0..NA+NB-2]), so the
+// passes do not wait on each other; the caller sums the accumulators at the end.
+template <int NA, int NB>
+__device__ __forceinline__ void mfma_split_acc(const bf16x8* a, const bf16x8* b, floatx4* acc)
+{
+    acc[0] = mfma_bf16(a[0], b[0], acc[0]);
+    if constexpr (NB > 1) acc[1] = mfma_bf16(a[0], b[1], acc[1]);
+    if constexpr (NA > 1) acc[NB] = mfma_bf16(a[1], b[0], acc[NB]);
 }
 
 // Index of the t-th lower-triangular 16x16 tile (row tile >= column tile).
@@ -390,7 +462,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rt + 4 * lg + e, s = 16 * ct + lr;
                 float a = 0.f;
-                if (s < r) a = s_beta[r] * expf(s_gam[r] - s_gam[s]) * s_rk[r] * s_rk[s] * acc[e];
+                if (s < r) a = s_beta[r] * __expf(s_gam[r] - s_gam[s]) * s_rk[r] * s_rk[s] * acc[e];
                 s_a[r][s] = a;
             }
         }
@@ -476,7 +548,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             for (int e = 0; e < 4; ++e) {
                 const int r = 16 * rt + 4 * lg + e, s = 16 * ct + lr;
                 float p = 0.f;
-                if (s <= r) p = expf(s_gam[r] - s_gam[s]) * s_rq[r] * s_rk[s] * acc[e];
+                if (s <= r) p = __expf(s_gam[r] - s_gam[s]) * s_rq[r] * s_rk[s] * acc[e];
                 s_a[r][s] = p;
             }
         }
@@ -491,14 +563,24 @@ template <int D, int C, typename TIn>
 struct ChunkRegs {
     using G = Geo<D, C, std::is_same<TIn, float>::value>;
     using Raw = typename RawFrag<TIn>::type;
-    static constexpr int RTW = (G::RT + 3) / 4;  // row tiles per wave
-    static constexpr int MTW = (G::MT + 3) / 4;  // state row tiles per wave
-    Raw ka[RTW][G::KTD], qa[RTW][G::KTD];       // K, Q rows (A operands), as loaded
-    TIn vv[RTW][4];                             // V in accumulator layout, as loaded
-    float4 sc[RTW][4];                          // per-token scalars
-    bf16x8 tf[RTW][G::KTC][2], pf[RTW][G::KTC][2];  // T, Ptil (hi, lo)
-    bf16x8 kt[MTW][G::KTC][G::NS];                  // K^T tiles
-    float gc;                                       // Gamma_C
+    // bf16 K and Q chunks are staged through LDS with coalesced loads (a 16-lane group reads
+    // one contiguous 256-byte row); fp32 inputs (small head dims) load MFMA fragments
+    // directly and split them at use.
+    static constexpr bool KQ_LDS = !std::is_same<TIn, float>::value;
+    static constexpr int RTW = (G::RT + 3) / 4;          // row tiles per wave
+    static constexpr int MTW = (G::MT + 3) / 4;          // state row tiles per wave
+    static constexpr int NPIECE = C * D / 8;             // 16-byte pieces of a K (or Q) chunk
+    static constexpr int KQP = (NPIECE + 255) / 256;     // pieces per thread
+    static constexpr int NFRAG = KQ_LDS ? 1 : RTW;
+    static constexpr int NKTD = KQ_LDS ? 1 : G::KTD;
+    u32x4 kp[KQ_LDS ? KQP : 1], qp[KQ_LDS ? KQP : 1];     // K, Q pieces of the chunk (LDS path)
+    Raw ka[NFRAG][NKTD], qa[NFRAG][NKTD];                 // K, Q fragments (direct path)
+    TIn vv[RTW][4];                                       // V in accumulator layout, as loaded
+    floatx4 scv;                                          // one token's scalars (LDS path)
+    floatx4 sc[KQ_LDS ? 1 : RTW][4];                      // per-token scalars (direct path)
+    bf16x8 tf[RTW][G::KTC][2], pf[RTW][G::KTC][2];        // T, Ptil (hi, lo)
+    bf16x8 kt[KQ_LDS ? 1 : MTW][KQ_LDS ? 1 : G::KTC][G::NS];  // K^T tiles (direct path)
+    float gc;                                             // Gamma_C
 };
 
 template <int D, int C, typename TIn>
@@ -513,16 +595,23 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     using R = ChunkRegs<D, C, TIn>;
     constexpr int DP = G::DP, CP = G::CP, RT = G::RT, KTC = G::KTC, KTD = G::KTD, MT = G::MT;
     constexpr int NS = G::NS, RTW = R::RTW, MTW = R::MTW;
+    constexpr bool KQ_LDS = R::KQ_LDS;
     constexpr int NCB = D / 16;
     constexpr int MS = DP + 8;  // LDS stride of M^T rows (bf16)
     constexpr int XS = CP + 8;  // LDS stride of X^T, U^T, W^T rows (bf16)
+    constexpr int KS = DP + 8;  // LDS stride of K / Q chunk rows (bf16)
 
     // B operands built in-kernel, stored transposed (value channel major) so that a lane's
-    // eight k-consecutive elements are contiguous.
+    // eight k-consecutive elements are contiguous; and the K / Q chunk (A operands).
     __shared__ __align__(16) __bf16 s_m[2][16][MS];  // state block (hi, lo)
     __shared__ __align__(16) __bf16 s_x[2][16][XS];  // X
     __shared__ __align__(16) __bf16 s_u[2][16][XS];  // U
     __shared__ __align__(16) __bf16 s_w[2][16][XS];  // W = diag(r_k exp(gamma_C - gamma)) U
+    // K rows (two buffers by chunk parity: read up to the state update), Q rows (read only
+    // before the first barrier) and per-token scalars (two buffers).
+    __shared__ __align__(16) __bf16 s_k[2][KQ_LDS ? C : 1][KQ_LDS ? KS : 8];
+    __shared__ __align__(16) __bf16 s_q[KQ_LDS ? C : 1][KQ_LDS ? KS : 8];
+    __shared__ __align__(16) floatx4 s_sc[2][KQ_LDS ? C : 1];
 
     // Workgroups that share a QK head run on the same XCD (blockIdx % 8 picks the XCD), so
     // their common K/Q/T/Ptil reads meet in one L2.
@@ -537,36 +626,40 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
     const int64_t nch = L.nch;
 
-    // Zero every B-operand buffer once: padded k ranges (features >= D, tokens >= C) are
+    // Zero every LDS operand buffer once: padded k ranges (features >= D, tokens >= C) are
     // never written and must read as zero.
     {
-        __bf16* z = &s_m[0][0][0];
-        for (int i = tid; i < 2 * 16 * MS; i += 256) z[i] = (__bf16)0.f;
-        z = &s_x[0][0][0];
-        for (int i = tid; i < 2 * 16 * XS; i += 256) z[i] = (__bf16)0.f;
-        z = &s_u[0][0][0];
-        for (int i = tid; i < 2 * 16 * XS; i += 256) z[i] = (__bf16)0.f;
-        z = &s_w[0][0][0];
-        for (int i = tid; i < 2 * 16 * XS; i += 256) z[i] = (__bf16)0.f;
+        auto zero = [&](__bf16* z, int n) {
+            for (int i = tid; i < n; i += 256) z[i] = (__bf16)0.f;
+        };
+        zero(&s_m[0][0][0], 2 * 16 * MS);
+        zero(&s_x[0][0][0], 2 * 16 * XS);
+        zero(&s_u[0][0][0], 2 * 16 * XS);
+        zero(&s_w[0][0][0], 2 * 16 * XS);
+        if constexpr (KQ_LDS) {
+            zero(&s_k[0][0][0], 2 * C * KS);
+            zero(&s_q[0][0], C * KS);
+        }
     }
     __syncthreads();
 
-    // State block in accumulator layout: tile mt = w + 4 i holds M[16 mt + 4 lg + e][cb 16 + lr].
-    floatx4 macc[MTW];
-    const int64_t sbase = nh * (int64_t)D * D;
     // Four accumulator rows of one column, split, as two 8-byte LDS stores (hi, lo).
     auto put4 = [&](__bf16* hi_row, __bf16* lo_row, floatx4 val) {
         bf16x4 hi, lo;
 #pragma unroll
         for (int e = 0; e < 4; ++e) {
-            __bf16 h, l;
-            split_bf16(val[e], h, l);
-            hi[e] = h;
-            lo[e] = l;
+            __bf16 hh, ll;
+            split_bf16(val[e], hh, ll);
+            hi[e] = hh;
+            lo[e] = ll;
         }
         *reinterpret_cast<bf16x4*>(hi_row) = hi;
         *reinterpret_cast<bf16x4*>(lo_row) = lo;
     };
+
+    // State block in accumulator layout: tile mt = w + 4 i holds M[16 mt + 4 lg + e][cb 16 + lr].
+    floatx4 macc[MTW];
+    const int64_t sbase = nh * (int64_t)D * D;
     auto store_m_lds = [&](int i, int mt) {
         put4(&s_m[0][lr][16 * mt + 4 * lg], &s_m[1][lr][16 * mt + 4 * lg], macc[i]);
     };
@@ -581,88 +674,185 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
             store_m_lds(i, mt);
         }
     }
-    __syncthreads();
+
+    // Byte strides and this lane's fixed byte offsets inside each per-chunk buffer range.
+    constexpr int ES = sizeof(TIn);
+    const int64_t row_qk = (int64_t)h_qk * D * ES;  // between consecutive tokens of q, k
+    const int64_t row_v = (int64_t)h_v * D * ES;    // ... of v
+    const int64_t row_o = (int64_t)h_v * D * 4;     // ... of out
+    int off_v[RTW][4], off_o[RTW][4];
+#pragma unroll
+    for (int i = 0; i < RTW; ++i)
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int rr = 16 * (w + 4 * i) + 4 * lg + e;
+            off_v[i][e] = (int)(rr * row_v) + lr * ES;
+            off_o[i][e] = (int)(rr * row_o) + lr * 4;
+        }
 
     auto load = [&](R& x, int64_t c) {
         c = c < nch ? c : nch - 1;  // past the end: reload the last chunk (never computed)
         const int64_t c0 = c * C;
         const int64_t tok0 = seq * T + c0;
+        const int64_t rows = (T - c0) < C ? (T - c0) : C;  // tokens of this chunk
         const int64_t vh = (seq * nch + c) * h_v + h;
-        const char* t_base = ws + L.t + (size_t)vh * G::TP_BYTES;
-        const char* p_base = ws + L.p + (size_t)vh * G::TP_BYTES;
-        const float4* sc = reinterpret_cast<const float4*>(ws + L.sc + (size_t)vh * G::SC_BYTES);
-        const char* kt_base = ws + L.kt + (size_t)((seq * nch + c) * h_qk + hq) * G::KT_BYTES;
+        const auto r_t = make_rsrc(ws + L.t + (size_t)vh * G::TP_BYTES, G::TP_BYTES);
+        const auto r_p = make_rsrc(ws + L.p + (size_t)vh * G::TP_BYTES, G::TP_BYTES);
+        const auto r_sc = make_rsrc(ws + L.sc + (size_t)vh * G::SC_BYTES, G::SC_BYTES);
+        const auto r_kt = make_rsrc(ws + L.kt + (size_t)((seq * nch + c) * h_qk + hq) * G::KT_BYTES,
+                                    G::KT_BYTES);
+        // q / k rows of QK head hq and the v block of this workgroup; rows past the end
+        // fall outside the range and read zero.
+        const int64_t kq_bytes = (rows - 1) * row_qk + D * ES;
+        const auto r_k = make_rsrc(k + (tok0 * h_qk + hq) * (int64_t)D, kq_bytes);
+        const auto r_q = make_rsrc(q + (tok0 * h_qk + hq) * (int64_t)D, kq_bytes);
+        const auto r_v = make_rsrc(v + (tok0 * h_v + h) * (int64_t)D + cb * 16, (rows - 1) * row_v + 16 * ES);
+        if constexpr (KQ_LDS) {
+#pragma unroll
+            for (int p = 0; p < R::KQP; ++p) {
+                const int pidx = tid + 256 * p;
+                const int r = (pidx / (D / 8)) % C, f = (pidx % (D / 8)) * 8;
+                const int off = (int)(r * row_qk) + f * ES;
+                x.kp[p] = buf_u32x4(r_k, off);
+                x.qp[p] = buf_u32x4(r_q, off);
+            }
+            x.scv = buf_floatx4(r_sc, (tid % C) * 16);
+        }
 #pragma unroll
         for (int i = 0; i < RTW; ++i) {
             const int rt = w + 4 * i;
             if (rt >= RT) continue;
-            const int r = 16 * rt + lr;
-            const bool rok = c0 + r < T;
-            // Rows past the end and padded features read clamped, finite data: their
-            // products meet zero factors (beta = 0 scalars, zero state rows), so no mask.
+            if constexpr (!KQ_LDS) {
+                // Padded features (f >= D) read zero through an out-of-range offset.
 #pragma unroll
-            for (int kt = 0; kt < KTD; ++kt) {
-                const int f = 32 * kt + 8 * lg;
-                const bool ok = rok && f < D;
-                const int64_t off = ((tok0 + (ok ? r : 0)) * h_qk + hq) * (int64_t)D + (ok ? f : 0);
-                x.ka[i][kt] = load_raw_frag<TIn>(k + off);
-                x.qa[i][kt] = load_raw_frag<TIn>(q + off);
+                for (int kt = 0; kt < KTD; ++kt) {
+                    const int f = 32 * kt + 8 * lg;
+                    const int off = f < D ? (int)((16 * rt + lr) * row_qk) + f * ES : 0x7fffffff - 64;
+                    x.ka[i][kt] = buf_raw_frag<TIn>(r_k, off);
+                    x.qa[i][kt] = buf_raw_frag<TIn>(r_q, off);
+                }
             }
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                const int rr = 16 * rt + 4 * lg + e;
-                const bool ok = c0 + rr < T;
-                x.vv[i][e] = v[((tok0 + (ok ? rr : 0)) * h_v + h) * (int64_t)D + cb * 16 + lr];
-                x.sc[i][e] = sc[rr];
+                x.vv[i][e] = buf_elem<TIn>(r_v, off_v[i][e]);
+                if constexpr (!KQ_LDS) x.sc[i][e] = buf_floatx4(r_sc, (16 * rt + 4 * lg + e) * 16);
             }
 #pragma unroll
             for (int kt = 0; kt < KTC; ++kt) {
                 if (32 * kt > 16 * rt + 15) continue;
-                const size_t o = (size_t)(rt * KTC + kt) * 2 * 1024 + l * 16;
-                x.tf[i][kt][0] = *reinterpret_cast<const bf16x8*>(t_base + o);
-                x.tf[i][kt][1] = *reinterpret_cast<const bf16x8*>(t_base + o + 1024);
-                x.pf[i][kt][0] = *reinterpret_cast<const bf16x8*>(p_base + o);
-                x.pf[i][kt][1] = *reinterpret_cast<const bf16x8*>(p_base + o + 1024);
+                const int o = (rt * KTC + kt) * 2 * 1024 + l * 16;
+                x.tf[i][kt][0] = buf_bf16x8(r_t, o);
+                x.tf[i][kt][1] = buf_bf16x8(r_t, o + 1024);
+                x.pf[i][kt][0] = buf_bf16x8(r_p, o);
+                x.pf[i][kt][1] = buf_bf16x8(r_p, o + 1024);
             }
         }
+        if constexpr (!KQ_LDS) {
 #pragma unroll
-        for (int i = 0; i < MTW; ++i) {
-            const int mt = w + 4 * i;
-            if (mt >= MT) continue;
+            for (int i = 0; i < MTW; ++i) {
+                const int mt = w + 4 * i;
+                if (mt >= MT) continue;
 #pragma unroll
-            for (int kt = 0; kt < KTC; ++kt)
+                for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
-                for (int part = 0; part < NS; ++part)
-                    x.kt[i][kt][part] = *reinterpret_cast<const bf16x8*>(
-                        kt_base + (size_t)((mt * KTC + kt) * NS + part) * 1024 + l * 16);
+                    for (int part = 0; part < NS; ++part)
+                        x.kt[i][kt][part] = buf_bf16x8(r_kt, ((mt * KTC + kt) * NS + part) * 1024 + l * 16);
+            }
         }
-        x.gc = reinterpret_cast<const float*>(ws + L.gc)[vh];
+        // A vector load (every lane the same word), not a scalar one: scalar loads share the
+        // LDS wait counter, and the wait before each barrier would stall on its round trip.
+        x.gc = buf_elem<float>(make_rsrc(ws + L.gc + (size_t)vh * 4, 4), 0);
     };
 
-    auto compute = [&](const R& x, int64_t c) {
+    // K / Q pieces and scalars of a chunk into LDS buffer `b` (rows past the end arrived as
+    // zero).
+    auto store_kq = [&](const R& x, int b) {
+        if constexpr (KQ_LDS) {
+#pragma unroll
+            for (int p = 0; p < R::KQP; ++p) {
+                const int pidx = tid + 256 * p;
+                if (R::NPIECE % 256 != 0 && pidx >= R::NPIECE) continue;
+                const int r = pidx / (D / 8), f = (pidx % (D / 8)) * 8;
+                *reinterpret_cast<u32x4*>(&s_k[b][r][f]) = x.kp[p];
+                *reinterpret_cast<u32x4*>(&s_q[r][f]) = x.qp[p];
+            }
+            if (tid < C) s_sc[b][tid] = x.scv;
+        }
+    };
+
+    // Outputs of a chunk wait in registers and are stored after the next wait for loads:
+    // vector-memory loads and stores share one completion counter, so a store issued just
+    // before that wait would stall it for the write round trip.
+    floatx4 opend[RTW];
+    auto store_out = [&](int64_t c) {
         const int64_t c0 = c * C;
+        const int64_t rows = (T - c0) < C ? (T - c0) : C;
+        const auto r_o = make_rsrc(out + ((seq * T + c0) * h_v + h) * (int64_t)D + cb * 16,
+                                   (rows - 1) * row_o + 64);
+#pragma unroll
+        for (int i = 0; i < RTW; ++i) {
+            const int rt = w + 4 * i;
+            if (rt >= RT) continue;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                // Element to a scalar first: a bit cast of a vector-element expression picked
+                // element 0 for every e in this compiler.
+                const float val = opend[i][e];
+                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), r_o, off_o[i][e], 0, 0);
+            }
+        }
+    };
+
+    // Scalars {beta, beta Gamma r_k, Gamma r_q, r_k exp(gamma_C - gamma)} of accumulator
+    // row e of row tile w + 4 i.
+    auto scal = [&](const R& x, int b, int i, int e) -> floatx4 {
+        if constexpr (KQ_LDS) return s_sc[b][16 * (w + 4 * i) + 4 * lg + e];
+        else return x.sc[i][e];
+    };
+
+    auto compute = [&](const R& x, int b) {
         // (1) K M0 and Q M0; X = diag(beta) V - diag(beta Gamma r_k) K M0
         floatx4 qm[RTW];
 #pragma unroll
         for (int i = 0; i < RTW; ++i) {
             const int rt = w + 4 * i;
             if (rt >= RT) continue;
-            floatx4 km = {0.f, 0.f, 0.f, 0.f}, qq = {0.f, 0.f, 0.f, 0.f};
+            // Independent accumulators per k-tile parity and split pass (summed below), so
+            // consecutive MFMAs do not wait on each other's results.
+            constexpr int NP = NS + 1;  // passes per k tile: M hi, M lo (and K lo)
+            floatx4 kacc[2][NP], qacc[2][NP];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int pp = 0; pp < NP; ++pp) kacc[j][pp] = qacc[j][pp] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kt = 0; kt < KTD; ++kt) {
                 bf16x8 mb[2], ka[NS], qa[NS];
                 mb[0] = *reinterpret_cast<const bf16x8*>(&s_m[0][lr][32 * kt + 8 * lg]);
                 mb[1] = *reinterpret_cast<const bf16x8*>(&s_m[1][lr][32 * kt + 8 * lg]);
-                to_pieces(x.ka[i][kt], ka);
-                to_pieces(x.qa[i][kt], qa);
-                km = mfma_split<NS, 2>(ka, mb, km);
-                qq = mfma_split<NS, 2>(qa, mb, qq);
+                if constexpr (KQ_LDS) {
+                    ka[0] = *reinterpret_cast<const bf16x8*>(&s_k[b][16 * rt + lr][32 * kt + 8 * lg]);
+                    qa[0] = *reinterpret_cast<const bf16x8*>(&s_q[16 * rt + lr][32 * kt + 8 * lg]);
+                } else {
+                    to_pieces(x.ka[i][kt], ka);
+                    to_pieces(x.qa[i][kt], qa);
+                }
+                mfma_split_acc<NS, 2>(ka, mb, kacc[kt & 1]);
+                mfma_split_acc<NS, 2>(qa, mb, qacc[kt & 1]);
             }
+            floatx4 km = kacc[0][0], qq = qacc[0][0];
+#pragma unroll
+            for (int j = 0; j < 2; ++j)
+#pragma unroll
+                for (int pp = (j == 0 ? 1 : 0); pp < NP; ++pp) {
+                    km += kacc[j][pp];
+                    qq += qacc[j][pp];
+                }
             qm[i] = qq;
             floatx4 xv;
 #pragma unroll
             for (int e = 0; e < 4; ++e)
-                xv[e] = x.sc[i][e].x * raw_to_f32(x.vv[i][e]) - x.sc[i][e].y * km[e];
+                xv[e] = scal(x, b, i, e)[0] * raw_to_f32(x.vv[i][e]) - scal(x, b, i, e)[1] * km[e];
             put4(&s_x[0][lr][16 * rt + 4 * lg], &s_x[1][lr][16 * rt + 4 * lg], xv);
         }
         __syncthreads();
@@ -671,18 +861,19 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
         for (int i = 0; i < RTW; ++i) {
             const int rt = w + 4 * i;
             if (rt >= RT) continue;
-            floatx4 u = {0.f, 0.f, 0.f, 0.f};
+            floatx4 uacc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
             for (int kt = 0; kt < KTC; ++kt) {
                 if (32 * kt > 16 * rt + 15) continue;
                 bf16x8 xb[2];
                 xb[0] = *reinterpret_cast<const bf16x8*>(&s_x[0][lr][32 * kt + 8 * lg]);
                 xb[1] = *reinterpret_cast<const bf16x8*>(&s_x[1][lr][32 * kt + 8 * lg]);
-                u = mfma_split<2, 2>(x.tf[i][kt], xb, u);
+                mfma_split_acc<2, 2>(x.tf[i][kt], xb, uacc);
             }
+            const floatx4 u = uacc[0] + uacc[1] + uacc[2];
             floatx4 wv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wv[e] = x.sc[i][e].w * u[e];
+            for (int e = 0; e < 4; ++e) wv[e] = scal(x, b, i, e)[3] * u[e];
             put4(&s_u[0][lr][16 * rt + 4 * lg], &s_u[1][lr][16 * rt + 4 * lg], u);
             put4(&s_w[0][lr][16 * rt + 4 * lg], &s_w[1][lr][16 * rt + 4 * lg], wv);
         }
@@ -692,67 +883,102 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
         for (int i = 0; i < RTW; ++i) {
             const int rt = w + 4 * i;
             if (rt >= RT) continue;
-            floatx4 o;
+            floatx4 oacc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
 #pragma unroll
-            for (int e = 0; e < 4; ++e) o[e] = x.sc[i][e].z * qm[i][e];
+            for (int e = 0; e < 4; ++e) oacc[0][e] = scal(x, b, i, e)[2] * qm[i][e];
 #pragma unroll
             for (int kt = 0; kt < KTC; ++kt) {
                 if (32 * kt > 16 * rt + 15) continue;
                 bf16x8 ub[2];
                 ub[0] = *reinterpret_cast<const bf16x8*>(&s_u[0][lr][32 * kt + 8 * lg]);
                 ub[1] = *reinterpret_cast<const bf16x8*>(&s_u[1][lr][32 * kt + 8 * lg]);
-                o = mfma_split<2, 2>(x.pf[i][kt], ub, o);
+                mfma_split_acc<2, 2>(x.pf[i][kt], ub, oacc);
             }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int64_t tok = c0 + 16 * rt + 4 * lg + e;
-                if (tok < T) out[((seq * T + tok) * h_v + h) * (int64_t)D + cb * 16 + lr] = o[e];
-            }
+            opend[i] = oacc[0] + oacc[1] + oacc[2];
         }
         // (4) M <- Gamma_C M + K^T W
 #pragma unroll
         for (int i = 0; i < MTW; ++i) {
             const int mt = w + 4 * i;
             if (mt >= MT) continue;
-            floatx4 acc;
+            constexpr int NP = NS + 1;
+            floatx4 acc[NP];
 #pragma unroll
-            for (int e = 0; e < 4; ++e) acc[e] = x.gc * macc[i][e];
+            for (int e = 0; e < 4; ++e) acc[0][e] = x.gc * macc[i][e];
+#pragma unroll
+            for (int pp = 1; pp < NP; ++pp) acc[pp] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
             for (int kt = 0; kt < KTC; ++kt) {
                 bf16x8 wb[2];
                 wb[0] = *reinterpret_cast<const bf16x8*>(&s_w[0][lr][32 * kt + 8 * lg]);
                 wb[1] = *reinterpret_cast<const bf16x8*>(&s_w[1][lr][32 * kt + 8 * lg]);
-                acc = mfma_split<NS, 2>(x.kt[i][kt], wb, acc);
+                if constexpr (KQ_LDS) {
+                    // K^T fragment: feature 16 mt + lr, tokens 32 kt + 8 lg + e, read across
+                    // the K rows in LDS (tokens past the chunk are zero rows).
+                    bf16x8 ktf[1];
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const int tok = 32 * kt + 8 * lg + e;
+                        ktf[0][e] = tok < C ? s_k[b][tok][16 * mt + lr] : (__bf16)0.f;
+                    }
+                    mfma_split_acc<1, 2>(ktf, wb, acc);
+                } else {
+                    mfma_split_acc<NS, 2>(x.kt[i][kt], wb, acc);
+                }
             }
-            macc[i] = acc;
+            floatx4 mnew = acc[0];
+#pragma unroll
+            for (int pp = 1; pp < NP; ++pp) mnew += acc[pp];
+            macc[i] = mnew;
             store_m_lds(i, mt);
         }
-        __syncthreads();
     };
 
+    // A full wait: nothing left in flight, so the compiler's wait bookkeeping starts clean
+    // (no loop-carried loads that would force early waits inside the next chunk).
+    auto settle = [&]() { __builtin_amdgcn_s_waitcnt(0); };
+
     if constexpr (C <= 64) {
-        // The next chunk's fragments load while this chunk computes; the rotation at the
-        // end of the iteration is where the wait for them lands, after all of this
-        // chunk's work (not at their first use in the next iteration).
-        R cur, nxt;
-        load(cur, 0);
-        // Settle the first chunk's loads before the loop, so the only waits inside it are
-        // for this iteration's own prefetch (at the rotation) and for LDS.
-        __builtin_amdgcn_s_waitcnt(0);
+        // Two operand sets alternate: the next chunk's operands load while this chunk
+        // computes, and the wait for them lands at the end of the chunk.
+        // Even chunks use LDS buffer 0, odd chunks buffer 1. Q and buffer (c + 1) & 1 are
+        // last read by chunk c - 1 / before chunk c's first barrier, so they can be refilled
+        // at the end of chunk c.
+        R A, B;
+        load(A, 0);
+        store_kq(A, 0);
+        settle();
+        __syncthreads();
 #pragma unroll 1
-        for (int64_t c = 0; c < nch; ++c) {
-            load(nxt, c + 1);
-            compute(cur, c);
-            cur = nxt;
+        for (int64_t c = 0; c < nch; c += 2) {
+            load(B, c + 1);
+            compute(A, 0);
+            store_kq(B, 1);
+            settle();
+            __syncthreads();
+            store_out(c);
+            if (c + 1 >= nch) break;
+            load(A, c + 2);
+            compute(B, 1);
+            store_kq(A, 0);
+            settle();
+            __syncthreads();
+            store_out(c + 1);
         }
     } else {
-        // Two sets of C = 128 fragments do not fit the register file.
-        R cur;
+        // Two sets of C = 128 operands do not fit the register file: load at the top.
+        R A;
 #pragma unroll 1
         for (int64_t c = 0; c < nch; ++c) {
-            load(cur, c);
-            compute(cur, c);
+            load(A, c);
+            store_kq(A, (int)(c & 1));
+            settle();
+            __syncthreads();
+            if (c > 0) store_out(c - 1);
+            compute(A, (int)(c & 1));
+            __syncthreads();
         }
+        store_out(nch - 1);
     }
 
 #pragma unroll
