@@ -102,6 +102,10 @@ gdn_status validate(const gdn_dims* d, int32_t mode, const void* q, const void* 
     // normalisation rows (n * t * h_qk / 16).
     if (mode > 0 && d->n * ((d->t + mode - 1) / mode) * (int64_t)d->h_qk >= (INT64_C(1) << 31))
         return GDN_ERR_SHAPE;
+    // The chunked kernels address one chunk of q, k, v and out with 32-bit byte offsets:
+    // keep a chunk's extent (fp32 out is the largest) below 2^30 bytes.
+    if (mode > 0 && (int64_t)mode * d->h_v * d->d_k * 4 + 64 >= (INT64_C(1) << 30))
+        return GDN_ERR_SHAPE;
     if (mode == 0 && s.qk / d->d_k / 16 >= (INT64_C(1) << 31)) return GDN_ERR_SHAPE;
 
     const bool work = d->n > 0;

@@ -10,37 +10,45 @@
 // Gamma_r = exp(gamma_r)). Every value channel j obeys m_r = alpha_r m_{r-1} + khat_r u_r
 // with u_r = beta_r (v_r - alpha_r khat_r . m_{r-1}); unrolling m_{r-1} turns the C
 // updates into one unit lower triangular system (the UT transform of the delta rule):
-//   (I + A) U = diag(beta) V - diag(beta Gamma) Khat M0,
+//   (I + A) U = diag(beta) (V - diag(Gamma) Khat M0),
 //   A[r][s] = beta_r exp(gamma_r - gamma_s) khat_r . khat_s        (s < r)
-// so with T = (I + A)^-1 (WY form):
-//   U   = T X,                      X = diag(beta) V - diag(beta Gamma r_k) (K M0)
-//   O   = diag(Gamma r_q) (Q M0) + Ptil U,
-//         Ptil[r][s] = exp(gamma_r - gamma_s) r_q,r r_k,s q_r . k_s  (s <= r)
-//   M_C = Gamma_C M0 + K^T diag(r_k exp(gamma_C - gamma)) U
-// where K, Q are the raw inputs and r_k, r_q the inverse norms: the normalisation is kept
-// as diagonal scalings so the bf16 inputs enter the MFMAs exactly. Decays only appear as
-// exp(gamma_r - gamma_s) with s <= r, never as 1/Gamma, so nothing overflows.
+// With T = (I + A)^-1 and K, Q the raw inputs, r_k, r_q their inverse norms:
+//   U   = T' X,          T' = T diag(beta),   X = V - diag(a) (K M0),   a = Gamma r_k
+//   O   = diag(o) (Q M0) + Ptil U,            o = Gamma r_q,
+//         Ptil[r][s] = exp(gamma_r - gamma_s) r_q,r r_k,s q_r . k_s   (s <= r)
+//   M_C = Gamma_C M0 + K^T diag(s) U,         s = r_k exp(gamma_C - gamma)
+// The normalisation stays a diagonal scaling so the bf16 inputs enter the MFMAs exactly,
+// and decays only appear as exp(gamma_r - gamma_s) with s <= r, so nothing overflows.
 //
 // Two kernels:
 //  * chunk_prep_kernel (one workgroup per sequence, chunk and QK head; fully parallel):
-//    inverse norms, gate prefix sums, K K^T and Q K^T on MFMA, A, T = (I + A)^-1 by
-//    blocked forward substitution in LDS (16x16 diagonal blocks by substitution, the
-//    off-diagonal blocks with fp32 MFMA), and writes to the workspace T and Ptil as
-//    hi/lo bf16 pairs already in MFMA A-operand order, K^T tiles, and per-token scalars.
+//    inverse norms, gate prefix sums, the Gram matrices K K^T and Q K^T (MFMA, once per QK
+//    head), then per V head A, T = (I + A)^-1 by blocked forward substitution in LDS, and
+//    the per-token scalars. T' and Ptil go to the workspace as hi/lo bf16 MFMA A-operand
+//    tiles (lower-triangular tiles only), K^T as A-operand tiles.
 //  * chunk_scan_kernel (one workgroup per sequence, V head and 16 value channels;
-//    sequential over chunks): the state block stays in MFMA accumulators for the whole
-//    call; per chunk K M0 and Q M0, X, U = T X, O and the state update run on MFMA.
+//    sequential over chunks). Two "chain" waves each keep half of the state's d_k rows in
+//    MFMA accumulators and run the recurrence; per chunk they exchange one partial
+//    product K M0 through LDS, with a single workgroup barrier per chunk. The other waves
+//    form the outputs O of the previous chunk from the state and U the chain waves publish.
 //
-// Decay factors exp(gamma_r - gamma_s) <= 1 inside the C x C matrices use the hardware
-// exponential (__expf); its relative error, a few 1e-6 at these arguments, is far below the
-// split-bf16 operand precision.
+// Operand order. Contractions over d_k and over chunk tokens both use k tiles of 32. The
+// state's accumulator rows hold features in a permuted order (tile mt, row 4a + e holds
+// feature 32 (mt >> 1) + 8 a + 4 (mt & 1) + e) and token k slots are permuted the same way
+// (slot 8 lg + 4 h + e of token tile kt is token 32 kt + 16 h + 4 lg + e): then the four
+// accumulator values a lane holds in two adjacent row tiles are exactly the eight k values
+// that lane needs as a B operand, so U, W, X and the state feed the next MFMA from
+// registers. Raw K and Q rows stay in natural feature order. The prepared A operands (T',
+// Ptil, K^T) are written with the same token permutation.
 //
-// Precision: an MFMA operand that is not an exact bf16 input (the state, X, U, T, Ptil) is
-// split into hi = bf16(x) and lo = bf16(x - hi) and multiplied as hi*hi + hi*lo + lo*hi
-// (or hi + lo against an exact operand), which keeps about 16 significant bits per
-// operand and fp32 accumulation; rounding them to one bf16 would not meet the accuracy
-// the recurrence needs (the page's "Keep the recurrent state on-chip" section keeps the
-// state and gate in 32-bit floats for the same reason).
+// Precision: an MFMA operand that is not an exact bf16 input (the state, X, U, W, T',
+// Ptil) is split into hi = bf16(x) and lo = bf16(x - hi) and multiplied as
+// hi*hi + hi*lo + lo*hi (or hi + lo against an exact operand), which keeps about 16
+// significant bits per operand with fp32 accumulation; one bf16 rounding would not meet the
+// accuracy the recurrence needs (the page's "Keep the recurrent state on-chip" section keeps
+// the state and gate in 32-bit floats for the same reason). Decay factors
+// exp(gamma_r - gamma_s) <= 1 inside the C x C matrices use the hardware exponential
+// (__expf); its relative error, a few 1e-6 at these arguments, is far below that precision.
 #include <type_traits>
 
 #include "gdn_internal.hpp"
@@ -49,8 +57,8 @@ namespace gdn {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef float floatx8 __attribute__((ext_vector_type(8)));
 typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
 
 __device__ __forceinline__ floatx4 mfma_bf16(bf16x8 a, bf16x8 b, floatx4 c)
@@ -80,28 +88,52 @@ __device__ __forceinline__ void lds_fence()
 //   A fragment (16 rows x 32 k): row lr, k = 8 lg + 0..7
 //   B fragment (32 k x 16 cols): col lr, k = 8 lg + 0..7
 //   accumulator (16 x 16 fp32):  rows 4 lg + 0..3, col lr
-// Only the row/column roles matter: A and B enumerate k the same way, so the contraction
-// is the same whatever order the hardware pairs the eight elements in.
+// A and B enumerate k the same way, so any fixed relabelling of the 32 k slots applied to
+// both operands leaves the product unchanged; the permutations below rely on that.
+
+// Feature held by accumulator row rho (0..15) of state tile mt.
+__host__ __device__ constexpr int feat_of(int mt, int rho)
+{
+    return 32 * (mt >> 1) + 8 * (rho >> 2) + 4 * (mt & 1) + (rho & 3);
+}
+
+// Chunk token in k slot 8 lg + j of token k tile kt.
+__host__ __device__ constexpr int tok_of(int kt, int lg, int j)
+{
+    return 32 * kt + 16 * (j >> 2) + 4 * lg + (j & 3);
+}
+
+// Lower-triangular operand tiles are stored compactly: row tile rt (16 tokens) keeps the
+// token k tiles 0 .. rt / 2, i.e. those that reach the diagonal. Index of (rt, 0):
+__host__ __device__ constexpr int tri_off(int rt)
+{
+    return (rt / 2) * (rt / 2 + 1) + (rt & 1) * (rt / 2 + 1);
+}
 
 template <int D, int C, bool F32IN>
 struct Geo {
     static constexpr int DP = D < 32 ? 32 : D;  // contraction over d, padded to k = 32
     static constexpr int CP = C < 32 ? 32 : C;  // contraction over chunk tokens, padded
-    static constexpr int RT = C / 16;           // 16-token row tiles of a chunk
-    static constexpr int KTC = CP / 32;         // k tiles over chunk tokens
     static constexpr int KTD = DP / 32;         // k tiles over d
-    static constexpr int MT = D / 16;           // 16-row tiles of the state (d_k)
+    static constexpr int MTP = DP / 16;         // 16-row state tiles (padded features zero)
+    static constexpr int KTC = CP / 32;         // k tiles over chunk tokens
+    static constexpr int RT = C / 16;           // 16-token row tiles of a chunk
     static constexpr int NS = F32IN ? 2 : 1;    // bf16 pieces per q/k element
-    static constexpr size_t KT_BYTES = (size_t)MT * KTC * NS * 1024;  // per (chunk, QK head)
-    static constexpr size_t TP_BYTES = (size_t)RT * KTC * 2 * 1024;   // per (chunk, V head)
-    static constexpr size_t SC_BYTES = (size_t)C * 16;                // per (chunk, V head)
+    static constexpr int NTRI = tri_off(RT);    // stored lower-triangular tiles
+    static constexpr int NCH = KTD >= 2 ? 2 : 1;  // chain waves (split of d_k)
+    static constexpr int KTH = KTD / NCH;       // d k tiles per chain wave
+    static constexpr int MTH = 2 * KTH;         // state tiles per chain wave
+    static constexpr int NOW = 4 - NCH;         // output waves
+    static constexpr int RTO = (RT + NOW - 1) / NOW;  // row tiles per output wave
+    static constexpr size_t KT_BYTES = (size_t)MTP * KTC * NS * 1024;  // per (chunk, QK head)
+    static constexpr size_t TRI_BYTES = (size_t)NTRI * 2 * 1024;      // per (chunk, V head)
+    static constexpr size_t SC_BYTES = (size_t)3 * CP * 4 + 16;       // per (chunk, V head)
 };
 
 // Workspace regions; every region starts 256-byte aligned.
 struct ChunkWs {
-    int64_t nch;                    // chunks per sequence
-    size_t kt, t, p, sc, gc, total; // byte offsets
-    size_t kt_bytes, tp_bytes, sc_bytes;
+    int64_t nch;                  // chunks per sequence
+    size_t kt, tt, pt, sc, total; // byte offsets: K^T, T', Ptil, scalars
 };
 
 size_t align256(size_t x)
@@ -113,56 +145,22 @@ ChunkWs chunk_ws(int64_t n, int64_t t, int32_t h_qk, int32_t h_v, int32_t d, int
                  bool f32in)
 {
     const int dp = d < 32 ? 32 : d, cp = chunk < 32 ? 32 : chunk;
-    (void)dp;
+    const size_t kt_bytes = (size_t)(dp / 16) * (cp / 32) * (f32in ? 2 : 1) * 1024;
+    const size_t tri_bytes = (size_t)tri_off(chunk / 16) * 2 * 1024;
+    const size_t sc_bytes = (size_t)3 * cp * 4 + 16;
     ChunkWs w;
     w.nch = (t + chunk - 1) / chunk;
-    w.kt_bytes = (size_t)(d / 16) * (cp / 32) * (f32in ? 2 : 1) * 1024;
-    w.tp_bytes = (size_t)(chunk / 16) * (cp / 32) * 2 * 1024;
-    w.sc_bytes = (size_t)chunk * 16;
     const size_t nq = (size_t)n * w.nch * h_qk, nv = (size_t)n * w.nch * h_v;
     w.kt = 0;
-    w.t = w.kt + align256(nq * w.kt_bytes);
-    w.p = w.t + align256(nv * w.tp_bytes);
-    w.sc = w.p + align256(nv * w.tp_bytes);
-    w.gc = w.sc + align256(nv * w.sc_bytes);
-    w.total = w.gc + align256(nv * sizeof(float));
+    w.tt = w.kt + align256(nq * kt_bytes);
+    w.pt = w.tt + align256(nv * tri_bytes);
+    w.sc = w.pt + align256(nv * tri_bytes);
+    w.total = w.sc + align256(nv * sc_bytes);
     return w;
 }
 
-// Eight consecutive q/k elements as bf16 fragment pieces: the exact value for bf16
-// input; hi and lo for fp32 input; zero when !ok. `p` must point to readable memory even
-// when !ok: the load is unconditional and the mask is a select, so no branch (and no
-// early wait on outstanding loads) is tied to the lane predicate.
-template <typename TIn>
-__device__ __forceinline__ void load_frag(const TIn* p, bool ok, bf16x8* piece)
-{
-    if constexpr (std::is_same<TIn, float>::value) {
-        const float4 a = reinterpret_cast<const float4*>(p)[0];
-        const float4 b = reinterpret_cast<const float4*>(p)[1];
-        const float x[8] = {a.x, a.y, a.z, a.w, b.x, b.y, b.z, b.w};
-        bf16x8 hi, lo;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-            __bf16 h, l;
-            split_bf16(ok ? x[e] : 0.f, h, l);
-            hi[e] = h;
-            lo[e] = l;
-        }
-        piece[0] = hi;
-        piece[1] = lo;
-    } else {
-        const bf16x8 val = *reinterpret_cast<const bf16x8*>(p);
-        bf16x8 zero;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) zero[e] = (__bf16)0.f;
-        piece[0] = ok ? val : zero;
-    }
-}
-
-// Raw fragment storage for the scan kernel's prefetch registers: the loaded bits are kept
-// as they arrive and turned into MFMA pieces at use, so issuing the next chunk's loads
-// never has to wait for them.
-typedef float floatx8 __attribute__((ext_vector_type(8)));
+// Raw fragment storage for prefetch registers: the loaded bits are kept as they arrive and
+// turned into MFMA pieces at use, so issuing the next chunk's loads never has to wait.
 template <typename TIn>
 struct RawFrag;
 template <>
@@ -173,12 +171,6 @@ template <>
 struct RawFrag<float> {
     using type = floatx8;
 };
-
-template <typename TIn>
-__device__ __forceinline__ typename RawFrag<TIn>::type load_raw_frag(const TIn* p)
-{
-    return *reinterpret_cast<const typename RawFrag<TIn>::type*>(p);
-}
 
 __device__ __forceinline__ void to_pieces(const bf16x8& raw, bf16x8* piece)
 {
@@ -207,24 +199,24 @@ __device__ __forceinline__ float raw_to_f32(float x)
 }
 
 // Buffer resources: a base address and byte range in scalar registers, re-based once per
-// chunk with scalar adds, while each lane keeps one fixed byte offset. Lanes whose offset
+// chunk with scalar adds, while each lane keeps fixed byte offsets. Lanes whose offset
 // falls outside the range read zero (and their stores are dropped), which handles the rows
-// past the end of a sequence without per-lane branches. The 0x00020000 word is the raw
-// (untyped, unswizzled) descriptor format of the gfx9 family.
+// past the end of a sequence and padded features without per-lane branches. The 0x00020000
+// word is the raw (untyped, unswizzled) descriptor format of the gfx9 family.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes)
 {
     const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
     return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
 }
 
+// A byte offset beyond every buffer range used here (ranges stay below 2^30; the host
+// checks the chunk's q/k/v/out extents against that bound). Added to an in-range offset
+// (below 2^30) it stays below 2^32, so the hardware's unsigned offset does not wrap.
+constexpr uint32_t OOR = 0x60000000u;
+
 __device__ __forceinline__ bf16x8 buf_bf16x8(__amdgpu_buffer_rsrc_t r, int off)
 {
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
-}
-
-__device__ __forceinline__ u32x4 buf_u32x4(__amdgpu_buffer_rsrc_t r, int off)
-{
-    return __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
 }
 
 __device__ __forceinline__ floatx4 buf_floatx4(__amdgpu_buffer_rsrc_t r, int off)
@@ -273,14 +265,43 @@ __device__ __forceinline__ floatx4 mfma_split(const bf16x8* a, const bf16x8* b, 
     return acc;
 }
 
-// The same product with each split pass in its own accumulator (acc[0..NA+NB-2]), so the
-// passes do not wait on each other; the caller sums the accumulators at the end.
+// The same product with each split pass in its own accumulator (acc[0 .. NA + NB - 2]),
+// so the passes do not wait on each other; the caller sums the accumulators at the end.
 template <int NA, int NB>
 __device__ __forceinline__ void mfma_split_acc(const bf16x8* a, const bf16x8* b, floatx4* acc)
 {
     acc[0] = mfma_bf16(a[0], b[0], acc[0]);
     if constexpr (NB > 1) acc[1] = mfma_bf16(a[0], b[1], acc[1]);
     if constexpr (NA > 1) acc[NB] = mfma_bf16(a[1], b[0], acc[NB]);
+}
+
+// hi/lo B-fragment pieces of one k tile from the accumulators of its two row tiles.
+__device__ __forceinline__ void pair_to_frag(const floatx4& a0, const floatx4& a1, bf16x8& hi,
+                                             bf16x8& lo)
+{
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        __bf16 h, l;
+        split_bf16(a0[e], h, l);
+        hi[e] = h;
+        lo[e] = l;
+        split_bf16(a1[e], h, l);
+        hi[4 + e] = h;
+        lo[4 + e] = l;
+    }
+}
+
+// Per-row-tile values (RT row tiles of 16 tokens, accumulator layout) as token k-tile
+// B fragments; row tiles past the chunk (C = 16 pads to one k tile of 32) are zero.
+template <int RT, int KTC>
+__device__ __forceinline__ void rows_to_frags(const floatx4* rows, bf16x8 (*fr)[2])
+{
+#pragma unroll
+    for (int kt = 0; kt < KTC; ++kt) {
+        const floatx4 z = {0.f, 0.f, 0.f, 0.f};
+        pair_to_frag(2 * kt < RT ? rows[2 * kt] : z, 2 * kt + 1 < RT ? rows[2 * kt + 1] : z,
+                     fr[kt][0], fr[kt][1]);
+    }
 }
 
 // Index of the t-th lower-triangular 16x16 tile (row tile >= column tile).
@@ -300,23 +321,25 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 {
     constexpr bool F32IN = std::is_same<TIn, float>::value;
     using G = Geo<D, C, F32IN>;
-    constexpr int DP = G::DP, RT = G::RT, KTC = G::KTC, KTD = G::KTD, MT = G::MT, NS = G::NS;
-    constexpr int NB = C / 16;    // 16x16 diagonal blocks of T
-    constexpr int KS = DP + 8;    // LDS row stride of the K chunk (bf16)
-    constexpr int CS = C + 4;     // LDS row stride of the C x C fp32 matrices
-    constexpr size_t K_LDS = (size_t)NS * C * KS * 2;
-    constexpr size_t AT_LDS = (size_t)2 * C * CS * 4;
-    constexpr size_t U_LDS = K_LDS > AT_LDS ? K_LDS : AT_LDS;
+    constexpr int DP = G::DP, CP = G::CP, RT = G::RT, KTC = G::KTC, KTD = G::KTD;
+    constexpr int MTP = G::MTP, NS = G::NS, NTRI = G::NTRI;
+    constexpr int NB = RT;        // 16x16 diagonal blocks of T
+    constexpr int KS = DP + 8;    // LDS row stride of the K / Q pieces (bf16)
+    constexpr int CS = CP + 4;    // LDS row stride of the CP x CP fp32 matrices
+    constexpr size_t KQ_LDS = (size_t)2 * NS * CP * KS * 2;
+    constexpr size_t AT_LDS = (size_t)2 * CP * CS * 4;
+    constexpr size_t U_LDS = KQ_LDS > AT_LDS ? KQ_LDS : AT_LDS;
 
-    // The K chunk (phase 0) and the A / T matrices (later phases) share one buffer.
+    // The K and Q chunks (first phases) and the A / T matrices (later phases) share one
+    // buffer; the Gram matrices live in registers in between.
     __shared__ __align__(16) char s_buf[U_LDS];
-    __shared__ float s_rk[C], s_rq[C], s_gam[C], s_beta[C];
+    __shared__ float s_rk[CP], s_rq[CP], s_gam[CP], s_beta[CP];
     __shared__ float s_x[4][16][17];  // per-wave 16x16 scratch
-    auto s_k = [&](int part, int r, int f) -> __bf16& {
-        return reinterpret_cast<__bf16*>(s_buf)[((size_t)part * C + r) * KS + f];
+    auto s_kq = [&](int which, int part, int r, int f) -> __bf16& {
+        return reinterpret_cast<__bf16*>(s_buf)[(((size_t)which * NS + part) * CP + r) * KS + f];
     };
     float(*s_a)[CS] = reinterpret_cast<float(*)[CS]>(s_buf);
-    float(*s_t)[CS] = reinterpret_cast<float(*)[CS]>(s_buf + (size_t)C * CS * 4);
+    float(*s_t)[CS] = reinterpret_cast<float(*)[CS]>(s_buf + (size_t)CP * CS * 4);
 
     const int64_t nch = L.nch;
     const int hq = (int)(blockIdx.x % h_qk);
@@ -329,11 +352,12 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     const int grp = h_v / h_qk;
     const int64_t tok0 = seq * T + c0;  // flattened token index of the chunk's first token
 
-    // ---- phase 0: inverse norms of q and k rows; the K chunk into LDS as bf16 pieces
+    // ---- phase 0: inverse norms of the q and k rows; both chunks into LDS as bf16 pieces
+    //      (rows past the chunk and padded features are zero)
     {
         constexpr int EPL = D / 16;  // elements per lane, 16 lanes per row
         const int sub = tid & 15;
-        for (int r0 = 0; r0 < C; r0 += 16) {
+        for (int r0 = 0; r0 < CP; r0 += 16) {
             const int r = r0 + (tid >> 4);
             const bool ok = r < Cr;
             const int64_t off = ((tok0 + (ok ? r : 0)) * h_qk + hq) * (int64_t)D + sub * EPL;
@@ -356,51 +380,85 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             for (int e = 0; e < EPL; ++e) {
                 __bf16 hi, lo;
                 split_bf16(ok ? kv[e] : 0.f, hi, lo);
-                s_k(0, r, sub * EPL + e) = hi;
-                if constexpr (NS > 1) s_k(1, r, sub * EPL + e) = lo;
+                s_kq(0, 0, r, sub * EPL + e) = hi;
+                if constexpr (NS > 1) s_kq(0, 1, r, sub * EPL + e) = lo;
+                split_bf16(ok ? qv[e] : 0.f, hi, lo);
+                s_kq(1, 0, r, sub * EPL + e) = hi;
+                if constexpr (NS > 1) s_kq(1, 1, r, sub * EPL + e) = lo;
             }
             if constexpr (D < DP) {  // zero the padded features
 #pragma unroll
                 for (int e = 0; e < (DP - D) / 16; ++e)
-                    for (int part = 0; part < NS; ++part)
-                        s_k(part, r, D + sub * ((DP - D) / 16) + e) = (__bf16)0.f;
+#pragma unroll
+                    for (int which = 0; which < 2; ++which)
+#pragma unroll
+                        for (int part = 0; part < NS; ++part)
+                            s_kq(which, part, r, D + sub * ((DP - D) / 16) + e) = (__bf16)0.f;
             }
         }
     }
     __syncthreads();
 
-    // ---- K^T tiles (A operand of K^T W in the scan kernel): tile (mt, kt, part) holds
-    //      K[token 32 kt + 8 lg + e][feature 16 mt + lr]
+    // ---- phase 1: K^T tiles (A operand of the state update): tile (mt, kt, part) holds
+    //      K[token tok_of(kt, lg, j)][feature feat_of(mt, lr)] in lane l, slot j
     {
         char* kt_base = ws + L.kt + (size_t)((seq * nch + c) * h_qk + hq) * G::KT_BYTES;
-        constexpr int NTILE = MT * KTC * NS;
+        constexpr int NTILE = MTP * KTC * NS;
         for (int ti = w; ti < NTILE; ti += 4) {
             const int part = ti % NS, kt = (ti / NS) % KTC, mt = ti / (NS * KTC);
-            const int f = 16 * mt + lr, r0 = 32 * kt + 8 * lg;
+            const int f = feat_of(mt, lr);
             bf16x8 val;
 #pragma unroll
-            for (int e = 0; e < 8; ++e) val[e] = (r0 + e < C) ? s_k(part, r0 + e, f) : (__bf16)0.f;
+            for (int j = 0; j < 8; ++j) val[j] = s_kq(0, part, tok_of(kt, lg, j), f);
             *reinterpret_cast<bf16x8*>(kt_base + (size_t)ti * 1024 + l * 16) = val;
         }
     }
-    __syncthreads();  // the K buffer becomes A / T below
 
-    // Fragments of the q/k rows of this chunk, straight from the input tensors.
-    auto qk_frag = [&](const TIn* base, int row, int kt, bf16x8* piece) {
-        const int f = 32 * kt + 8 * lg;
-        const bool ok = row < Cr && f < D;
-        load_frag<TIn>(base + ((tok0 + (ok ? row : 0)) * h_qk + hq) * (int64_t)D + (ok ? f : 0), ok,
-                       piece);
-    };
+    // ---- phase 2: Gram matrices K K^T and Q K^T (raw inputs), lower 16x16 tiles, kept in
+    //      registers for every V head of this QK head
+    constexpr int NTL = RT * (RT + 1) / 2;
+    constexpr int NTW = (NTL + 3) / 4;   // tiles per wave
+    constexpr int NPG = NS == 1 ? 1 : 3; // split passes of a Gram product
+    floatx4 gk[NTW], gq[NTW];
+#pragma unroll
+    for (int i = 0; i < NTW; ++i) {
+        gk[i] = floatx4{0.f, 0.f, 0.f, 0.f};
+        gq[i] = gk[i];
+        const int ti = w + 4 * i;
+        if (ti < NTL) {
+            int rt, ct;
+            tri_tile(ti, rt, ct);
+            floatx4 ak[NPG], aq[NPG];
+#pragma unroll
+            for (int p = 0; p < NPG; ++p) ak[p] = aq[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kt = 0; kt < KTD; ++kt) {
+                bf16x8 a_k[NS], a_q[NS], b[NS];
+#pragma unroll
+                for (int part = 0; part < NS; ++part) {
+                    a_k[part] = *reinterpret_cast<const bf16x8*>(&s_kq(0, part, 16 * rt + lr, 32 * kt + 8 * lg));
+                    a_q[part] = *reinterpret_cast<const bf16x8*>(&s_kq(1, part, 16 * rt + lr, 32 * kt + 8 * lg));
+                    b[part] = *reinterpret_cast<const bf16x8*>(&s_kq(0, part, 16 * ct + lr, 32 * kt + 8 * lg));
+                }
+                mfma_split_acc<NS, NS>(a_k, b, ak);
+                mfma_split_acc<NS, NS>(a_q, b, aq);
+            }
+#pragma unroll
+            for (int p = 0; p < NPG; ++p) {
+                gk[i] += ak[p];
+                gq[i] += aq[p];
+            }
+        }
+    }
+    __syncthreads();  // the K / Q buffer becomes A / T below
 
-    constexpr int NTL = RT * (RT + 1) / 2;  // lower-triangular 16x16 tiles of a C x C matrix
     for (int gi = 0; gi < grp; ++gi) {
         const int hv = hq * grp + gi;
         const int64_t vh = (seq * nch + c) * h_v + hv;
 
-        // ---- phase 1: gate prefix sums gamma (wave 0), per-token scalars
+        // ---- phase 3: gate prefix sums gamma (wave 0), write strengths
         if (w == 0) {
-            constexpr int E = (C + 63) / 64;
+            constexpr int E = (CP + 63) / 64;
             float gv[E], bv[E];
             float run = 0.f;
 #pragma unroll
@@ -424,51 +482,48 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 #pragma unroll
             for (int e = 0; e < E; ++e) {
                 const int i = l * E + e;
-                if (i < C) {
+                if (i < CP) {
                     s_gam[i] = gv[e] + excl;
                     s_beta[i] = bv[e];
                 }
             }
         }
         __syncthreads();
+
+        // ---- per-token scalars a = Gamma r_k, s = r_k exp(gamma_C - gamma), o = Gamma r_q
+        //      and Gamma_C (padded tokens carry r_k = r_q = 0, so their scalars are zero)
         {
-            const float gam_c = s_gam[C - 1];  // padded tokens add g = 0
-            if (tid < C) {
+            float* scp = reinterpret_cast<float*>(ws + L.sc + (size_t)vh * G::SC_BYTES);
+            const float gam_c = s_gam[CP - 1];  // padded tokens add g = 0
+            if (tid < CP) {
                 const int i = tid;
                 const float Gi = expf(s_gam[i]);
-                float4 o;
-                o.x = s_beta[i];                         // beta_r
-                o.y = s_beta[i] * Gi * s_rk[i];          // beta_r Gamma_r r_k,r
-                o.z = Gi * s_rq[i];                      // Gamma_r r_q,r
-                o.w = s_rk[i] * expf(gam_c - s_gam[i]);  // r_k,r exp(gamma_C - gamma_r)
-                reinterpret_cast<float4*>(ws + L.sc + (size_t)vh * G::SC_BYTES)[i] = o;
+                scp[i] = Gi * s_rk[i];
+                scp[CP + i] = s_rk[i] * expf(gam_c - s_gam[i]);
+                scp[2 * CP + i] = Gi * s_rq[i];
             }
-            if (tid == 0) reinterpret_cast<float*>(ws + L.gc)[vh] = expf(gam_c);
+            if (tid == 0) scp[3 * CP] = expf(gam_c);
         }
 
-        // ---- phase 2: A = strictly lower (beta_r exp(gamma_r - gamma_s) r_k,r r_k,s k_r . k_s)
-        for (int ti = w; ti < NTL; ti += 4) {
-            int rt, ct;
-            tri_tile(ti, rt, ct);
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        // ---- phase 4: A = strictly lower (beta_r exp(gamma_r - gamma_s) r_k,r r_k,s k_r . k_s)
 #pragma unroll
-            for (int kt = 0; kt < KTD; ++kt) {
-                bf16x8 a[NS], b[NS];
-                qk_frag(k, 16 * rt + lr, kt, a);
-                qk_frag(k, 16 * ct + lr, kt, b);
-                acc = mfma_split<NS, NS>(a, b, acc);
-            }
+        for (int i = 0; i < NTW; ++i) {
+            const int ti = w + 4 * i;
+            if (ti < NTL) {
+                int rt, ct;
+                tri_tile(ti, rt, ct);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rt + 4 * lg + e, s = 16 * ct + lr;
-                float a = 0.f;
-                if (s < r) a = s_beta[r] * __expf(s_gam[r] - s_gam[s]) * s_rk[r] * s_rk[s] * acc[e];
-                s_a[r][s] = a;
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rt + 4 * lg + e, s = 16 * ct + lr;
+                    float a = 0.f;
+                    if (s < r) a = s_beta[r] * __expf(s_gam[r] - s_gam[s]) * s_rk[r] * s_rk[s] * gk[i][e];
+                    s_a[r][s] = a;
+                }
             }
         }
         __syncthreads();
 
-        // ---- phase 3: diagonal 16x16 blocks of T by forward substitution, one lane per
+        // ---- phase 5: diagonal 16x16 blocks of T by forward substitution, one lane per
         //      column: T[r][s] = delta_rs - sum_{m<r} A[r][m] T[m][s]
         if (tid < NB * 16) {
             const int b = tid >> 4, s = tid & 15;
@@ -485,7 +540,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         }
         __syncthreads();
 
-        // ---- phase 4: off-diagonal blocks, block row by block row:
+        // ---- phase 6: off-diagonal blocks, block row by block row:
         //      T_ij = -T_ii (sum_{m=j}^{i-1} A_im T_mj)   (fp32 MFMA)
         for (int i = 1; i < NB; ++i) {
             for (int j = w; j < i; j += 4) {
@@ -510,77 +565,86 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             __syncthreads();
         }
 
-        // ---- write a lower-triangular C x C matrix as hi/lo MFMA A-operand tiles
-        auto write_tiles = [&](float(*src)[CS], char* base) {
-            for (int ti = w; ti < RT * KTC; ti += 4) {
-                const int rt = ti / KTC, kt = ti % KTC;
-                if (32 * kt > 16 * rt + 15) continue;  // above the diagonal: never read
-                const int r = 16 * rt + lr, s0 = 32 * kt + 8 * lg;
+        // ---- a lower-triangular CP x CP matrix (times a column scaling) as compact hi/lo
+        //      A-operand tiles with the permuted token order in k
+        auto write_tiles = [&](float(*src)[CS], bool col_beta, char* base) {
+            for (int ti = w; ti < NTRI; ti += 4) {
+                int rt = 0;
+                while (tri_off(rt + 1) <= ti) ++rt;
+                const int kt = ti - tri_off(rt);
+                const int r = 16 * rt + lr;
                 bf16x8 hi, lo;
 #pragma unroll
-                for (int e = 0; e < 8; ++e) {
-                    const int s = s0 + e;
-                    const float x = (s <= r && s < C) ? src[r][s] : 0.f;
+                for (int j = 0; j < 8; ++j) {
+                    const int s = tok_of(kt, lg, j);
+                    float x = s <= r ? src[r][s] : 0.f;
+                    if (col_beta) x *= s_beta[s];
                     __bf16 h, lw;
                     split_bf16(x, h, lw);
-                    hi[e] = h;
-                    lo[e] = lw;
+                    hi[j] = h;
+                    lo[j] = lw;
                 }
                 *reinterpret_cast<bf16x8*>(base + (size_t)(2 * ti) * 1024 + l * 16) = hi;
                 *reinterpret_cast<bf16x8*>(base + (size_t)(2 * ti + 1) * 1024 + l * 16) = lo;
             }
         };
-        write_tiles(s_t, ws + L.t + (size_t)vh * G::TP_BYTES);
+        // T' = T diag(beta)
+        write_tiles(s_t, true, ws + L.tt + (size_t)vh * G::TRI_BYTES);
 
-        // ---- phase 5: Ptil = lower (exp(gamma_r - gamma_s) r_q,r r_k,s q_r . k_s), into A's space
-        for (int ti = w; ti < NTL; ti += 4) {
-            int rt, ct;
-            tri_tile(ti, rt, ct);
-            floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+        // ---- phase 7: Ptil = lower (exp(gamma_r - gamma_s) r_q,r r_k,s q_r . k_s), into A's
+        //      space (A is no longer read)
 #pragma unroll
-            for (int kt = 0; kt < KTD; ++kt) {
-                bf16x8 a[NS], b[NS];
-                qk_frag(q, 16 * rt + lr, kt, a);
-                qk_frag(k, 16 * ct + lr, kt, b);
-                acc = mfma_split<NS, NS>(a, b, acc);
-            }
+        for (int i = 0; i < NTW; ++i) {
+            const int ti = w + 4 * i;
+            if (ti < NTL) {
+                int rt, ct;
+                tri_tile(ti, rt, ct);
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                const int r = 16 * rt + 4 * lg + e, s = 16 * ct + lr;
-                float p = 0.f;
-                if (s <= r) p = __expf(s_gam[r] - s_gam[s]) * s_rq[r] * s_rk[s] * acc[e];
-                s_a[r][s] = p;
+                for (int e = 0; e < 4; ++e) {
+                    const int r = 16 * rt + 4 * lg + e, s = 16 * ct + lr;
+                    float p = 0.f;
+                    if (s <= r) p = __expf(s_gam[r] - s_gam[s]) * s_rq[r] * s_rk[s] * gq[i][e];
+                    s_a[r][s] = p;
+                }
             }
         }
         __syncthreads();
-        write_tiles(s_a, ws + L.p + (size_t)vh * G::TP_BYTES);
+        write_tiles(s_a, false, ws + L.pt + (size_t)vh * G::TRI_BYTES);
         __syncthreads();
     }
 }
 
 // =============================================================================== scan
 template <int D, int C, typename TIn>
-struct ChunkRegs {
+struct ScanGeo {
     using G = Geo<D, C, std::is_same<TIn, float>::value>;
-    using Raw = typename RawFrag<TIn>::type;
-    // bf16 K and Q chunks are staged through LDS with coalesced loads (a 16-lane group reads
-    // one contiguous 256-byte row); fp32 inputs (small head dims) load MFMA fragments
-    // directly and split them at use.
-    static constexpr bool KQ_LDS = !std::is_same<TIn, float>::value;
-    static constexpr int RTW = (G::RT + 3) / 4;          // row tiles per wave
-    static constexpr int MTW = (G::MT + 3) / 4;          // state row tiles per wave
-    static constexpr int NPIECE = C * D / 8;             // 16-byte pieces of a K (or Q) chunk
-    static constexpr int KQP = (NPIECE + 255) / 256;     // pieces per thread
-    static constexpr int NFRAG = KQ_LDS ? 1 : RTW;
-    static constexpr int NKTD = KQ_LDS ? 1 : G::KTD;
-    u32x4 kp[KQ_LDS ? KQP : 1], qp[KQ_LDS ? KQP : 1];     // K, Q pieces of the chunk (LDS path)
-    Raw ka[NFRAG][NKTD], qa[NFRAG][NKTD];                 // K, Q fragments (direct path)
-    TIn vv[RTW][4];                                       // V in accumulator layout, as loaded
-    floatx4 scv;                                          // one token's scalars (LDS path)
-    floatx4 sc[KQ_LDS ? 1 : RTW][4];                      // per-token scalars (direct path)
-    bf16x8 tf[RTW][G::KTC][2], pf[RTW][G::KTC][2];        // T, Ptil (hi, lo)
-    bf16x8 kt[KQ_LDS ? 1 : MTW][KQ_LDS ? 1 : G::KTC][G::NS];  // K^T tiles (direct path)
-    float gc;                                             // Gamma_C
+    // Two operand sets alternate (the next chunk's loads fly while this chunk computes)
+    // when both fit the register file; at C = 128 one set is loaded per chunk.
+    static constexpr bool DB = C <= 64;
+    // T' tiles (2 NTRI pieces of 1 KB) are staged into LDS by the output waves, NTS
+    // pieces each, one chunk ahead of the chain waves that read them.
+    static constexpr int NTS = (2 * G::NTRI + G::NOW - 1) / G::NOW;
+};
+
+// Operands a chain wave loads for one chunk c (and the K rows of chunk c + 1).
+template <int D, int C, typename TIn>
+struct ChainSet {
+    using G = Geo<D, C, std::is_same<TIn, float>::value>;
+    typename RawFrag<TIn>::type kr[G::RT][G::KTH];  // K rows of chunk c + 1 (A fragments)
+    bf16x8 ktf[G::MTH][G::KTC][G::NS];                // K^T tiles of this wave's state rows
+    TIn vv[G::RT][4];                                 // V in accumulator layout, as loaded
+    floatx4 av[G::RT], sv[G::RT];                     // scalars a and s of the accumulator rows
+    float gc;                                         // Gamma_C
+};
+
+// Operands an output wave loads for window j (finishing chunk j - 1, starting chunk j).
+template <int D, int C, typename TIn>
+struct OutSet {
+    using G = Geo<D, C, std::is_same<TIn, float>::value>;
+    typename RawFrag<TIn>::type qr[G::RTO][G::KTD];  // Q rows of chunk j (A fragments)
+    bf16x8 pf[G::RTO][G::KTC][2];                     // Ptil of chunk j - 1, zero past the diagonal
+    floatx4 ov[G::RTO];                               // scalars o of chunk j - 1
+    bf16x8 tst[ScanGeo<D, C, TIn>::NTS];             // T' pieces of chunk j + 1, for LDS
 };
 
 template <int D, int C, typename TIn>
@@ -592,33 +656,30 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
 {
     constexpr bool F32IN = std::is_same<TIn, float>::value;
     using G = Geo<D, C, F32IN>;
-    using R = ChunkRegs<D, C, TIn>;
-    constexpr int DP = G::DP, CP = G::CP, RT = G::RT, KTC = G::KTC, KTD = G::KTD, MT = G::MT;
-    constexpr int NS = G::NS, RTW = R::RTW, MTW = R::MTW;
-    constexpr bool KQ_LDS = R::KQ_LDS;
-    constexpr int NCB = D / 16;
-    constexpr int MS = DP + 8;  // LDS stride of M^T rows (bf16)
-    constexpr int XS = CP + 8;  // LDS stride of X^T, U^T, W^T rows (bf16)
-    constexpr int KS = DP + 8;  // LDS stride of K / Q chunk rows (bf16)
+    using SG = ScanGeo<D, C, TIn>;
+    using Raw = typename RawFrag<TIn>::type;
+    using CS = ChainSet<D, C, TIn>;
+    using OS = OutSet<D, C, TIn>;
+    constexpr int CP = G::CP, RT = G::RT, KTC = G::KTC, KTD = G::KTD, NS = G::NS;
+    constexpr int NTRI = G::NTRI, NCH = G::NCH, KTH = G::KTH, MTH = G::MTH;
+    constexpr int NOW = G::NOW, RTO = G::RTO, NTS = SG::NTS;
+    constexpr int ES = sizeof(TIn);
+    constexpr int NP = NS == 1 ? 2 : 3;  // split passes of (q/k piece) x (hi, lo operand)
 
-    // B operands built in-kernel, stored transposed (value channel major) so that a lane's
-    // eight k-consecutive elements are contiguous; and the K / Q chunk (A operands).
-    __shared__ __align__(16) __bf16 s_m[2][16][MS];  // state block (hi, lo)
-    __shared__ __align__(16) __bf16 s_x[2][16][XS];  // X
-    __shared__ __align__(16) __bf16 s_u[2][16][XS];  // U
-    __shared__ __align__(16) __bf16 s_w[2][16][XS];  // W = diag(r_k exp(gamma_C - gamma)) U
-    // K rows (two buffers by chunk parity: read up to the state update), Q rows (read only
-    // before the first barrier) and per-token scalars (two buffers).
-    __shared__ __align__(16) __bf16 s_k[2][KQ_LDS ? C : 1][KQ_LDS ? KS : 8];
-    __shared__ __align__(16) __bf16 s_q[KQ_LDS ? C : 1][KQ_LDS ? KS : 8];
-    __shared__ __align__(16) floatx4 s_sc[2][KQ_LDS ? C : 1];
+    // Exchange buffers, one 16-byte value per lane per slot, double-buffered by chunk parity:
+    // partial K M0 of each chain wave, the state's B fragments (hi, lo), U's B fragments,
+    // and the T' tiles.
+    __shared__ __align__(16) floatx4 s_xp[2][NCH][RT][64];
+    __shared__ __align__(16) bf16x8 s_mf[2][KTD][2][64];
+    __shared__ __align__(16) bf16x8 s_uf[2][KTC][2][64];
+    __shared__ __align__(16) bf16x8 s_tf[2][2 * NTRI][64];
 
     // Workgroups that share a QK head run on the same XCD (blockIdx % 8 picks the XCD), so
-    // their common K/Q/T/Ptil reads meet in one L2.
+    // their common K/Q/T'/Ptil reads meet in one L2.
     int64_t lin = blockIdx.x;
     if (nblocks % 8 == 0) lin = (int64_t)(blockIdx.x % 8) * (nblocks / 8) + blockIdx.x / 8;
-    const int cb = (int)(lin % NCB);
-    const int64_t nh = lin / NCB;
+    const int cb = (int)(lin % (D / 16));
+    const int64_t nh = lin / (D / 16);
     const int64_t seq = nh / h_v;
     const int h = (int)(nh - seq * h_v);
     const int hq = h / (h_v / h_qk);
@@ -626,368 +687,383 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
     const int64_t nch = L.nch;
 
-    // Zero every LDS operand buffer once: padded k ranges (features >= D, tokens >= C) are
-    // never written and must read as zero.
-    {
-        auto zero = [&](__bf16* z, int n) {
-            for (int i = tid; i < n; i += 256) z[i] = (__bf16)0.f;
+    // Byte strides between consecutive tokens of q/k, v and out.
+    const int64_t row_qk = (int64_t)h_qk * D * ES;
+    const int64_t row_v = (int64_t)h_v * D * ES;
+    const int64_t row_o = (int64_t)h_v * D * 4;
+    auto clampc = [&](int64_t c) { return c < 0 ? 0 : (c < nch ? c : nch - 1); };
+    auto tok0_of = [&](int64_t c) { return seq * T + c * C; };
+    auto rows_of = [&](int64_t c) { return (T - c * C) < C ? (T - c * C) : (int64_t)C; };
+    auto vh_of = [&](int64_t c) { return (size_t)((seq * nch + c) * h_v + h); };
+    auto sc_rsrc = [&](int64_t c) { return make_rsrc(ws + L.sc + vh_of(c) * G::SC_BYTES, G::SC_BYTES); };
+    // K or Q rows of chunk c as A fragments: row tile rt, feature k tile kt (features past D
+    // and rows past the sequence read zero).
+    auto qk_rsrc = [&](const TIn* base, int64_t c) {
+        return make_rsrc(base + (tok0_of(c) * h_qk + hq) * (int64_t)D, (rows_of(c) - 1) * row_qk + D * ES);
+    };
+    // The feature test depends on the lane (only D = 16 pads), so it selects between two
+    // constants and is added, rather than guarding the address computation: lane-divergent
+    // branches anywhere in this kernel would let the register allocator place copies under
+    // a partial exec mask.
+    auto qk_off = [&](int rt, int kt) {
+        const int f = 32 * kt + 8 * lg;
+        const uint32_t pad = (rt < RT && f < D) ? 0u : OOR;
+        return (int)((uint32_t)((16 * rt + lr) * row_qk) + (uint32_t)(f * ES) + pad);
+    };
+    // A full wait: nothing left in flight, so the compiler's wait bookkeeping starts clean
+    // at the next chunk (no loop-carried loads that would force early waits).
+    auto settle = [&]() { __builtin_amdgcn_s_waitcnt(0); };
+
+    if (w < NCH) {
+        // ======================================================= chain wave hh
+        const int hh = w;
+        // The state block through buffer resources: padded features (D = 16) fall outside
+        // the range, and a missing initial state is an empty range, so both read zero.
+        const int64_t sbase = nh * (int64_t)D * D;
+        auto st_off = [&](int mt, int e) {
+            const int f = feat_of(mt, 4 * lg + e);
+            return (int)((uint32_t)((f * D + cb * 16 + lr) * 4) + (f < D ? 0u : OOR));
         };
-        zero(&s_m[0][0][0], 2 * 16 * MS);
-        zero(&s_x[0][0][0], 2 * 16 * XS);
-        zero(&s_u[0][0][0], 2 * 16 * XS);
-        zero(&s_w[0][0][0], 2 * 16 * XS);
-        if constexpr (KQ_LDS) {
-            zero(&s_k[0][0][0], 2 * C * KS);
-            zero(&s_q[0][0], C * KS);
+        floatx4 macc[MTH];  // state tiles hh * MTH + i
+        {
+            const auto r = make_rsrc(state_in + (state_in ? sbase : 0), state_in ? (int64_t)D * D * 4 : 0);
+#pragma unroll
+            for (int i = 0; i < MTH; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) macc[i][e] = buf_elem<float>(r, st_off(hh * MTH + i, e));
         }
-    }
-    __syncthreads();
-
-    // Four accumulator rows of one column, split, as two 8-byte LDS stores (hi, lo).
-    auto put4 = [&](__bf16* hi_row, __bf16* lo_row, floatx4 val) {
-        bf16x4 hi, lo;
+        bf16x8 mf[KTH][2];  // the state as B fragments (hi, lo) of this wave's d k tiles
+        auto split_state = [&]() {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            __bf16 hh, ll;
-            split_bf16(val[e], hh, ll);
-            hi[e] = hh;
-            lo[e] = ll;
-        }
-        *reinterpret_cast<bf16x4*>(hi_row) = hi;
-        *reinterpret_cast<bf16x4*>(lo_row) = lo;
-    };
-
-    // State block in accumulator layout: tile mt = w + 4 i holds M[16 mt + 4 lg + e][cb 16 + lr].
-    floatx4 macc[MTW];
-    const int64_t sbase = nh * (int64_t)D * D;
-    auto store_m_lds = [&](int i, int mt) {
-        put4(&s_m[0][lr][16 * mt + 4 * lg], &s_m[1][lr][16 * mt + 4 * lg], macc[i]);
-    };
+            for (int kk = 0; kk < KTH; ++kk) pair_to_frag(macc[2 * kk], macc[2 * kk + 1], mf[kk][0], mf[kk][1]);
+        };
+        auto load_k = [&](Raw (*kr)[KTH], int64_t c) {
+            const auto r = qk_rsrc(k, clampc(c));
 #pragma unroll
-    for (int i = 0; i < MTW; ++i) {
-        const int mt = w + 4 * i;
-        if (mt < MT) {
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-            for (int e = 0; e < 4; ++e)
-                macc[i][e] = state_in ? state_in[sbase + (int64_t)(16 * mt + 4 * lg + e) * D + cb * 16 + lr]
-                                      : 0.f;
-            store_m_lds(i, mt);
-        }
-    }
-
-    // Byte strides and this lane's fixed byte offsets inside each per-chunk buffer range.
-    constexpr int ES = sizeof(TIn);
-    const int64_t row_qk = (int64_t)h_qk * D * ES;  // between consecutive tokens of q, k
-    const int64_t row_v = (int64_t)h_v * D * ES;    // ... of v
-    const int64_t row_o = (int64_t)h_v * D * 4;     // ... of out
-    int off_v[RTW][4], off_o[RTW][4];
+                for (int kk = 0; kk < KTH; ++kk) kr[rt][kk] = buf_raw_frag<TIn>(r, qk_off(rt, hh * KTH + kk));
+        };
+        auto load = [&](CS& x, int64_t c) {
+            load_k(x.kr, c + 1);
+            c = clampc(c);
+            const auto r_v = make_rsrc(v + (tok0_of(c) * h_v + h) * (int64_t)D + cb * 16,
+                                       (rows_of(c) - 1) * row_v + 16 * ES);
+            const auto rs = sc_rsrc(c);
 #pragma unroll
-    for (int i = 0; i < RTW; ++i)
+            for (int rt = 0; rt < RT; ++rt) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-            const int rr = 16 * (w + 4 * i) + 4 * lg + e;
-            off_v[i][e] = (int)(rr * row_v) + lr * ES;
-            off_o[i][e] = (int)(rr * row_o) + lr * 4;
-        }
-
-    auto load = [&](R& x, int64_t c) {
-        c = c < nch ? c : nch - 1;  // past the end: reload the last chunk (never computed)
-        const int64_t c0 = c * C;
-        const int64_t tok0 = seq * T + c0;
-        const int64_t rows = (T - c0) < C ? (T - c0) : C;  // tokens of this chunk
-        const int64_t vh = (seq * nch + c) * h_v + h;
-        const auto r_t = make_rsrc(ws + L.t + (size_t)vh * G::TP_BYTES, G::TP_BYTES);
-        const auto r_p = make_rsrc(ws + L.p + (size_t)vh * G::TP_BYTES, G::TP_BYTES);
-        const auto r_sc = make_rsrc(ws + L.sc + (size_t)vh * G::SC_BYTES, G::SC_BYTES);
-        const auto r_kt = make_rsrc(ws + L.kt + (size_t)((seq * nch + c) * h_qk + hq) * G::KT_BYTES,
-                                    G::KT_BYTES);
-        // q / k rows of QK head hq and the v block of this workgroup; rows past the end
-        // fall outside the range and read zero.
-        const int64_t kq_bytes = (rows - 1) * row_qk + D * ES;
-        const auto r_k = make_rsrc(k + (tok0 * h_qk + hq) * (int64_t)D, kq_bytes);
-        const auto r_q = make_rsrc(q + (tok0 * h_qk + hq) * (int64_t)D, kq_bytes);
-        const auto r_v = make_rsrc(v + (tok0 * h_v + h) * (int64_t)D + cb * 16, (rows - 1) * row_v + 16 * ES);
-        if constexpr (KQ_LDS) {
-#pragma unroll
-            for (int p = 0; p < R::KQP; ++p) {
-                const int pidx = tid + 256 * p;
-                const int r = (pidx / (D / 8)) % C, f = (pidx % (D / 8)) * 8;
-                const int off = (int)(r * row_qk) + f * ES;
-                x.kp[p] = buf_u32x4(r_k, off);
-                x.qp[p] = buf_u32x4(r_q, off);
+                for (int e = 0; e < 4; ++e)
+                    x.vv[rt][e] = buf_elem<TIn>(r_v, (int)((16 * rt + 4 * lg + e) * row_v) + lr * ES);
+                x.av[rt] = buf_floatx4(rs, (16 * rt + 4 * lg) * 4);
+                x.sv[rt] = buf_floatx4(rs, CP * 4 + (16 * rt + 4 * lg) * 4);
             }
-            x.scv = buf_floatx4(r_sc, (tid % C) * 16);
-        }
+            const auto r_kt = make_rsrc(ws + L.kt + (size_t)((seq * nch + c) * h_qk + hq) * G::KT_BYTES,
+                                        G::KT_BYTES);
 #pragma unroll
-        for (int i = 0; i < RTW; ++i) {
-            const int rt = w + 4 * i;
-            if (rt >= RT) continue;
-            if constexpr (!KQ_LDS) {
-                // Padded features (f >= D) read zero through an out-of-range offset.
-#pragma unroll
-                for (int kt = 0; kt < KTD; ++kt) {
-                    const int f = 32 * kt + 8 * lg;
-                    const int off = f < D ? (int)((16 * rt + lr) * row_qk) + f * ES : 0x7fffffff - 64;
-                    x.ka[i][kt] = buf_raw_frag<TIn>(r_k, off);
-                    x.qa[i][kt] = buf_raw_frag<TIn>(r_q, off);
-                }
-            }
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                x.vv[i][e] = buf_elem<TIn>(r_v, off_v[i][e]);
-                if constexpr (!KQ_LDS) x.sc[i][e] = buf_floatx4(r_sc, (16 * rt + 4 * lg + e) * 16);
-            }
-#pragma unroll
-            for (int kt = 0; kt < KTC; ++kt) {
-                if (32 * kt > 16 * rt + 15) continue;
-                const int o = (rt * KTC + kt) * 2 * 1024 + l * 16;
-                x.tf[i][kt][0] = buf_bf16x8(r_t, o);
-                x.tf[i][kt][1] = buf_bf16x8(r_t, o + 1024);
-                x.pf[i][kt][0] = buf_bf16x8(r_p, o);
-                x.pf[i][kt][1] = buf_bf16x8(r_p, o + 1024);
-            }
-        }
-        if constexpr (!KQ_LDS) {
-#pragma unroll
-            for (int i = 0; i < MTW; ++i) {
-                const int mt = w + 4 * i;
-                if (mt >= MT) continue;
+            for (int i = 0; i < MTH; ++i)
 #pragma unroll
                 for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
                     for (int part = 0; part < NS; ++part)
-                        x.kt[i][kt][part] = buf_bf16x8(r_kt, ((mt * KTC + kt) * NS + part) * 1024 + l * 16);
-            }
-        }
-        // A vector load (every lane the same word), not a scalar one: scalar loads share the
-        // LDS wait counter, and the wait before each barrier would stall on its round trip.
-        x.gc = buf_elem<float>(make_rsrc(ws + L.gc + (size_t)vh * 4, 4), 0);
-    };
+                        x.ktf[i][kt][part] =
+                            buf_bf16x8(r_kt, (((hh * MTH + i) * KTC + kt) * NS + part) * 1024 + l * 16);
+            // A vector load (every lane the same word), not a scalar one: scalar loads share
+            // the LDS wait counter, and the wait before each barrier would stall on them.
+            x.gc = buf_elem<float>(rs, 3 * CP * 4);
+        };
 
-    // K / Q pieces and scalars of a chunk into LDS buffer `b` (rows past the end arrived as
-    // zero).
-    auto store_kq = [&](const R& x, int b) {
-        if constexpr (KQ_LDS) {
+        // This wave's part of K M0 for the chunk whose K rows are given.
+        floatx4 pp[RT];
+        auto partial_km = [&](const Raw (*kr)[KTH]) {
 #pragma unroll
-            for (int p = 0; p < R::KQP; ++p) {
-                const int pidx = tid + 256 * p;
-                if (R::NPIECE % 256 != 0 && pidx >= R::NPIECE) continue;
-                const int r = pidx / (D / 8), f = (pidx % (D / 8)) * 8;
-                *reinterpret_cast<u32x4*>(&s_k[b][r][f]) = x.kp[p];
-                *reinterpret_cast<u32x4*>(&s_q[r][f]) = x.qp[p];
-            }
-            if (tid < C) s_sc[b][tid] = x.scv;
-        }
-    };
-
-    // Outputs of a chunk wait in registers and are stored after the next wait for loads:
-    // vector-memory loads and stores share one completion counter, so a store issued just
-    // before that wait would stall it for the write round trip.
-    floatx4 opend[RTW];
-    auto store_out = [&](int64_t c) {
-        const int64_t c0 = c * C;
-        const int64_t rows = (T - c0) < C ? (T - c0) : C;
-        const auto r_o = make_rsrc(out + ((seq * T + c0) * h_v + h) * (int64_t)D + cb * 16,
-                                   (rows - 1) * row_o + 64);
+            for (int rt = 0; rt < RT; ++rt) {
+                floatx4 acc[2][NP];
 #pragma unroll
-        for (int i = 0; i < RTW; ++i) {
-            const int rt = w + 4 * i;
-            if (rt >= RT) continue;
+                for (int j = 0; j < 2; ++j)
 #pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                // Element to a scalar first: a bit cast of a vector-element expression picked
-                // element 0 for every e in this compiler.
-                const float val = opend[i][e];
-                __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), r_o, off_o[i][e], 0, 0);
-            }
-        }
-    };
-
-    // Scalars {beta, beta Gamma r_k, Gamma r_q, r_k exp(gamma_C - gamma)} of accumulator
-    // row e of row tile w + 4 i.
-    auto scal = [&](const R& x, int b, int i, int e) -> floatx4 {
-        if constexpr (KQ_LDS) return s_sc[b][16 * (w + 4 * i) + 4 * lg + e];
-        else return x.sc[i][e];
-    };
-
-    auto compute = [&](const R& x, int b) {
-        // (1) K M0 and Q M0; X = diag(beta) V - diag(beta Gamma r_k) K M0
-        floatx4 qm[RTW];
+                    for (int p = 0; p < NP; ++p) acc[j][p] = floatx4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-        for (int i = 0; i < RTW; ++i) {
-            const int rt = w + 4 * i;
-            if (rt >= RT) continue;
-            // Independent accumulators per k-tile parity and split pass (summed below), so
-            // consecutive MFMAs do not wait on each other's results.
-            constexpr int NP = NS + 1;  // passes per k tile: M hi, M lo (and K lo)
-            floatx4 kacc[2][NP], qacc[2][NP];
-#pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int pp = 0; pp < NP; ++pp) kacc[j][pp] = qacc[j][pp] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kt = 0; kt < KTD; ++kt) {
-                bf16x8 mb[2], ka[NS], qa[NS];
-                mb[0] = *reinterpret_cast<const bf16x8*>(&s_m[0][lr][32 * kt + 8 * lg]);
-                mb[1] = *reinterpret_cast<const bf16x8*>(&s_m[1][lr][32 * kt + 8 * lg]);
-                if constexpr (KQ_LDS) {
-                    ka[0] = *reinterpret_cast<const bf16x8*>(&s_k[b][16 * rt + lr][32 * kt + 8 * lg]);
-                    qa[0] = *reinterpret_cast<const bf16x8*>(&s_q[16 * rt + lr][32 * kt + 8 * lg]);
-                } else {
-                    to_pieces(x.ka[i][kt], ka);
-                    to_pieces(x.qa[i][kt], qa);
+                for (int kk = 0; kk < KTH; ++kk) {
+                    bf16x8 ka[NS];
+                    to_pieces(kr[rt][kk], ka);
+                    mfma_split_acc<NS, 2>(ka, mf[kk], acc[kk & 1]);
                 }
-                mfma_split_acc<NS, 2>(ka, mb, kacc[kt & 1]);
-                mfma_split_acc<NS, 2>(qa, mb, qacc[kt & 1]);
+                floatx4 s = acc[0][0];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int p = (j == 0 ? 1 : 0); p < NP; ++p) s += acc[j][p];
+                pp[rt] = s;
             }
-            floatx4 km = kacc[0][0], qq = qacc[0][0];
+        };
+        auto publish = [&](int par) {
+            if constexpr (NCH > 1) {
 #pragma unroll
-            for (int j = 0; j < 2; ++j)
-#pragma unroll
-                for (int pp = (j == 0 ? 1 : 0); pp < NP; ++pp) {
-                    km += kacc[j][pp];
-                    qq += qacc[j][pp];
-                }
-            qm[i] = qq;
-            floatx4 xv;
-#pragma unroll
-            for (int e = 0; e < 4; ++e)
-                xv[e] = scal(x, b, i, e)[0] * raw_to_f32(x.vv[i][e]) - scal(x, b, i, e)[1] * km[e];
-            put4(&s_x[0][lr][16 * rt + 4 * lg], &s_x[1][lr][16 * rt + 4 * lg], xv);
-        }
-        __syncthreads();
-        // (2) U = T X; W = diag(r_k exp(gamma_C - gamma)) U
-#pragma unroll
-        for (int i = 0; i < RTW; ++i) {
-            const int rt = w + 4 * i;
-            if (rt >= RT) continue;
-            floatx4 uacc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-            for (int kt = 0; kt < KTC; ++kt) {
-                if (32 * kt > 16 * rt + 15) continue;
-                bf16x8 xb[2];
-                xb[0] = *reinterpret_cast<const bf16x8*>(&s_x[0][lr][32 * kt + 8 * lg]);
-                xb[1] = *reinterpret_cast<const bf16x8*>(&s_x[1][lr][32 * kt + 8 * lg]);
-                mfma_split_acc<2, 2>(x.tf[i][kt], xb, uacc);
+                for (int rt = 0; rt < RT; ++rt) s_xp[par][hh][rt][l] = pp[rt];
             }
-            const floatx4 u = uacc[0] + uacc[1] + uacc[2];
-            floatx4 wv;
 #pragma unroll
-            for (int e = 0; e < 4; ++e) wv[e] = scal(x, b, i, e)[3] * u[e];
-            put4(&s_u[0][lr][16 * rt + 4 * lg], &s_u[1][lr][16 * rt + 4 * lg], u);
-            put4(&s_w[0][lr][16 * rt + 4 * lg], &s_w[1][lr][16 * rt + 4 * lg], wv);
-        }
-        __syncthreads();
-        // (3) O = diag(Gamma r_q) Q M0 + Ptil U
+            for (int kk = 0; kk < KTH; ++kk)
 #pragma unroll
-        for (int i = 0; i < RTW; ++i) {
-            const int rt = w + 4 * i;
-            if (rt >= RT) continue;
-            floatx4 oacc[3] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) oacc[0][e] = scal(x, b, i, e)[2] * qm[i][e];
-#pragma unroll
-            for (int kt = 0; kt < KTC; ++kt) {
-                if (32 * kt > 16 * rt + 15) continue;
-                bf16x8 ub[2];
-                ub[0] = *reinterpret_cast<const bf16x8*>(&s_u[0][lr][32 * kt + 8 * lg]);
-                ub[1] = *reinterpret_cast<const bf16x8*>(&s_u[1][lr][32 * kt + 8 * lg]);
-                mfma_split_acc<2, 2>(x.pf[i][kt], ub, oacc);
-            }
-            opend[i] = oacc[0] + oacc[1] + oacc[2];
-        }
-        // (4) M <- Gamma_C M + K^T W
-#pragma unroll
-        for (int i = 0; i < MTW; ++i) {
-            const int mt = w + 4 * i;
-            if (mt >= MT) continue;
-            constexpr int NP = NS + 1;
-            floatx4 acc[NP];
-#pragma unroll
-            for (int e = 0; e < 4; ++e) acc[0][e] = x.gc * macc[i][e];
-#pragma unroll
-            for (int pp = 1; pp < NP; ++pp) acc[pp] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kt = 0; kt < KTC; ++kt) {
-                bf16x8 wb[2];
-                wb[0] = *reinterpret_cast<const bf16x8*>(&s_w[0][lr][32 * kt + 8 * lg]);
-                wb[1] = *reinterpret_cast<const bf16x8*>(&s_w[1][lr][32 * kt + 8 * lg]);
-                if constexpr (KQ_LDS) {
-                    // K^T fragment: feature 16 mt + lr, tokens 32 kt + 8 lg + e, read across
-                    // the K rows in LDS (tokens past the chunk are zero rows).
-                    bf16x8 ktf[1];
-#pragma unroll
-                    for (int e = 0; e < 8; ++e) {
-                        const int tok = 32 * kt + 8 * lg + e;
-                        ktf[0][e] = tok < C ? s_k[b][tok][16 * mt + lr] : (__bf16)0.f;
-                    }
-                    mfma_split_acc<1, 2>(ktf, wb, acc);
-                } else {
-                    mfma_split_acc<NS, 2>(x.kt[i][kt], wb, acc);
-                }
-            }
-            floatx4 mnew = acc[0];
-#pragma unroll
-            for (int pp = 1; pp < NP; ++pp) mnew += acc[pp];
-            macc[i] = mnew;
-            store_m_lds(i, mt);
-        }
-    };
+                for (int p = 0; p < 2; ++p) s_mf[par][hh * KTH + kk][p][l] = mf[kk][p];
+        };
 
-    // A full wait: nothing left in flight, so the compiler's wait bookkeeping starts clean
-    // (no loop-carried loads that would force early waits inside the next chunk).
-    auto settle = [&]() { __builtin_amdgcn_s_waitcnt(0); };
+        // One chunk, between the barrier that publishes its inputs and the next one.
+        auto window = [&](const CS& x, int64_t c) {
+            const int par = (int)(c & 1);
+            // X = V - diag(a) K M0, with K M0 the sum of both waves' parts (the same order of
+            // addition in both waves, so both compute identical U)
+            floatx4 xv[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                floatx4 z = pp[rt];
+                if constexpr (NCH > 1) z += s_xp[par][hh ^ 1][rt][l];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xv[rt][e] = raw_to_f32(x.vv[rt][e]) - x.av[rt][e] * z[e];
+            }
+            bf16x8 xf[KTC][2];
+            rows_to_frags<RT, KTC>(xv, xf);
+            // U = T' X (lower triangular: row tile rt uses token k tiles 0 .. rt / 2)
+            floatx4 u[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                floatx4 acc[3];
+#pragma unroll
+                for (int p = 0; p < 3; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kt = 0; 2 * kt <= rt; ++kt) {
+                    const bf16x8 tf[2] = {s_tf[par][2 * (tri_off(rt) + kt)][l],
+                                          s_tf[par][2 * (tri_off(rt) + kt) + 1][l]};
+                    mfma_split_acc<2, 2>(tf, xf[kt], acc);
+                }
+                u[rt] = acc[0] + acc[1] + acc[2];
+            }
+            if (hh == 0) {  // U for the output waves
+                bf16x8 uf[KTC][2];
+                rows_to_frags<RT, KTC>(u, uf);
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) s_uf[par][kt][p][l] = uf[kt][p];
+            }
+            // W = diag(s) U;  M <- Gamma_C M + K^T W
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) u[rt] *= x.sv[rt];
+            bf16x8 wf[KTC][2];
+            rows_to_frags<RT, KTC>(u, wf);
+#pragma unroll
+            for (int i = 0; i < MTH; ++i) {
+                floatx4 acc[NP];
+                acc[0] = x.gc * macc[i];
+#pragma unroll
+                for (int p = 1; p < NP; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt) mfma_split_acc<NS, 2>(x.ktf[i][kt], wf[kt], acc);
+                floatx4 s = acc[0];
+#pragma unroll
+                for (int p = 1; p < NP; ++p) s += acc[p];
+                macc[i] = s;
+            }
+            // The next chunk's partial K M0 (past the last chunk: computed on reloaded rows
+            // and never read).
+            split_state();
+            partial_km(x.kr);
+            publish(par ^ 1);
+        };
 
-    if constexpr (C <= 64) {
-        // Two operand sets alternate: the next chunk's operands load while this chunk
-        // computes, and the wait for them lands at the end of the chunk.
-        // Even chunks use LDS buffer 0, odd chunks buffer 1. Q and buffer (c + 1) & 1 are
-        // last read by chunk c - 1 / before chunk c's first barrier, so they can be refilled
-        // at the end of chunk c.
-        R A, B;
+        split_state();
+        {
+            Raw k0[RT][KTH];
+            load_k(k0, 0);
+            partial_km(k0);
+        }
+        publish(0);
+        CS A;
         load(A, 0);
-        store_kq(A, 0);
-        settle();
-        __syncthreads();
+        if constexpr (SG::DB) {
+            CS B;
+            settle();
+            for (int64_t c = 0;;) {
+                load(B, c + 1);
+                __syncthreads();
+                window(A, c);
+                settle();
+                if (++c >= nch) break;
+                load(A, c + 1);
+                __syncthreads();
+                window(B, c);
+                settle();
+                if (++c >= nch) break;
+            }
+        } else {
 #pragma unroll 1
-        for (int64_t c = 0; c < nch; c += 2) {
-            load(B, c + 1);
-            compute(A, 0);
-            store_kq(B, 1);
-            settle();
-            __syncthreads();
-            store_out(c);
-            if (c + 1 >= nch) break;
-            load(A, c + 2);
-            compute(B, 1);
-            store_kq(A, 0);
-            settle();
-            __syncthreads();
-            store_out(c + 1);
+            for (int64_t c = 0; c < nch; ++c) {
+                if (c > 0) load(A, c);
+                __syncthreads();
+                window(A, c);
+                settle();
+            }
+        }
+        __syncthreads();  // matches the output waves' last window
+
+        {
+            const auto r = make_rsrc(state_out + sbase, (int64_t)D * D * 4);
+#pragma unroll
+            for (int i = 0; i < MTH; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float val = macc[i][e];
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), r, st_off(hh * MTH + i, e), 0, 0);
+                }
         }
     } else {
-        // Two sets of C = 128 operands do not fit the register file: load at the top.
-        R A;
-#pragma unroll 1
-        for (int64_t c = 0; c < nch; ++c) {
-            load(A, c);
-            store_kq(A, (int)(c & 1));
-            settle();
-            __syncthreads();
-            if (c > 0) store_out(c - 1);
-            compute(A, (int)(c & 1));
-            __syncthreads();
-        }
-        store_out(nch - 1);
-    }
+        // ======================================================= output wave ow
+        // Row tiles ow, ow + NOW, ...; one chunk behind the chain waves. Window j finishes
+        // the outputs of chunk j - 1 and starts Q M0 of chunk j.
+        const int ow = w - NCH;
+        floatx4 qm[RTO];  // Q M0 of the chunk being finished
 
+        auto load_t = [&](bf16x8* tst, int64_t c) {
+            const auto r = make_rsrc(ws + L.tt + vh_of(clampc(c)) * G::TRI_BYTES, G::TRI_BYTES);
 #pragma unroll
-    for (int i = 0; i < MTW; ++i) {
-        const int mt = w + 4 * i;
-        if (mt >= MT) continue;
+            for (int m = 0; m < NTS; ++m) {
+                const int pi = ow + NOW * m;
+                tst[m] = buf_bf16x8(r, pi < 2 * NTRI ? pi * 1024 + l * 16 : (int)OOR);
+            }
+        };
+        auto store_t = [&](const bf16x8* tst, int par) {
 #pragma unroll
-        for (int e = 0; e < 4; ++e)
-            state_out[sbase + (int64_t)(16 * mt + 4 * lg + e) * D + cb * 16 + lr] = macc[i][e];
+            for (int m = 0; m < NTS; ++m) {
+                const int pi = ow + NOW * m;
+                if (pi < 2 * NTRI) s_tf[par][pi][l] = tst[m];
+            }
+        };
+        auto load = [&](OS& x, int64_t j) {
+            {
+                const auto r = qk_rsrc(q, clampc(j));
+#pragma unroll
+                for (int i = 0; i < RTO; ++i)
+#pragma unroll
+                    for (int kt = 0; kt < KTD; ++kt) x.qr[i][kt] = buf_raw_frag<TIn>(r, qk_off(ow + NOW * i, kt));
+            }
+            {
+                const int64_t c = clampc(j - 1);
+                const auto r = make_rsrc(ws + L.pt + vh_of(c) * G::TRI_BYTES, G::TRI_BYTES);
+                const auto rs = sc_rsrc(c);
+#pragma unroll
+                for (int i = 0; i < RTO; ++i) {
+                    const int rt = ow + NOW * i;
+#pragma unroll
+                    for (int kt = 0; kt < KTC; ++kt) {
+                        const bool ok = rt < RT && 2 * kt <= rt;
+                        const int o = (tri_off(rt) + kt) * 2048 + l * 16;
+                        x.pf[i][kt][0] = buf_bf16x8(r, ok ? o : (int)OOR);
+                        x.pf[i][kt][1] = buf_bf16x8(r, ok ? o + 1024 : (int)OOR);
+                    }
+                    x.ov[i] = buf_floatx4(rs, rt < RT ? 2 * CP * 4 + (16 * rt + 4 * lg) * 4 : (int)OOR);
+                }
+            }
+            load_t(x.tst, j + 1);
+        };
+        // O = diag(o) Q M0 + Ptil U of chunk c, U from LDS.
+        auto do_out = [&](const OS& x, int64_t c) {
+            const int par = (int)(c & 1);
+            bf16x8 ufr[KTC][2];
+#pragma unroll
+            for (int kt = 0; kt < KTC; ++kt)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) ufr[kt][p] = s_uf[par][kt][p][l];
+            const auto r_o = make_rsrc(out + (tok0_of(c) * h_v + h) * (int64_t)D + cb * 16,
+                                       (rows_of(c) - 1) * row_o + 64);
+#pragma unroll
+            for (int i = 0; i < RTO; ++i) {
+                const int rt = ow + NOW * i;
+                if (rt >= RT) continue;
+                floatx4 acc[3];
+                acc[0] = x.ov[i] * qm[i];
+                acc[1] = acc[2] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt)
+                    if (2 * kt <= rt) mfma_split_acc<2, 2>(x.pf[i][kt], ufr[kt], acc);
+                const floatx4 o = acc[0] + acc[1] + acc[2];
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    // Element to a scalar first: a bit cast of a vector-element expression
+                    // picked element 0 for every e in this compiler.
+                    const float val = o[e];
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), r_o,
+                                                          (int)((16 * rt + 4 * lg + e) * row_o) + lr * 4, 0, 0);
+                }
+            }
+        };
+        // Q M0 of chunk c, the state from LDS.
+        auto do_qm = [&](const OS& x, int64_t c) {
+            const int par = (int)(c & 1);
+            bf16x8 mfr[KTD][2];
+#pragma unroll
+            for (int kt = 0; kt < KTD; ++kt)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) mfr[kt][p] = s_mf[par][kt][p][l];
+#pragma unroll
+            for (int i = 0; i < RTO; ++i) {
+                if (ow + NOW * i >= RT) continue;
+                floatx4 acc[2][NP];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int p = 0; p < NP; ++p) acc[j][p] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kt = 0; kt < KTD; ++kt) {
+                    bf16x8 qa[NS];
+                    to_pieces(x.qr[i][kt], qa);
+                    mfma_split_acc<NS, 2>(qa, mfr[kt], acc[kt & 1]);
+                }
+                floatx4 s = acc[0][0];
+#pragma unroll
+                for (int j = 0; j < 2; ++j)
+#pragma unroll
+                    for (int p = (j == 0 ? 1 : 0); p < NP; ++p) s += acc[j][p];
+                qm[i] = s;
+            }
+        };
+        auto window = [&](const OS& x, int64_t j) {
+            store_t(x.tst, (int)((j + 1) & 1));  // T' of chunk j + 1
+            if (j >= 1) do_out(x, j - 1);
+            if (j < nch) do_qm(x, j);
+        };
+
+        {
+            bf16x8 t0[NTS];
+            load_t(t0, 0);
+            settle();
+            store_t(t0, 0);
+        }
+        OS A;
+        load(A, 0);
+        if constexpr (SG::DB) {
+            OS B;
+            settle();
+            for (int64_t j = 0;;) {
+                load(B, j + 1);
+                __syncthreads();
+                window(A, j);
+                settle();
+                if (++j > nch) break;
+                load(A, j + 1);
+                __syncthreads();
+                window(B, j);
+                settle();
+                if (++j > nch) break;
+            }
+        } else {
+#pragma unroll 1
+            for (int64_t j = 0; j <= nch; ++j) {
+                if (j > 0) load(A, j);
+                __syncthreads();
+                window(A, j);
+                settle();
+            }
+        }
     }
 }
 

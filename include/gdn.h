@@ -120,6 +120,8 @@ size_t gdn_workspace_bytes(const gdn_dims* dims, int32_t chunk);
  * updates are solved jointly (UT transform of the delta-rule updates, WY form) with bf16
  * matrix-core products; the state is carried across chunks on chip. t need not be a
  * multiple of chunk. Needs gdn_workspace_bytes(dims, chunk) bytes of workspace.
+ * GDN_ERR_SHAPE also when chunk * h_v * d_v * 4 + 64 >= 2^30 (one chunk's output rows
+ * must fit 32-bit in-kernel offsets).
  */
 gdn_status gdn_prefill_chunked(const gdn_dims* dims, int32_t chunk, const void* q,
                                const void* k, const void* v, const float* g,
