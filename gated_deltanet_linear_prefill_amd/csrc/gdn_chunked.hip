@@ -77,6 +77,20 @@ __device__ __forceinline__ void split_bf16(float x, __bf16& hi, __bf16& lo)
     lo = (__bf16)(x - (float)hi);
 }
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+typedef float floatx2 __attribute__((ext_vector_type(2)));
+
+// The same split for two values at once, each piece pair packed in one dword (the first
+// value in the low half): one packed conversion gives both hi values, which are widened
+// back with a shift and a mask.
+__device__ __forceinline__ void split2(float x0, float x1, uint32_t* hi, uint32_t* lo)
+{
+    const uint32_t h = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{x0, x1}, bf16x2));
+    const float h0 = __uint_as_float(h << 16), h1 = __uint_as_float(h & 0xffff0000u);
+    *hi = h;
+    *lo = __builtin_bit_cast(uint32_t, __builtin_convertvector(floatx2{x0 - h0, x1 - h1}, bf16x2));
+}
+
 // Wait for this wave's LDS traffic and keep the compiler from moving memory accesses
 // across the point (used between a wave's own LDS write and read-back).
 __device__ __forceinline__ void lds_fence()
@@ -179,23 +193,11 @@ __device__ __forceinline__ void to_pieces(const bf16x8& raw, bf16x8* piece)
 
 __device__ __forceinline__ void to_pieces(const floatx8& raw, bf16x8* piece)
 {
+    uint32_t hi[4], lo[4];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-        __bf16 h, l;
-        split_bf16(raw[e], h, l);
-        piece[0][e] = h;
-        piece[1][e] = l;
-    }
-}
-
-__device__ __forceinline__ float raw_to_f32(uint16_t x)
-{
-    return bf16_bits_to_f32(x);
-}
-
-__device__ __forceinline__ float raw_to_f32(float x)
-{
-    return x;
+    for (int p = 0; p < 4; ++p) split2(raw[2 * p], raw[2 * p + 1], &hi[p], &lo[p]);
+    piece[0] = __builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]});
+    piece[1] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
 }
 
 // Buffer resources: a base address and byte range in scalar registers, re-based once per
@@ -226,12 +228,6 @@ __device__ __forceinline__ floatx4 buf_floatx4(__amdgpu_buffer_rsrc_t r, int off
 
 template <typename TIn>
 __device__ __forceinline__ TIn buf_elem(__amdgpu_buffer_rsrc_t r, int off);
-
-template <>
-__device__ __forceinline__ uint16_t buf_elem<uint16_t>(__amdgpu_buffer_rsrc_t r, int off)
-{
-    return __builtin_amdgcn_raw_buffer_load_b16(r, off, 0, 0);
-}
 
 template <>
 __device__ __forceinline__ float buf_elem<float>(__amdgpu_buffer_rsrc_t r, int off)
@@ -279,16 +275,13 @@ __device__ __forceinline__ void mfma_split_acc(const bf16x8* a, const bf16x8* b,
 __device__ __forceinline__ void pair_to_frag(const floatx4& a0, const floatx4& a1, bf16x8& hi,
                                              bf16x8& lo)
 {
-#pragma unroll
-    for (int e = 0; e < 4; ++e) {
-        __bf16 h, l;
-        split_bf16(a0[e], h, l);
-        hi[e] = h;
-        lo[e] = l;
-        split_bf16(a1[e], h, l);
-        hi[4 + e] = h;
-        lo[4 + e] = l;
-    }
+    uint32_t h[4], l[4];
+    split2(a0[0], a0[1], &h[0], &l[0]);
+    split2(a0[2], a0[3], &h[1], &l[1]);
+    split2(a1[0], a1[1], &h[2], &l[2]);
+    split2(a1[2], a1[3], &h[3], &l[3]);
+    hi = __builtin_bit_cast(bf16x8, u32x4{h[0], h[1], h[2], h[3]});
+    lo = __builtin_bit_cast(bf16x8, u32x4{l[0], l[1], l[2], l[3]});
 }
 
 // Per-row-tile values (RT row tiles of 16 tokens, accumulator layout) as token k-tile
@@ -621,31 +614,52 @@ struct ScanGeo {
     // Two operand sets alternate (the next chunk's loads fly while this chunk computes)
     // when both fit the register file; at C = 128 one set is loaded per chunk.
     static constexpr bool DB = C <= 64;
-    // T' tiles (2 NTRI pieces of 1 KB) are staged into LDS by the output waves, NTS
-    // pieces each, one chunk ahead of the chain waves that read them.
-    static constexpr int NTS = (2 * G::NTRI + G::NOW - 1) / G::NOW;
+    // The output waves stage what both chain waves read into LDS, one chunk ahead: the T'
+    // tiles (2 NTRI pieces of 1 KB, NTS per output wave) and, from the last output wave,
+    // the V block (transposed to channel-major fp32) and the scalars a, s and Gamma_C.
+    static constexpr int CPV = G::CP < 64 ? 64 : G::CP;  // staged token slots
+    static constexpr int TPL = CPV / 64;                  // staged tokens per lane
+    static constexpr int VS = CPV + 4;                    // LDS row stride of the V block
+    // LDS besides the T' tiles; where the tiles do not fit next to it (d = 128 with
+    // C = 128) the chain waves read T' from the workspace instead.
+    static constexpr size_t LDS_REST = (size_t)2 * G::NCH * G::RT * 1024 + (size_t)2 * G::KTD * 2048 +
+                                       (size_t)2 * G::RT * 1024 + (size_t)2 * 16 * VS * 4 +
+                                       (size_t)2 * 2 * CPV * 4 + 16;
+    static constexpr bool TLDS = LDS_REST + (size_t)2 * 2 * G::NTRI * 1024 <= 160 * 1024;
+    static constexpr int NTS = TLDS ? (2 * G::NTRI + G::NOW - 1) / G::NOW : 1;
 };
 
-// Operands a chain wave loads for one chunk c (and the K rows of chunk c + 1).
+// Operands a chain wave loads for chunk c: K^T tiles of chunk c and K rows of chunk c + 1.
 template <int D, int C, typename TIn>
 struct ChainSet {
     using G = Geo<D, C, std::is_same<TIn, float>::value>;
     typename RawFrag<TIn>::type kr[G::RT][G::KTH];  // K rows of chunk c + 1 (A fragments)
     bf16x8 ktf[G::MTH][G::KTC][G::NS];                // K^T tiles of this wave's state rows
-    TIn vv[G::RT][4];                                 // V in accumulator layout, as loaded
-    floatx4 av[G::RT], sv[G::RT];                     // scalars a and s of the accumulator rows
-    float gc;                                         // Gamma_C
 };
 
-// Operands an output wave loads for window j (finishing chunk j - 1, starting chunk j).
+// Operands an output wave loads for window j (finishing chunk j - 1, starting chunk j),
+// and what it stages for the chain waves' chunk j + 1.
 template <int D, int C, typename TIn>
 struct OutSet {
     using G = Geo<D, C, std::is_same<TIn, float>::value>;
+    using SG = ScanGeo<D, C, TIn>;
     typename RawFrag<TIn>::type qr[G::RTO][G::KTD];  // Q rows of chunk j (A fragments)
     bf16x8 pf[G::RTO][G::KTC][2];                     // Ptil of chunk j - 1, zero past the diagonal
     floatx4 ov[G::RTO];                               // scalars o of chunk j - 1
-    bf16x8 tst[ScanGeo<D, C, TIn>::NTS];             // T' pieces of chunk j + 1, for LDS
+    bf16x8 tst[SG::NTS];                              // T' pieces of chunk j + 1
+    typename RawFrag<TIn>::type vr[SG::TPL][2];      // V rows of chunk j + 1 (16 channels)
+    float sa[SG::TPL], ss[SG::TPL], gc;               // a, s of those tokens; Gamma_C
 };
+
+__device__ __forceinline__ float elem_f32(const bf16x8& r, int e)
+{
+    return (float)r[e];
+}
+
+__device__ __forceinline__ float elem_f32(const floatx8& r, int e)
+{
+    return r[e];
+}
 
 template <int D, int C, typename TIn>
 __global__ void __launch_bounds__(256)
@@ -662,17 +676,21 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     using OS = OutSet<D, C, TIn>;
     constexpr int CP = G::CP, RT = G::RT, KTC = G::KTC, KTD = G::KTD, NS = G::NS;
     constexpr int NTRI = G::NTRI, NCH = G::NCH, KTH = G::KTH, MTH = G::MTH;
-    constexpr int NOW = G::NOW, RTO = G::RTO, NTS = SG::NTS;
+    constexpr int NOW = G::NOW, RTO = G::RTO, NTS = SG::NTS, CPV = SG::CPV, TPL = SG::TPL;
     constexpr int ES = sizeof(TIn);
-    constexpr int NP = NS == 1 ? 2 : 3;  // split passes of (q/k piece) x (hi, lo operand)
 
-    // Exchange buffers, one 16-byte value per lane per slot, double-buffered by chunk parity:
-    // partial K M0 of each chain wave, the state's B fragments (hi, lo), U's B fragments,
-    // and the T' tiles.
+    // LDS, double-buffered by chunk parity, one 16-byte value per lane per slot where a
+    // wave's fragment passes to another wave unchanged:
+    //   s_xp  partial K M0 of each chain wave        s_mf  the state's B fragments (hi, lo)
+    //   s_uf  U (fp32, accumulator layout)           s_tf  T' tiles
+    //   s_vt  V block, channel-major fp32            s_sc  scalars a, s; s_gc Gamma_C
     __shared__ __align__(16) floatx4 s_xp[2][NCH][RT][64];
     __shared__ __align__(16) bf16x8 s_mf[2][KTD][2][64];
-    __shared__ __align__(16) bf16x8 s_uf[2][KTC][2][64];
-    __shared__ __align__(16) bf16x8 s_tf[2][2 * NTRI][64];
+    __shared__ __align__(16) floatx4 s_uf[2][RT][64];
+    __shared__ __align__(16) bf16x8 s_tf[SG::TLDS ? 2 : 1][SG::TLDS ? 2 * NTRI : 1][64];
+    __shared__ __align__(16) float s_vt[2][16][SG::VS];
+    __shared__ __align__(16) float s_sc[2][2][CPV];
+    __shared__ float s_gc[2];
 
     // Workgroups that share a QK head run on the same XCD (blockIdx % 8 picks the XCD), so
     // their common K/Q/T'/Ptil reads meet in one L2.
@@ -701,18 +719,22 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     auto qk_rsrc = [&](const TIn* base, int64_t c) {
         return make_rsrc(base + (tok0_of(c) * h_qk + hq) * (int64_t)D, (rows_of(c) - 1) * row_qk + D * ES);
     };
-    // The feature test depends on the lane (only D = 16 pads), so it selects between two
-    // constants and is added, rather than guarding the address computation: lane-divergent
-    // branches anywhere in this kernel would let the register allocator place copies under
-    // a partial exec mask.
+    // A lane-dependent condition selects between two constants and is added, rather than
+    // guarding the address computation: lane-divergent branches anywhere in this kernel
+    // would let the register allocator place copies under a partial exec mask.
+    auto pad_if = [&](bool in_range) { return in_range ? 0u : OOR; };
     auto qk_off = [&](int rt, int kt) {
         const int f = 32 * kt + 8 * lg;
-        const uint32_t pad = (rt < RT && f < D) ? 0u : OOR;
-        return (int)((uint32_t)((16 * rt + lr) * row_qk) + (uint32_t)(f * ES) + pad);
+        return (int)((uint32_t)((16 * rt + lr) * row_qk) + (uint32_t)(f * ES) + pad_if(rt < RT && f < D));
     };
     // A full wait: nothing left in flight, so the compiler's wait bookkeeping starts clean
     // at the next chunk (no loop-carried loads that would force early waits).
     auto settle = [&]() { __builtin_amdgcn_s_waitcnt(0); };
+    // Four consecutive staged values of accumulator rows 4 lg .. 4 lg + 3 of row tile rt.
+    auto vt4 = [&](int par, int rt) { return *reinterpret_cast<const floatx4*>(&s_vt[par][lr][16 * rt + 4 * lg]); };
+    auto sc4 = [&](int par, int which, int rt) {
+        return *reinterpret_cast<const floatx4*>(&s_sc[par][which][16 * rt + 4 * lg]);
+    };
 
     if (w < NCH) {
         // ======================================================= chain wave hh
@@ -722,7 +744,7 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
         const int64_t sbase = nh * (int64_t)D * D;
         auto st_off = [&](int mt, int e) {
             const int f = feat_of(mt, 4 * lg + e);
-            return (int)((uint32_t)((f * D + cb * 16 + lr) * 4) + (f < D ? 0u : OOR));
+            return (int)((uint32_t)((f * D + cb * 16 + lr) * 4) + pad_if(f < D));
         };
         floatx4 macc[MTH];  // state tiles hh * MTH + i
         {
@@ -744,20 +766,8 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
 #pragma unroll
                 for (int kk = 0; kk < KTH; ++kk) kr[rt][kk] = buf_raw_frag<TIn>(r, qk_off(rt, hh * KTH + kk));
         };
-        auto load = [&](CS& x, int64_t c) {
-            load_k(x.kr, c + 1);
+        auto load_kt = [&](bf16x8 (*ktf)[KTC][NS], int64_t c) {
             c = clampc(c);
-            const auto r_v = make_rsrc(v + (tok0_of(c) * h_v + h) * (int64_t)D + cb * 16,
-                                       (rows_of(c) - 1) * row_v + 16 * ES);
-            const auto rs = sc_rsrc(c);
-#pragma unroll
-            for (int rt = 0; rt < RT; ++rt) {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)
-                    x.vv[rt][e] = buf_elem<TIn>(r_v, (int)((16 * rt + 4 * lg + e) * row_v) + lr * ES);
-                x.av[rt] = buf_floatx4(rs, (16 * rt + 4 * lg) * 4);
-                x.sv[rt] = buf_floatx4(rs, CP * 4 + (16 * rt + 4 * lg) * 4);
-            }
             const auto r_kt = make_rsrc(ws + L.kt + (size_t)((seq * nch + c) * h_qk + hq) * G::KT_BYTES,
                                         G::KT_BYTES);
 #pragma unroll
@@ -766,11 +776,8 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                 for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
                     for (int part = 0; part < NS; ++part)
-                        x.ktf[i][kt][part] =
+                        ktf[i][kt][part] =
                             buf_bf16x8(r_kt, (((hh * MTH + i) * KTC + kt) * NS + part) * 1024 + l * 16);
-            // A vector load (every lane the same word), not a scalar one: scalar loads share
-            // the LDS wait counter, and the wait before each barrier would stall on them.
-            x.gc = buf_elem<float>(rs, 3 * CP * 4);
         };
 
         // This wave's part of K M0 for the chunk whose K rows are given.
@@ -778,23 +785,14 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
         auto partial_km = [&](const Raw (*kr)[KTH]) {
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                floatx4 acc[2][NP];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int p = 0; p < NP; ++p) acc[j][p] = floatx4{0.f, 0.f, 0.f, 0.f};
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kk = 0; kk < KTH; ++kk) {
                     bf16x8 ka[NS];
                     to_pieces(kr[rt][kk], ka);
-                    mfma_split_acc<NS, 2>(ka, mf[kk], acc[kk & 1]);
+                    acc = mfma_split<NS, 2>(ka, mf[kk], acc);
                 }
-                floatx4 s = acc[0][0];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int p = (j == 0 ? 1 : 0); p < NP; ++p) s += acc[j][p];
-                pp[rt] = s;
+                pp[rt] = acc;
             }
         };
         auto publish = [&](int par) {
@@ -808,9 +806,19 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                 for (int p = 0; p < 2; ++p) s_mf[par][hh * KTH + kk][p][l] = mf[kk][p];
         };
 
-        // One chunk, between the barrier that publishes its inputs and the next one.
-        auto window = [&](const CS& x, int64_t c) {
+        // One chunk, between the barrier that publishes its inputs and the next one. Each
+        // operand set is reloaded for the next chunk right after its last use here (the
+        // scheduling barriers keep the loads behind those uses), so one set per operand
+        // suffices and every load has about a chunk to arrive.
+        CS x;
+        auto window = [&](int64_t c) {
             const int par = (int)(c & 1);
+            // T' first: nothing in this chunk computes it, so its LDS latency overlaps X.
+            bf16x8 tfr[SG::TLDS ? 2 * NTRI : 1];
+            if constexpr (SG::TLDS) {
+#pragma unroll
+                for (int pi = 0; pi < 2 * NTRI; ++pi) tfr[pi] = s_tf[par][pi][l];
+            }
             // X = V - diag(a) K M0, with K M0 the sum of both waves' parts (the same order of
             // addition in both waves, so both compute identical U)
             floatx4 xv[RT];
@@ -818,91 +826,69 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
             for (int rt = 0; rt < RT; ++rt) {
                 floatx4 z = pp[rt];
                 if constexpr (NCH > 1) z += s_xp[par][hh ^ 1][rt][l];
-#pragma unroll
-                for (int e = 0; e < 4; ++e) xv[rt][e] = raw_to_f32(x.vv[rt][e]) - x.av[rt][e] * z[e];
+                xv[rt] = vt4(par, rt) - sc4(par, 0, rt) * z;
             }
             bf16x8 xf[KTC][2];
             rows_to_frags<RT, KTC>(xv, xf);
+            const auto r_t = make_rsrc(ws + L.tt + vh_of(c) * G::TRI_BYTES, SG::TLDS ? 0 : G::TRI_BYTES);
             // U = T' X (lower triangular: row tile rt uses token k tiles 0 .. rt / 2)
             floatx4 u[RT];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
-                floatx4 acc[3];
-#pragma unroll
-                for (int p = 0; p < 3; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kt = 0; 2 * kt <= rt; ++kt) {
-                    const bf16x8 tf[2] = {s_tf[par][2 * (tri_off(rt) + kt)][l],
-                                          s_tf[par][2 * (tri_off(rt) + kt) + 1][l]};
-                    mfma_split_acc<2, 2>(tf, xf[kt], acc);
+                    const int pi = 2 * (tri_off(rt) + kt);
+                    bf16x8 tf[2];
+                    if constexpr (SG::TLDS) {
+                        tf[0] = tfr[pi];
+                        tf[1] = tfr[pi + 1];
+                    } else {
+                        tf[0] = buf_bf16x8(r_t, pi * 1024 + l * 16);
+                        tf[1] = buf_bf16x8(r_t, pi * 1024 + 1024 + l * 16);
+                    }
+                    acc = mfma_split<2, 2>(tf, xf[kt], acc);
                 }
-                u[rt] = acc[0] + acc[1] + acc[2];
+                u[rt] = acc;
             }
             if (hh == 0) {  // U for the output waves
-                bf16x8 uf[KTC][2];
-                rows_to_frags<RT, KTC>(u, uf);
 #pragma unroll
-                for (int kt = 0; kt < KTC; ++kt)
-#pragma unroll
-                    for (int p = 0; p < 2; ++p) s_uf[par][kt][p][l] = uf[kt][p];
+                for (int rt = 0; rt < RT; ++rt) s_uf[par][rt][l] = u[rt];
             }
             // W = diag(s) U;  M <- Gamma_C M + K^T W
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) u[rt] *= x.sv[rt];
+            for (int rt = 0; rt < RT; ++rt) u[rt] *= sc4(par, 1, rt);
             bf16x8 wf[KTC][2];
             rows_to_frags<RT, KTC>(u, wf);
+            const float gc = s_gc[par];
 #pragma unroll
             for (int i = 0; i < MTH; ++i) {
-                floatx4 acc[NP];
-                acc[0] = x.gc * macc[i];
+                floatx4 acc = gc * macc[i];
 #pragma unroll
-                for (int p = 1; p < NP; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kt = 0; kt < KTC; ++kt) mfma_split_acc<NS, 2>(x.ktf[i][kt], wf[kt], acc);
-                floatx4 s = acc[0];
-#pragma unroll
-                for (int p = 1; p < NP; ++p) s += acc[p];
-                macc[i] = s;
+                for (int kt = 0; kt < KTC; ++kt) acc = mfma_split<NS, 2>(x.ktf[i][kt], wf[kt], acc);
+                macc[i] = acc;
             }
+            __builtin_amdgcn_sched_barrier(0);
+            load_kt(x.ktf, c + 1);
             // The next chunk's partial K M0 (past the last chunk: computed on reloaded rows
             // and never read).
             split_state();
             partial_km(x.kr);
+            __builtin_amdgcn_sched_barrier(0);
+            load_k(x.kr, c + 2);
             publish(par ^ 1);
         };
 
         split_state();
-        {
-            Raw k0[RT][KTH];
-            load_k(k0, 0);
-            partial_km(k0);
-        }
+        load_k(x.kr, 0);
+        partial_km(x.kr);
         publish(0);
-        CS A;
-        load(A, 0);
-        if constexpr (SG::DB) {
-            CS B;
-            settle();
-            for (int64_t c = 0;;) {
-                load(B, c + 1);
-                __syncthreads();
-                window(A, c);
-                settle();
-                if (++c >= nch) break;
-                load(A, c + 1);
-                __syncthreads();
-                window(B, c);
-                settle();
-                if (++c >= nch) break;
-            }
-        } else {
+        load_kt(x.ktf, 0);
+        load_k(x.kr, 1);
 #pragma unroll 1
-            for (int64_t c = 0; c < nch; ++c) {
-                if (c > 0) load(A, c);
-                __syncthreads();
-                window(A, c);
-                settle();
-            }
+        for (int64_t c = 0; c < nch; ++c) {
+            __syncthreads();
+            window(c);
         }
         __syncthreads();  // matches the output waves' last window
 
@@ -921,21 +907,58 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
         // Row tiles ow, ow + NOW, ...; one chunk behind the chain waves. Window j finishes
         // the outputs of chunk j - 1 and starts Q M0 of chunk j.
         const int ow = w - NCH;
+        const bool stager = ow == NOW - 1;  // wave-uniform
         floatx4 qm[RTO];  // Q M0 of the chunk being finished
 
-        auto load_t = [&](bf16x8* tst, int64_t c) {
-            const auto r = make_rsrc(ws + L.tt + vh_of(clampc(c)) * G::TRI_BYTES, G::TRI_BYTES);
+        // What the chain waves read in chunk c: T' pieces (every output wave) and the V
+        // block, a, s and Gamma_C (the stager).
+        auto load_stage = [&](OS& x, int64_t c) {
+            c = clampc(c);
+            if constexpr (SG::TLDS) {
+                const auto r = make_rsrc(ws + L.tt + vh_of(c) * G::TRI_BYTES, G::TRI_BYTES);
 #pragma unroll
-            for (int m = 0; m < NTS; ++m) {
-                const int pi = ow + NOW * m;
-                tst[m] = buf_bf16x8(r, pi < 2 * NTRI ? pi * 1024 + l * 16 : (int)OOR);
+                for (int m = 0; m < NTS; ++m) {
+                    const int pi = ow + NOW * m;
+                    x.tst[m] = buf_bf16x8(r, pi < 2 * NTRI ? pi * 1024 + l * 16 : (int)OOR);
+                }
+            }
+            if (stager) {
+                const auto r_v = make_rsrc(v + (tok0_of(c) * h_v + h) * (int64_t)D + cb * 16,
+                                           (rows_of(c) - 1) * row_v + 16 * ES);
+                const auto rs = sc_rsrc(c);
+#pragma unroll
+                for (int tp = 0; tp < TPL; ++tp) {
+                    const int t = l + 64 * tp;
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf)
+                        x.vr[tp][hf] = buf_raw_frag<TIn>(
+                            r_v, (int)((uint32_t)(t * row_v) + (uint32_t)(8 * hf * ES) + pad_if(t < CP)));
+                    x.sa[tp] = buf_elem<float>(rs, (int)((uint32_t)(4 * t) + pad_if(t < CP)));
+                    x.ss[tp] = buf_elem<float>(rs, (int)((uint32_t)(4 * (CP + t)) + pad_if(t < CP)));
+                }
+                x.gc = buf_elem<float>(rs, 3 * CP * 4);
             }
         };
-        auto store_t = [&](const bf16x8* tst, int par) {
+        auto store_stage = [&](const OS& x, int par) {
+            if constexpr (SG::TLDS) {
 #pragma unroll
-            for (int m = 0; m < NTS; ++m) {
-                const int pi = ow + NOW * m;
-                if (pi < 2 * NTRI) s_tf[par][pi][l] = tst[m];
+                for (int m = 0; m < NTS; ++m) {
+                    const int pi = ow + NOW * m;
+                    if (pi < 2 * NTRI) s_tf[par][pi][l] = x.tst[m];
+                }
+            }
+            if (stager) {
+#pragma unroll
+                for (int tp = 0; tp < TPL; ++tp) {
+                    const int t = l + 64 * tp;  // < CPV; slots past CP hold zeros
+#pragma unroll
+                    for (int hf = 0; hf < 2; ++hf)
+#pragma unroll
+                        for (int e = 0; e < 8; ++e) s_vt[par][8 * hf + e][t] = elem_f32(x.vr[tp][hf], e);
+                    s_sc[par][0][t] = x.sa[tp];
+                    s_sc[par][1][t] = x.ss[tp];
+                }
+                s_gc[par] = x.gc;  // every lane writes the same value
             }
         };
         auto load = [&](OS& x, int64_t j) {
@@ -963,34 +986,31 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                     x.ov[i] = buf_floatx4(rs, rt < RT ? 2 * CP * 4 + (16 * rt + 4 * lg) * 4 : (int)OOR);
                 }
             }
-            load_t(x.tst, j + 1);
+            load_stage(x, j + 1);
         };
         // O = diag(o) Q M0 + Ptil U of chunk c, U from LDS.
         auto do_out = [&](const OS& x, int64_t c) {
             const int par = (int)(c & 1);
+            floatx4 urow[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) urow[rt] = s_uf[par][rt][l];
             bf16x8 ufr[KTC][2];
-#pragma unroll
-            for (int kt = 0; kt < KTC; ++kt)
-#pragma unroll
-                for (int p = 0; p < 2; ++p) ufr[kt][p] = s_uf[par][kt][p][l];
+            rows_to_frags<RT, KTC>(urow, ufr);
             const auto r_o = make_rsrc(out + (tok0_of(c) * h_v + h) * (int64_t)D + cb * 16,
                                        (rows_of(c) - 1) * row_o + 64);
 #pragma unroll
             for (int i = 0; i < RTO; ++i) {
                 const int rt = ow + NOW * i;
                 if (rt >= RT) continue;
-                floatx4 acc[3];
-                acc[0] = x.ov[i] * qm[i];
-                acc[1] = acc[2] = floatx4{0.f, 0.f, 0.f, 0.f};
+                floatx4 acc = x.ov[i] * qm[i];
 #pragma unroll
                 for (int kt = 0; kt < KTC; ++kt)
-                    if (2 * kt <= rt) mfma_split_acc<2, 2>(x.pf[i][kt], ufr[kt], acc);
-                const floatx4 o = acc[0] + acc[1] + acc[2];
+                    if (2 * kt <= rt) acc = mfma_split<2, 2>(x.pf[i][kt], ufr[kt], acc);
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     // Element to a scalar first: a bit cast of a vector-element expression
                     // picked element 0 for every e in this compiler.
-                    const float val = o[e];
+                    const float val = acc[e];
                     __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), r_o,
                                                           (int)((16 * rt + 4 * lg + e) * row_o) + lr * 4, 0, 0);
                 }
@@ -1007,36 +1027,27 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
 #pragma unroll
             for (int i = 0; i < RTO; ++i) {
                 if (ow + NOW * i >= RT) continue;
-                floatx4 acc[2][NP];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int p = 0; p < NP; ++p) acc[j][p] = floatx4{0.f, 0.f, 0.f, 0.f};
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kt = 0; kt < KTD; ++kt) {
                     bf16x8 qa[NS];
                     to_pieces(x.qr[i][kt], qa);
-                    mfma_split_acc<NS, 2>(qa, mfr[kt], acc[kt & 1]);
+                    acc = mfma_split<NS, 2>(qa, mfr[kt], acc);
                 }
-                floatx4 s = acc[0][0];
-#pragma unroll
-                for (int j = 0; j < 2; ++j)
-#pragma unroll
-                    for (int p = (j == 0 ? 1 : 0); p < NP; ++p) s += acc[j][p];
-                qm[i] = s;
+                qm[i] = acc;
             }
         };
         auto window = [&](const OS& x, int64_t j) {
-            store_t(x.tst, (int)((j + 1) & 1));  // T' of chunk j + 1
+            store_stage(x, (int)((j + 1) & 1));  // for the chain waves' chunk j + 1
             if (j >= 1) do_out(x, j - 1);
             if (j < nch) do_qm(x, j);
         };
 
         {
-            bf16x8 t0[NTS];
-            load_t(t0, 0);
+            OS s0;
+            load_stage(s0, 0);
             settle();
-            store_t(t0, 0);
+            store_stage(s0, 0);
         }
         OS A;
         load(A, 0);
