@@ -139,15 +139,14 @@ struct Geo {
     static constexpr int MTH = 2 * KTH;         // state tiles per chain wave
     static constexpr int NOW = 4 - NCH;         // output waves
     static constexpr int RTO = (RT + NOW - 1) / NOW;  // row tiles per output wave
-    static constexpr size_t KT_BYTES = (size_t)MTP * KTC * NS * 1024;  // per (chunk, QK head)
     static constexpr size_t TRI_BYTES = (size_t)NTRI * 2 * 1024;      // per (chunk, V head)
     static constexpr size_t SC_BYTES = (size_t)3 * CP * 4 + 16;       // per (chunk, V head)
 };
 
 // Workspace regions; every region starts 256-byte aligned.
 struct ChunkWs {
-    int64_t nch;                  // chunks per sequence
-    size_t kt, tt, pt, sc, total; // byte offsets: K^T, T', Ptil, scalars
+    int64_t nch;              // chunks per sequence
+    size_t tt, pt, sc, total; // byte offsets: T', Ptil, scalars
 };
 
 size_t align256(size_t x)
@@ -158,15 +157,16 @@ size_t align256(size_t x)
 ChunkWs chunk_ws(int64_t n, int64_t t, int32_t h_qk, int32_t h_v, int32_t d, int chunk,
                  bool f32in)
 {
-    const int dp = d < 32 ? 32 : d, cp = chunk < 32 ? 32 : chunk;
-    const size_t kt_bytes = (size_t)(dp / 16) * (cp / 32) * (f32in ? 2 : 1) * 1024;
+    (void)d;
+    (void)f32in;
+    const int cp = chunk < 32 ? 32 : chunk;
     const size_t tri_bytes = (size_t)tri_off(chunk / 16) * 2 * 1024;
     const size_t sc_bytes = (size_t)3 * cp * 4 + 16;
     ChunkWs w;
     w.nch = (t + chunk - 1) / chunk;
-    const size_t nq = (size_t)n * w.nch * h_qk, nv = (size_t)n * w.nch * h_v;
-    w.kt = 0;
-    w.tt = w.kt + align256(nq * kt_bytes);
+    (void)h_qk;
+    const size_t nv = (size_t)n * w.nch * h_v;
+    w.tt = 0;
     w.pt = w.tt + align256(nv * tri_bytes);
     w.sc = w.pt + align256(nv * tri_bytes);
     w.total = w.sc + align256(nv * sc_bytes);
@@ -314,8 +314,8 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 {
     constexpr bool F32IN = std::is_same<TIn, float>::value;
     using G = Geo<D, C, F32IN>;
-    constexpr int DP = G::DP, CP = G::CP, RT = G::RT, KTC = G::KTC, KTD = G::KTD;
-    constexpr int MTP = G::MTP, NS = G::NS, NTRI = G::NTRI;
+    constexpr int DP = G::DP, CP = G::CP, RT = G::RT, KTD = G::KTD;
+    constexpr int NS = G::NS, NTRI = G::NTRI;
     constexpr int NB = RT;        // 16x16 diagonal blocks of T
     constexpr int KS = DP + 8;    // LDS row stride of the K / Q pieces (bf16)
     constexpr int CS = CP + 4;    // LDS row stride of the CP x CP fp32 matrices
@@ -391,21 +391,6 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         }
     }
     __syncthreads();
-
-    // ---- phase 1: K^T tiles (A operand of the state update): tile (mt, kt, part) holds
-    //      K[token tok_of(kt, lg, j)][feature feat_of(mt, lr)] in lane l, slot j
-    {
-        char* kt_base = ws + L.kt + (size_t)((seq * nch + c) * h_qk + hq) * G::KT_BYTES;
-        constexpr int NTILE = MTP * KTC * NS;
-        for (int ti = w; ti < NTILE; ti += 4) {
-            const int part = ti % NS, kt = (ti / NS) % KTC, mt = ti / (NS * KTC);
-            const int f = feat_of(mt, lr);
-            bf16x8 val;
-#pragma unroll
-            for (int j = 0; j < 8; ++j) val[j] = s_kq(0, part, tok_of(kt, lg, j), f);
-            *reinterpret_cast<bf16x8*>(kt_base + (size_t)ti * 1024 + l * 16) = val;
-        }
-    }
 
     // ---- phase 2: Gram matrices K K^T and Q K^T (raw inputs), lower 16x16 tiles, kept in
     //      registers for every V head of this QK head
@@ -620,22 +605,37 @@ struct ScanGeo {
     static constexpr int CPV = G::CP < 64 ? 64 : G::CP;  // staged token slots
     static constexpr int TPL = CPV / 64;                  // staged tokens per lane
     static constexpr int VS = CPV + 4;                    // LDS row stride of the V block
-    // LDS besides the T' tiles; where the tiles do not fit next to it (d = 128 with
-    // C = 128) the chain waves read T' from the workspace instead.
+    // Each chain wave keeps the K rows of its feature half (as bf16 pieces) in LDS, where
+    // transposing reads turn them into the K^T operand of the state update.
+    static constexpr int KS = 32 * G::KTH + 8;            // LDS row stride of those rows
+    static constexpr size_t KB_BYTES = (size_t)G::NCH * G::NS * G::CP * KS * 2;
+    // LDS besides the T' tiles; where the tiles do not fit next to it (C = 128 with
+    // d >= 64) the chain waves read T' from the workspace instead.
     static constexpr size_t LDS_REST = (size_t)2 * G::NCH * G::RT * 1024 + (size_t)2 * G::KTD * 2048 +
                                        (size_t)2 * G::RT * 1024 + (size_t)2 * 16 * VS * 4 +
-                                       (size_t)2 * 2 * CPV * 4 + 16;
+                                       (size_t)2 * 2 * CPV * 4 + 16 + KB_BYTES;
     static constexpr bool TLDS = LDS_REST + (size_t)2 * 2 * G::NTRI * 1024 <= 160 * 1024;
     static constexpr int NTS = TLDS ? (2 * G::NTRI + G::NOW - 1) / G::NOW : 1;
 };
 
-// Operands a chain wave loads for chunk c: K^T tiles of chunk c and K rows of chunk c + 1.
+// Operands a chain wave loads for chunk c: the K rows of chunk c + 1.
 template <int D, int C, typename TIn>
 struct ChainSet {
     using G = Geo<D, C, std::is_same<TIn, float>::value>;
     typename RawFrag<TIn>::type kr[G::RT][G::KTH];  // K rows of chunk c + 1 (A fragments)
-    bf16x8 ktf[G::MTH][G::KTC][G::NS];                // K^T tiles of this wave's state rows
 };
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group, output
+// lane j receives in slot p element (j mod 4) of the 8 bytes addressed by lane
+// 4 p + j / 4 of the group (established with an in-bounds probe of the instruction).
+__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p)
+{
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf16;
+    const v4bf16 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) v4bf16*)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
 
 // Operands an output wave loads for window j (finishing chunk j - 1, starting chunk j),
 // and what it stages for the chain waves' chunk j + 1.
@@ -688,6 +688,7 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     __shared__ __align__(16) bf16x8 s_mf[2][KTD][2][64];
     __shared__ __align__(16) floatx4 s_uf[2][RT][64];
     __shared__ __align__(16) bf16x8 s_tf[SG::TLDS ? 2 : 1][SG::TLDS ? 2 * NTRI : 1][64];
+    __shared__ __align__(16) __bf16 s_kb[NCH][NS][CP][SG::KS];  // each chain wave's K rows
     __shared__ __align__(16) float s_vt[2][16][SG::VS];
     __shared__ __align__(16) float s_sc[2][2][CPV];
     __shared__ float s_gc[2];
@@ -766,18 +767,35 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
 #pragma unroll
                 for (int kk = 0; kk < KTH; ++kk) kr[rt][kk] = buf_raw_frag<TIn>(r, qk_off(rt, hh * KTH + kk));
         };
-        auto load_kt = [&](bf16x8 (*ktf)[KTC][NS], int64_t c) {
-            c = clampc(c);
-            const auto r_kt = make_rsrc(ws + L.kt + (size_t)((seq * nch + c) * h_qk + hq) * G::KT_BYTES,
-                                        G::KT_BYTES);
+        // This wave's K rows into its LDS buffer (row-major, features of its half; rows past
+        // the chunk stay zero). Only this wave reads them back, after its own writes.
+        auto store_k = [&](const Raw (*kr)[KTH]) {
 #pragma unroll
-            for (int i = 0; i < MTH; ++i)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                for (int kt = 0; kt < KTC; ++kt)
+                for (int kk = 0; kk < KTH; ++kk) {
+                    bf16x8 piece[NS];
+                    to_pieces(kr[rt][kk], piece);
 #pragma unroll
                     for (int part = 0; part < NS; ++part)
-                        ktf[i][kt][part] =
-                            buf_bf16x8(r_kt, (((hh * MTH + i) * KTC + kt) * NS + part) * 1024 + l * 16);
+                        *reinterpret_cast<bf16x8*>(&s_kb[hh][part][16 * rt + lr][32 * kk + 8 * lg]) = piece[part];
+                }
+        };
+        if constexpr (16 * RT < CP) {  // C = 16: token rows 16..31 of the padded k tile
+            for (int i = l; i < NS * (CP - 16 * RT) * SG::KS; i += 64) {
+                const int part = i / ((CP - 16 * RT) * SG::KS), rem = i % ((CP - 16 * RT) * SG::KS);
+                s_kb[hh][part][16 * RT + rem / SG::KS][rem % SG::KS] = (__bf16)0.f;
+            }
+        }
+        // K^T A fragment of this wave's state tile i, token k tile kt: two transposing reads,
+        // for token slots 0..3 and 4..7 (lane lr of group lg addresses token row
+        // 32 kt + 16 h + 4 lg + lr / 4 and the four features feat_of(mt, 4 (lr % 4) + 0..3)).
+        auto kt_frag = [&](int i, int kt, int part) {
+            const int col = 32 * (i >> 1) + 8 * (lr & 3) + 4 * (i & 1);
+            const int row = 32 * kt + 4 * lg + (lr >> 2);
+            const bf16x4 a = lds_read_tr16(&s_kb[hh][part][row][col]);
+            const bf16x4 b = lds_read_tr16(&s_kb[hh][part][row + 16][col]);
+            return bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
         };
 
         // This wave's part of K M0 for the chunk whose K rows are given.
@@ -806,10 +824,10 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                 for (int p = 0; p < 2; ++p) s_mf[par][hh * KTH + kk][p][l] = mf[kk][p];
         };
 
-        // One chunk, between the barrier that publishes its inputs and the next one. Each
-        // operand set is reloaded for the next chunk right after its last use here (the
-        // scheduling barriers keep the loads behind those uses), so one set per operand
-        // suffices and every load has about a chunk to arrive.
+        // One chunk, between the barrier that publishes its inputs and the next one. The K
+        // rows are reloaded for the next chunk right after their last use here (the
+        // scheduling barrier keeps the loads behind that use), so one register set
+        // suffices and the loads have about a chunk to arrive.
         CS x;
         auto window = [&](int64_t c) {
             const int par = (int)(c & 1);
@@ -865,15 +883,19 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
             for (int i = 0; i < MTH; ++i) {
                 floatx4 acc = gc * macc[i];
 #pragma unroll
-                for (int kt = 0; kt < KTC; ++kt) acc = mfma_split<NS, 2>(x.ktf[i][kt], wf[kt], acc);
+                for (int kt = 0; kt < KTC; ++kt) {
+                    bf16x8 ktp[NS];
+#pragma unroll
+                    for (int part = 0; part < NS; ++part) ktp[part] = kt_frag(i, kt, part);
+                    acc = mfma_split<NS, 2>(ktp, wf[kt], acc);
+                }
                 macc[i] = acc;
             }
-            __builtin_amdgcn_sched_barrier(0);
-            load_kt(x.ktf, c + 1);
             // The next chunk's partial K M0 (past the last chunk: computed on reloaded rows
-            // and never read).
+            // and never read); its K rows replace this chunk's in LDS.
             split_state();
             partial_km(x.kr);
+            store_k(x.kr);
             __builtin_amdgcn_sched_barrier(0);
             load_k(x.kr, c + 2);
             publish(par ^ 1);
@@ -882,8 +904,8 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
         split_state();
         load_k(x.kr, 0);
         partial_km(x.kr);
+        store_k(x.kr);
         publish(0);
-        load_kt(x.ktf, 0);
         load_k(x.kr, 1);
 #pragma unroll 1
         for (int64_t c = 0; c < nch; ++c) {
