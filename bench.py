@@ -11,7 +11,9 @@ One step is the whole hot path once:
 `value` is prefill tokens per second for the 30 layers (4096 / prefill seconds per step);
 `decode_us_per_token` is the decode part. Inputs are resident in HBM before timing starts.
 
-The JSON line also carries
+The JSON line also carries decode_cold_us_per_token (the decode step with its states out of
+the MALL) and hbm_copy_GBps (what a 1 GiB device copy reaches; the achievable HBM rate next to
+the 8 TB/s peak), both measured after the timed region, and
   roofline:     the prefill call (its two kernels) against HBM: algorithmic bytes per call
                 (q, k, v, g, beta read once, out and state_out written once) divided by the
                 mean call duration from HIP events around every timed call, on the stream
@@ -85,6 +87,39 @@ def measured_traffic():
     if fields.get("source_sha256") != sha or "bytes_per_call" not in fields:
         return None
     return int(fields["bytes_per_call"])
+
+
+def reference_rates(gdn, dec, dec_out, dev):
+    """Outside the timed region: the decode step with its state out of the 256 MB MALL
+    (six independent 30-layer state stacks used in turn, 360 MiB), and the HBM rate a plain
+    1 GiB device copy reaches (read + write bytes per second), the achievable counterpart
+    of the 8 TB/s peak."""
+    import torch
+    stacks = [torch.zeros(LAYERS, H_V, D, D, device=dev) for _ in range(6)]
+    calls = [gdn.bind_decode_step(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], st,
+                                  dec_out, st) for st in stacks]
+    for c in calls:
+        c()
+    torch.cuda.synchronize()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(31)]
+    for i in range(30):
+        evs[i].record()
+        calls[i % 6]()
+    evs[30].record()
+    torch.cuda.synchronize()
+    cold_us = evs[0].elapsed_time(evs[30]) / 30 * 1e3
+    del stacks, calls
+    a = torch.empty(1 << 28, device=dev)
+    b = torch.empty_like(a)
+    b.copy_(a)
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(5):
+        b.copy_(a)
+    e.record()
+    torch.cuda.synchronize()
+    copy_gbs = 2 * a.numel() * 4 * 5 / (s.elapsed_time(e) * 1e-3) / 1e9
+    return {"decode_cold_us": cold_us, "copy_GBps": copy_gbs}
 
 
 def cpu_baseline():
@@ -187,6 +222,7 @@ def main():
     achieved = prefill_bytes() / mean_call_s / 1e9
 
     traffic = measured_traffic()
+    extra = reference_rates(gdn, dec, dec_out, dev)
 
     res = {
         "metric": METRIC,
@@ -209,6 +245,9 @@ def main():
         "decode_us_per_token": sum(decode_ms) / len(decode_ms) * 1e3,
         "decode_GBps": decode_bytes() / (sum(decode_ms) / len(decode_ms) / 1e3) / 1e9,
         "prefill_us_per_layer": mean_call_s * 1e6,
+        "decode_cold_us_per_token": extra["decode_cold_us"],
+        "decode_cold_GBps": decode_bytes() / (extra["decode_cold_us"] * 1e-6) / 1e9,
+        "hbm_copy_GBps": extra["copy_GBps"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gdn_prefill_chunked call (chunk_prep_kernel + chunk_scan_kernel)",
