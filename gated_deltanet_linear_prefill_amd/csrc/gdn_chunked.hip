@@ -306,6 +306,14 @@ __device__ __forceinline__ void tri_tile(int t, int& rt, int& ct)
 }
 
 // =============================================================================== prep
+// Fragment index fi of a compact lower-triangular operand -> (row tile rt, k tile kt).
+__device__ __forceinline__ void tri_frag(int fi, int& rt, int& kt)
+{
+    rt = 0;
+    while (tri_off(rt + 1) <= fi) ++rt;
+    kt = fi - tri_off(rt);
+}
+
 template <int D, int C, typename TIn>
 __global__ void __launch_bounds__(256)
 chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ g,
@@ -322,6 +330,12 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     constexpr size_t KQ_LDS = (size_t)2 * NS * CP * KS * 2;
     constexpr size_t AT_LDS = (size_t)2 * CP * CS * 4;
     constexpr size_t U_LDS = KQ_LDS > AT_LDS ? KQ_LDS : AT_LDS;
+    // Waves that solve the diagonal blocks (one lane per column); the others write Ptil
+    // meanwhile (all waves when the diagonal blocks take all four).
+    constexpr int NBW = (NB * 16 + 63) / 64;
+    constexpr int PW0 = NBW < 4 ? NBW : 0;        // first Ptil wave
+    constexpr int NPW = 4 - PW0;                  // Ptil waves
+    constexpr int NFW = (NTRI + NPW - 1) / NPW;   // Ptil fragments per Ptil wave
 
     // The K and Q chunks (first phases) and the A / T matrices (later phases) share one
     // buffer; the Gram matrices live in registers in between.
@@ -345,87 +359,133 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     const int grp = h_v / h_qk;
     const int64_t tok0 = seq * T + c0;  // flattened token index of the chunk's first token
 
+    // Gate and write strength of one V head for this chunk (wave 0; E tokens per lane),
+    // loaded one V head ahead of their use.
+    constexpr int E = (CP + 63) / 64;
+    float gv[E], bv[E];
+    auto load_gb = [&](int hv) {
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = l * E + e;
+            const bool ok = i < Cr;
+            const int64_t off = (tok0 + (ok ? i : 0)) * h_v + hv;
+            const float g_in = g[off], b_in = beta[off];
+            gv[e] = ok ? g_in : 0.f;
+            bv[e] = ok ? b_in : 0.f;
+        }
+    };
+    if (w == 0) load_gb(hq * grp);
+
     // ---- phase 0: inverse norms of the q and k rows; both chunks into LDS as bf16 pieces
-    //      (rows past the chunk and padded features are zero)
+    //      (rows past the chunk and padded features are zero). The loads of a batch of
+    //      rows are all issued before any of them is used.
     {
         constexpr int EPL = D / 16;  // elements per lane, 16 lanes per row
+        constexpr int NPASS = CP / 16;
+        constexpr int BATCH = NPASS < 4 ? NPASS : 4;
         const int sub = tid & 15;
-        for (int r0 = 0; r0 < CP; r0 += 16) {
-            const int r = r0 + (tid >> 4);
-            const bool ok = r < Cr;
-            const int64_t off = ((tok0 + (ok ? r : 0)) * h_qk + hq) * (int64_t)D + sub * EPL;
-            float qv[EPL], kv[EPL];
-            load_n<EPL>(q + off, qv);
-            load_n<EPL>(k + off, kv);
-            float qq = 0.f, kk = 0.f;
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                qq += qv[e] * qv[e];
-                kk += kv[e] * kv[e];
-            }
-            qq = row16_sum(qq);
-            kk = row16_sum(kk);
-            if (sub == 0) {
-                s_rq[r] = ok ? 1.0f / sqrtf(qq + eps) : 0.f;
-                s_rk[r] = ok ? 1.0f / sqrtf(kk + eps) : 0.f;
+        for (int p0 = 0; p0 < NPASS; p0 += BATCH) {
+            float qv[BATCH][EPL], kv[BATCH][EPL];
+#pragma unroll
+            for (int b = 0; b < BATCH; ++b) {
+                const int r = 16 * (p0 + b) + (tid >> 4);
+                const bool ok = r < Cr;
+                const int64_t off = ((tok0 + (ok ? r : 0)) * h_qk + hq) * (int64_t)D + sub * EPL;
+                load_n<EPL>(q + off, qv[b]);
+                load_n<EPL>(k + off, kv[b]);
             }
 #pragma unroll
-            for (int e = 0; e < EPL; ++e) {
-                __bf16 hi, lo;
-                split_bf16(ok ? kv[e] : 0.f, hi, lo);
-                s_kq(0, 0, r, sub * EPL + e) = hi;
-                if constexpr (NS > 1) s_kq(0, 1, r, sub * EPL + e) = lo;
-                split_bf16(ok ? qv[e] : 0.f, hi, lo);
-                s_kq(1, 0, r, sub * EPL + e) = hi;
-                if constexpr (NS > 1) s_kq(1, 1, r, sub * EPL + e) = lo;
-            }
-            if constexpr (D < DP) {  // zero the padded features
+            for (int b = 0; b < BATCH; ++b) {
+                const int r = 16 * (p0 + b) + (tid >> 4);
+                const bool ok = r < Cr;
+                float qq = 0.f, kk = 0.f;
 #pragma unroll
-                for (int e = 0; e < (DP - D) / 16; ++e)
+                for (int e = 0; e < EPL; ++e) {
+                    qq += qv[b][e] * qv[b][e];
+                    kk += kv[b][e] * kv[b][e];
+                }
+                qq = row16_sum(qq);
+                kk = row16_sum(kk);
+                if (sub == 0) {
+                    s_rq[r] = ok ? 1.0f / sqrtf(qq + eps) : 0.f;
+                    s_rk[r] = ok ? 1.0f / sqrtf(kk + eps) : 0.f;
+                }
 #pragma unroll
-                    for (int which = 0; which < 2; ++which)
+                for (int e = 0; e < EPL; ++e) {
+                    __bf16 hi, lo;
+                    split_bf16(ok ? kv[b][e] : 0.f, hi, lo);
+                    s_kq(0, 0, r, sub * EPL + e) = hi;
+                    if constexpr (NS > 1) s_kq(0, 1, r, sub * EPL + e) = lo;
+                    split_bf16(ok ? qv[b][e] : 0.f, hi, lo);
+                    s_kq(1, 0, r, sub * EPL + e) = hi;
+                    if constexpr (NS > 1) s_kq(1, 1, r, sub * EPL + e) = lo;
+                }
+                if constexpr (D < DP) {  // zero the padded features
 #pragma unroll
-                        for (int part = 0; part < NS; ++part)
-                            s_kq(which, part, r, D + sub * ((DP - D) / 16) + e) = (__bf16)0.f;
+                    for (int e = 0; e < (DP - D) / 16; ++e)
+#pragma unroll
+                        for (int which = 0; which < 2; ++which)
+#pragma unroll
+                            for (int part = 0; part < NS; ++part)
+                                s_kq(which, part, r, D + sub * ((DP - D) / 16) + e) = (__bf16)0.f;
+                }
             }
         }
     }
     __syncthreads();
 
-    // ---- phase 2: Gram matrices K K^T and Q K^T (raw inputs), lower 16x16 tiles, kept in
-    //      registers for every V head of this QK head
+    // ---- phase 2: Gram matrices from the raw inputs, kept in registers for every V head
+    //      of this QK head.
+    //  * K K^T, lower 16x16 tiles (rt >= ct), accumulator rows r, columns s: for A.
+    //  * K Q^T, the tile pairs (2 kt, rt), (2 kt + 1, rt) behind Ptil^T fragment (rt, kt):
+    //    accumulator rows are tokens s of K, columns tokens r of Q, so the four values a
+    //    lane holds in the two tiles are the eight k slots (permuted token order) of the
+    //    B fragment of Ptil^T the scan kernel multiplies U^T with.
     constexpr int NTL = RT * (RT + 1) / 2;
-    constexpr int NTW = (NTL + 3) / 4;   // tiles per wave
+    constexpr int NTW = (NTL + 3) / 4;   // K K^T tiles per wave
     constexpr int NPG = NS == 1 ? 1 : 3; // split passes of a Gram product
-    floatx4 gk[NTW], gq[NTW];
+    // Gram tile: rows of chunk `wa` (0 = K, 1 = Q) tile ta against rows of chunk `wb` tile tb.
+    auto gram = [&](int wa, int ta, int wb, int tb) {
+        floatx4 acc[NPG];
+#pragma unroll
+        for (int p = 0; p < NPG; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int kt = 0; kt < KTD; ++kt) {
+            bf16x8 a[NS], b[NS];
+#pragma unroll
+            for (int part = 0; part < NS; ++part) {
+                a[part] = *reinterpret_cast<const bf16x8*>(&s_kq(wa, part, 16 * ta + lr, 32 * kt + 8 * lg));
+                b[part] = *reinterpret_cast<const bf16x8*>(&s_kq(wb, part, 16 * tb + lr, 32 * kt + 8 * lg));
+            }
+            mfma_split_acc<NS, NS>(a, b, acc);
+        }
+        floatx4 s = acc[0];
+#pragma unroll
+        for (int p = 1; p < NPG; ++p) s += acc[p];
+        return s;
+    };
+    floatx4 gk[NTW];
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
         gk[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-        gq[i] = gk[i];
         const int ti = w + 4 * i;
         if (ti < NTL) {
             int rt, ct;
             tri_tile(ti, rt, ct);
-            floatx4 ak[NPG], aq[NPG];
+            gk[i] = gram(0, rt, 0, ct);
+        }
+    }
+    floatx4 gp[NFW][2];  // K Q^T tile pairs of this wave's Ptil fragments
 #pragma unroll
-            for (int p = 0; p < NPG; ++p) ak[p] = aq[p] = floatx4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-            for (int kt = 0; kt < KTD; ++kt) {
-                bf16x8 a_k[NS], a_q[NS], b[NS];
-#pragma unroll
-                for (int part = 0; part < NS; ++part) {
-                    a_k[part] = *reinterpret_cast<const bf16x8*>(&s_kq(0, part, 16 * rt + lr, 32 * kt + 8 * lg));
-                    a_q[part] = *reinterpret_cast<const bf16x8*>(&s_kq(1, part, 16 * rt + lr, 32 * kt + 8 * lg));
-                    b[part] = *reinterpret_cast<const bf16x8*>(&s_kq(0, part, 16 * ct + lr, 32 * kt + 8 * lg));
-                }
-                mfma_split_acc<NS, NS>(a_k, b, ak);
-                mfma_split_acc<NS, NS>(a_q, b, aq);
-            }
-#pragma unroll
-            for (int p = 0; p < NPG; ++p) {
-                gk[i] += ak[p];
-                gq[i] += aq[p];
-            }
+    for (int i = 0; i < NFW; ++i) {
+        gp[i][0] = gp[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
+        const int fi = w - PW0 + NPW * i;
+        if (w >= PW0 && fi < NTRI) {
+            int rt, kt;
+            tri_frag(fi, rt, kt);
+            gp[i][0] = gram(0, 2 * kt, 1, rt);
+            if (2 * kt + 1 <= rt) gp[i][1] = gram(0, 2 * kt + 1, 1, rt);
         }
     }
     __syncthreads();  // the K / Q buffer becomes A / T below
@@ -434,21 +494,14 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         const int hv = hq * grp + gi;
         const int64_t vh = (seq * nch + c) * h_v + hv;
 
-        // ---- phase 3: gate prefix sums gamma (wave 0), write strengths
+        // ---- phase 3: gate prefix sums gamma (wave 0), write strengths; the next V head's
+        //      gate and write strength are loaded meanwhile
         if (w == 0) {
-            constexpr int E = (CP + 63) / 64;
-            float gv[E], bv[E];
-            float run = 0.f;
+            float run = 0.f, gs[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) {
-                const int i = l * E + e;
-                const bool ok = i < Cr;
-                const int64_t gi_off = (tok0 + (ok ? i : 0)) * h_v + hv;
-                const float g_in = g[gi_off], b_in = beta[gi_off];
-                gv[e] = ok ? g_in : 0.f;
-                bv[e] = ok ? b_in : 0.f;
                 run += gv[e];
-                gv[e] = run;
+                gs[e] = run;
             }
             float x = run;
 #pragma unroll
@@ -461,10 +514,11 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             for (int e = 0; e < E; ++e) {
                 const int i = l * E + e;
                 if (i < CP) {
-                    s_gam[i] = gv[e] + excl;
+                    s_gam[i] = gs[e] + excl;
                     s_beta[i] = bv[e];
                 }
             }
+            if (gi + 1 < grp) load_gb(hv + 1);
         }
         __syncthreads();
 
@@ -502,7 +556,8 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         __syncthreads();
 
         // ---- phase 5: diagonal 16x16 blocks of T by forward substitution, one lane per
-        //      column: T[r][s] = delta_rs - sum_{m<r} A[r][m] T[m][s]
+        //      column: T[r][s] = delta_rs - sum_{m<r} A[r][m] T[m][s]. The other waves
+        //      write Ptil^T meanwhile.
         if (tid < NB * 16) {
             const int b = tid >> 4, s = tid & 15;
             float t[16];
@@ -515,6 +570,34 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             }
 #pragma unroll
             for (int r = 0; r < 16; ++r) s_t[16 * b + r][16 * b + s] = t[r];
+        }
+        // Ptil^T B fragment (rt, kt), hi and lo: slot 4 h + e holds
+        // Ptil[16 rt + lr][16 (2 kt + h) + 4 lg + e], which is zero above the diagonal.
+        if (w >= PW0) {
+            char* pt_base = ws + L.pt + (size_t)vh * G::TRI_BYTES;
+#pragma unroll
+            for (int i = 0; i < NFW; ++i) {
+                const int fi = w - PW0 + NPW * i;
+                if (fi >= NTRI) continue;
+                int rt, kt;
+                tri_frag(fi, rt, kt);
+                const int r = 16 * rt + lr;
+                float val[8];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int s = 32 * kt + 16 * h + 4 * lg + e;
+                        float p = 0.f;
+                        if (s <= r) p = __expf(s_gam[r] - s_gam[s]) * s_rq[r] * s_rk[s] * gp[i][h][e];
+                        val[4 * h + e] = p;
+                    }
+                uint32_t hi[4], lo[4];
+#pragma unroll
+                for (int p = 0; p < 4; ++p) split2(val[2 * p], val[2 * p + 1], &hi[p], &lo[p]);
+                *reinterpret_cast<u32x4*>(pt_base + (size_t)(2 * fi) * 1024 + l * 16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+                *reinterpret_cast<u32x4*>(pt_base + (size_t)(2 * fi + 1) * 1024 + l * 16) = u32x4{lo[0], lo[1], lo[2], lo[3]};
+            }
         }
         __syncthreads();
 
@@ -543,52 +626,28 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             __syncthreads();
         }
 
-        // ---- a lower-triangular CP x CP matrix (times a column scaling) as compact hi/lo
-        //      A-operand tiles with the permuted token order in k
-        auto write_tiles = [&](float(*src)[CS], bool col_beta, char* base) {
-            for (int ti = w; ti < NTRI; ti += 4) {
-                int rt = 0;
-                while (tri_off(rt + 1) <= ti) ++rt;
-                const int kt = ti - tri_off(rt);
+        // ---- T' = T diag(beta) as compact hi/lo A-operand tiles with the permuted token
+        //      order in k
+        {
+            char* tt_base = ws + L.tt + (size_t)vh * G::TRI_BYTES;
+            for (int fi = w; fi < NTRI; fi += 4) {
+                int rt, kt;
+                tri_frag(fi, rt, kt);
                 const int r = 16 * rt + lr;
-                bf16x8 hi, lo;
+                float val[8];
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int s = tok_of(kt, lg, j);
-                    float x = s <= r ? src[r][s] : 0.f;
-                    if (col_beta) x *= s_beta[s];
-                    __bf16 h, lw;
-                    split_bf16(x, h, lw);
-                    hi[j] = h;
-                    lo[j] = lw;
+                    val[j] = s <= r ? s_t[r][s] * s_beta[s] : 0.f;
                 }
-                *reinterpret_cast<bf16x8*>(base + (size_t)(2 * ti) * 1024 + l * 16) = hi;
-                *reinterpret_cast<bf16x8*>(base + (size_t)(2 * ti + 1) * 1024 + l * 16) = lo;
-            }
-        };
-        // T' = T diag(beta)
-        write_tiles(s_t, true, ws + L.tt + (size_t)vh * G::TRI_BYTES);
-
-        // ---- phase 7: Ptil = lower (exp(gamma_r - gamma_s) r_q,r r_k,s q_r . k_s), into A's
-        //      space (A is no longer read)
+                uint32_t hi[4], lo[4];
 #pragma unroll
-        for (int i = 0; i < NTW; ++i) {
-            const int ti = w + 4 * i;
-            if (ti < NTL) {
-                int rt, ct;
-                tri_tile(ti, rt, ct);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * rt + 4 * lg + e, s = 16 * ct + lr;
-                    float p = 0.f;
-                    if (s <= r) p = __expf(s_gam[r] - s_gam[s]) * s_rq[r] * s_rk[s] * gq[i][e];
-                    s_a[r][s] = p;
-                }
+                for (int p = 0; p < 4; ++p) split2(val[2 * p], val[2 * p + 1], &hi[p], &lo[p]);
+                *reinterpret_cast<u32x4*>(tt_base + (size_t)(2 * fi) * 1024 + l * 16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
+                *reinterpret_cast<u32x4*>(tt_base + (size_t)(2 * fi + 1) * 1024 + l * 16) = u32x4{lo[0], lo[1], lo[2], lo[3]};
             }
         }
-        __syncthreads();
-        write_tiles(s_a, false, ws + L.pt + (size_t)vh * G::TRI_BYTES);
-        __syncthreads();
+        __syncthreads();  // s_a, s_t and the gate prefix sums are rewritten for the next V head
     }
 }
 
@@ -644,8 +703,8 @@ struct OutSet {
     using G = Geo<D, C, std::is_same<TIn, float>::value>;
     using SG = ScanGeo<D, C, TIn>;
     typename RawFrag<TIn>::type qr[G::RTO][G::KTD];  // Q rows of chunk j (A fragments)
-    bf16x8 pf[G::RTO][G::KTC][2];                     // Ptil of chunk j - 1, zero past the diagonal
-    floatx4 ov[G::RTO];                               // scalars o of chunk j - 1
+    bf16x8 pf[G::RTO][G::KTC][2];                     // Ptil^T of chunk j - 1 (B fragments)
+    float ov[G::RTO];                                 // scalar o of token lr of each row tile
     bf16x8 tst[SG::NTS];                              // T' pieces of chunk j + 1
     typename RawFrag<TIn>::type vr[SG::TPL][2];      // V rows of chunk j + 1 (16 channels)
     float sa[SG::TPL], ss[SG::TPL], gc;               // a, s of those tokens; Gamma_C
@@ -927,10 +986,10 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     } else {
         // ======================================================= output wave ow
         // Row tiles ow, ow + NOW, ...; one chunk behind the chain waves. Window j finishes
-        // the outputs of chunk j - 1 and starts Q M0 of chunk j.
+        // the outputs of chunk j - 1 and starts (Q M0)^T of chunk j.
         const int ow = w - NCH;
         const bool stager = ow == NOW - 1;  // wave-uniform
-        floatx4 qm[RTO];  // Q M0 of the chunk being finished
+        floatx4 qm[RTO];  // (Q M0)^T of the chunk being finished
 
         // What the chain waves read in chunk c: T' pieces (every output wave) and the V
         // block, a, s and Gamma_C (the stager).
@@ -1005,12 +1064,15 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                         x.pf[i][kt][0] = buf_bf16x8(r, ok ? o : (int)OOR);
                         x.pf[i][kt][1] = buf_bf16x8(r, ok ? o + 1024 : (int)OOR);
                     }
-                    x.ov[i] = buf_floatx4(rs, rt < RT ? 2 * CP * 4 + (16 * rt + 4 * lg) * 4 : (int)OOR);
+                    x.ov[i] = buf_elem<float>(rs, rt < RT ? 2 * CP * 4 + (16 * rt + lr) * 4 : (int)OOR);
                 }
             }
             load_stage(x, j + 1);
         };
-        // O = diag(o) Q M0 + Ptil U of chunk c, U from LDS.
+        // Outputs are formed transposed, O^T = (Q M0)^T diag(o) + U^T Ptil^T, as 16 value
+        // channels x 16 tokens tiles: the state and U fragments serve unchanged as A
+        // operands and the Q row fragments as B operands, Ptil^T arrives as B fragments, and
+        // each lane ends up with four consecutive channels of one token (one 16-byte store).
         auto do_out = [&](const OS& x, int64_t c) {
             const int par = (int)(c & 1);
             floatx4 urow[RT];
@@ -1027,18 +1089,12 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                 floatx4 acc = x.ov[i] * qm[i];
 #pragma unroll
                 for (int kt = 0; kt < KTC; ++kt)
-                    if (2 * kt <= rt) acc = mfma_split<2, 2>(x.pf[i][kt], ufr[kt], acc);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    // Element to a scalar first: a bit cast of a vector-element expression
-                    // picked element 0 for every e in this compiler.
-                    const float val = acc[e];
-                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), r_o,
-                                                          (int)((16 * rt + 4 * lg + e) * row_o) + lr * 4, 0, 0);
-                }
+                    if (2 * kt <= rt) acc = mfma_split<2, 2>(ufr[kt], x.pf[i][kt], acc);
+                __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), r_o,
+                                                       (int)((16 * rt + lr) * row_o) + lg * 16, 0, 0);
             }
         };
-        // Q M0 of chunk c, the state from LDS.
+        // (Q M0)^T of chunk c, the state from LDS.
         auto do_qm = [&](const OS& x, int64_t c) {
             const int par = (int)(c & 1);
             bf16x8 mfr[KTD][2];
@@ -1054,7 +1110,7 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                 for (int kt = 0; kt < KTD; ++kt) {
                     bf16x8 qa[NS];
                     to_pieces(x.qr[i][kt], qa);
-                    acc = mfma_split<NS, 2>(qa, mfr[kt], acc);
+                    acc = mfma_split<2, NS>(mfr[kt], qa, acc);
                 }
                 qm[i] = acc;
             }
