@@ -139,14 +139,17 @@ struct Geo {
     static constexpr int MTH = 2 * KTH;         // state tiles per chain wave
     static constexpr int NOW = 4 - NCH;         // output waves
     static constexpr int RTO = (RT + NOW - 1) / NOW;  // row tiles per output wave
+    static constexpr int NHF = RT * KTC;        // A fragments of the full C x C matrix H
+    static constexpr bool WITH_H = C <= 64;     // H is prepared for the scan kernel that uses it
     static constexpr size_t TRI_BYTES = (size_t)NTRI * 2 * 1024;      // per (chunk, V head)
+    static constexpr size_t H_BYTES = WITH_H ? (size_t)NHF * 2 * 1024 : 0;  // per (chunk, V head)
     static constexpr size_t SC_BYTES = (size_t)3 * CP * 4 + 16;       // per (chunk, V head)
 };
 
 // Workspace regions; every region starts 256-byte aligned.
 struct ChunkWs {
-    int64_t nch;              // chunks per sequence
-    size_t tt, pt, sc, total; // byte offsets: T', Ptil, scalars
+    int64_t nch;                  // chunks per sequence
+    size_t tt, pt, hh, sc, total; // byte offsets: T', Ptil, H, scalars
 };
 
 size_t align256(size_t x)
@@ -161,6 +164,7 @@ ChunkWs chunk_ws(int64_t n, int64_t t, int32_t h_qk, int32_t h_v, int32_t d, int
     (void)f32in;
     const int cp = chunk < 32 ? 32 : chunk;
     const size_t tri_bytes = (size_t)tri_off(chunk / 16) * 2 * 1024;
+    const size_t h_bytes = chunk <= 64 ? (size_t)(chunk / 16) * (cp / 32) * 2 * 1024 : 0;
     const size_t sc_bytes = (size_t)3 * cp * 4 + 16;
     ChunkWs w;
     w.nch = (t + chunk - 1) / chunk;
@@ -168,7 +172,8 @@ ChunkWs chunk_ws(int64_t n, int64_t t, int32_t h_qk, int32_t h_v, int32_t d, int
     const size_t nv = (size_t)n * w.nch * h_v;
     w.tt = 0;
     w.pt = w.tt + align256(nv * tri_bytes);
-    w.sc = w.pt + align256(nv * tri_bytes);
+    w.hh = w.pt + align256(nv * tri_bytes);
+    w.sc = w.hh + align256(nv * h_bytes);
     w.total = w.sc + align256(nv * sc_bytes);
     return w;
 }
@@ -322,7 +327,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 {
     constexpr bool F32IN = std::is_same<TIn, float>::value;
     using G = Geo<D, C, F32IN>;
-    constexpr int DP = G::DP, CP = G::CP, RT = G::RT, KTD = G::KTD;
+    constexpr int DP = G::DP, CP = G::CP, RT = G::RT, KTD = G::KTD, KTC = G::KTC;
     constexpr int NS = G::NS, NTRI = G::NTRI;
     constexpr int NB = RT;        // 16x16 diagonal blocks of T
     constexpr int KS = DP + 8;    // LDS row stride of the K / Q pieces (bf16)
@@ -488,6 +493,52 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             if (2 * kt + 1 <= rt) gp[i][1] = gram(0, 2 * kt + 1, 1, rt);
         }
     }
+    // K_c K_{c+1}^T against the next chunk's keys (zero past the sequence), for
+    // H = K_{c+1} K_c^T diag(s) T': wave w takes the rows of H in row tiles it = w, w + 4, ...
+    // The tile pairs over K_c's tokens m are kept as B fragments (k slots m in the permuted
+    // token order, columns the tokens i of chunk c + 1).
+    constexpr int NIT = G::WITH_H ? (RT + 3) / 4 : 0;
+    bf16x8 gnb[NIT > 0 ? NIT : 1][KTC][2];
+    if constexpr (G::WITH_H) {
+        const int64_t rows_next = T - (c0 + C) < C ? T - (c0 + C) : (int64_t)C;  // may be <= 0
+        const TIn* kn = k + ((tok0 + C) * h_qk + hq) * (int64_t)D;
+        const auto r = make_rsrc(rows_next > 0 ? kn : k, rows_next > 0 ? (rows_next - 1) * h_qk * D * (int64_t)sizeof(TIn) + D * (int64_t)sizeof(TIn) : 0);
+#pragma unroll
+        for (int i = 0; i < NIT; ++i) {
+            const int it = w + 4 * i;
+            floatx4 gt[2 * KTC];
+#pragma unroll
+            for (int mt = 0; mt < 2 * KTC; ++mt) gt[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
+            if (it < RT) {
+                bf16x8 bn[KTD][NS];
+#pragma unroll
+                for (int kt = 0; kt < KTD; ++kt) {
+                    const int f = 32 * kt + 8 * lg;
+                    const int off = ((16 * it + lr) * h_qk * D + f) * (int)sizeof(TIn);
+                    to_pieces(buf_raw_frag<TIn>(r, f < D ? off : (int)OOR), bn[kt]);
+                }
+#pragma unroll
+                for (int mt = 0; mt < RT; ++mt) {
+                    floatx4 acc[NPG];
+#pragma unroll
+                    for (int p = 0; p < NPG; ++p) acc[p] = floatx4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kt = 0; kt < KTD; ++kt) {
+                        bf16x8 a[NS];
+#pragma unroll
+                        for (int part = 0; part < NS; ++part)
+                            a[part] = *reinterpret_cast<const bf16x8*>(&s_kq(0, part, 16 * mt + lr, 32 * kt + 8 * lg));
+                        mfma_split_acc<NS, NS>(a, bn[kt], acc);
+                    }
+                    gt[mt] = acc[0];
+#pragma unroll
+                    for (int p = 1; p < NPG; ++p) gt[mt] += acc[p];
+                }
+            }
+#pragma unroll
+            for (int kt = 0; kt < KTC; ++kt) pair_to_frag(gt[2 * kt], gt[2 * kt + 1], gnb[i][kt][0], gnb[i][kt][1]);
+        }
+    }
     __syncthreads();  // the K / Q buffer becomes A / T below
 
     for (int gi = 0; gi < grp; ++gi) {
@@ -647,13 +698,676 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
                 *reinterpret_cast<u32x4*>(tt_base + (size_t)(2 * fi + 1) * 1024 + l * 16) = u32x4{lo[0], lo[1], lo[2], lo[3]};
             }
         }
+
+        // ---- H = K_{c+1} K_c^T diag(s) T' as A fragments (rows: tokens of chunk c + 1, k slots:
+        //      tokens of chunk c, permuted order), formed transposed: H^T = (diag(s) T')^T G^T
+        //      with G^T's B fragments from above. The A operand (diag(s) T')^T holds, for row
+        //      j and k slot of token m, s_m T[m][j] beta_j (zero for m < j), whose fragments
+        //      have the same registers as the B fragments of diag(s) T'.
+        if constexpr (G::WITH_H) {
+            char* hh_base = ws + L.hh + (size_t)vh * G::H_BYTES;
+            const float gam_c = s_gam[CP - 1];
+#pragma unroll
+            for (int i = 0; i < NIT; ++i) {
+                const int it = w + 4 * i;
+                if (it >= RT) continue;
+                floatx4 ht[2 * KTC];  // H^T tiles (jt, it)
+#pragma unroll
+                for (int jt = 0; jt < 2 * KTC; ++jt) {
+                    ht[jt] = floatx4{0.f, 0.f, 0.f, 0.f};
+                    if (jt >= RT) continue;
+#pragma unroll
+                    for (int kt = 0; kt < KTC; ++kt) {
+                        if (32 * kt + 31 < 16 * jt) continue;  // all m < j: zero block
+                        const int j = 16 * jt + lr;
+                        float val[8];
+#pragma unroll
+                        for (int q = 0; q < 8; ++q) {
+                            const int m = tok_of(kt, lg, q);
+                            val[q] = (m >= j && m < C) ? s_rk[m] * expf(gam_c - s_gam[m]) * s_t[m][j] * s_beta[j] : 0.f;
+                        }
+                        uint32_t hi[4], lo[4];
+#pragma unroll
+                        for (int p = 0; p < 4; ++p) split2(val[2 * p], val[2 * p + 1], &hi[p], &lo[p]);
+                        const bf16x8 a[2] = {__builtin_bit_cast(bf16x8, u32x4{hi[0], hi[1], hi[2], hi[3]}),
+                                             __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]})};
+                        ht[jt] = mfma_split<2, 2>(a, gnb[i][kt], ht[jt]);
+                    }
+                }
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt) {
+                    bf16x8 hi, lo;
+                    pair_to_frag(ht[2 * kt], ht[2 * kt + 1], hi, lo);
+                    const int fi = it * KTC + kt;
+                    *reinterpret_cast<bf16x8*>(hh_base + (size_t)(2 * fi) * 1024 + l * 16) = hi;
+                    *reinterpret_cast<bf16x8*>(hh_base + (size_t)(2 * fi + 1) * 1024 + l * 16) = lo;
+                }
+            }
+        }
         __syncthreads();  // s_a, s_t and the gate prefix sums are rewritten for the next V head
     }
 }
 
 // =============================================================================== scan
+// Scan workgroup: one "chain" wave, NSW "state" waves and four "helper" waves.
+//
+// The recursion the chain wave runs involves only X, the residuals V - diag(a) K M of a
+// chunk:
+//   X_{c+1} = V_{c+1} - diag(a_{c+1}) (Gamma_c P_{c+1} + H_c X_c),
+//   P_{c+1} = K_{c+1} M_c,     H_c = K_{c+1} K_c^T diag(s_c) T'_c  (prepared per chunk),
+// since K_{c+1} M_{c+1} = Gamma_c K_{c+1} M_c + K_{c+1} K_c^T W_c and W_c = diag(s_c) T'_c X_c.
+// P_{c+1} needs the state of one chunk earlier, so the state waves, which hold the state
+// split over d_k, form it (with the reduction over d_k) a chunk before it is used: no
+// exchange over d_k sits on the chain's path. The chain wave also forms U = T' X and
+// W = diag(s) U; the state waves apply M_{c+1} = Gamma_c M_c + K_c^T W_c one chunk later,
+// and the helpers form the outputs O_c = diag(o) Q_c M_c + Ptil_c U_c. The helpers also
+// move every input into LDS ahead of its use: global loads are the scarce resource here
+// (a load whose lanes cover 16 rows of 64 bytes, the MFMA fragment shape of a bf16 row,
+// runs at about a third of the rate of one covering whole 128-byte lines), so K and Q are
+// loaded as whole token rows and rewritten in LDS, where both K fragments and transposed
+// K^T fragments are read from the same copy.
+//
+// Time advances in windows c = -2, -1, ..., nch - 1 (and one idle window more when that
+// count is odd, so that the two-window loops below have no conditional half), each opened
+// by a workgroup barrier:
+//   chain   window c: X_{c+1}, U_{c+1}, W_{c+1}        (c >= -1)
+//   state   window c: M_{c+1} (c >= 0); Gamma_{c+1} P_{c+2} and K_{c+2}^T fragments
+//   helpers window c: outputs of chunk c (c >= 0); stage K_{c+3}, H_{c+1}, and T', the V
+//                     block and the scalars a, s, o, Gamma_C of chunk c + 2
+// Each exchange buffer is double-buffered by chunk parity (the scalars by chunk mod 4).
 template <int D, int C, typename TIn>
 struct ScanGeo {
+    using G = Geo<D, C, std::is_same<TIn, float>::value>;
+    static constexpr int ES = sizeof(TIn);
+    static constexpr int NSW = G::KTD >= 2 ? 2 : 1;       // state waves
+    static constexpr int KPS = G::KTD / NSW;               // d_k tiles per state wave
+    static constexpr int NHW = 4;                          // helper waves
+    static constexpr int THREADS = 64 * (1 + NSW + NHW);
+    static constexpr int RTH = (G::RT + NHW - 1) / NHW;    // output row tiles per helper
+    // Staged rows: one bf16 piece of DP features in 16-byte granules; granule j of row r sits
+    // at position j ^ swz(r).
+    static constexpr int ROWB = G::DP * 2;                 // bytes per staged row
+    static constexpr int RPB = 256 / ROWB;                 // staged rows per 64 LDS banks
+    // Raw q/k rows: RB bytes, loaded as LPR lanes of 16 bytes, RPI rows per instruction.
+    static constexpr int RB = D * ES;
+    static constexpr int LPR = RB / 16;
+    static constexpr int RPI = 64 / LPR;
+    static constexpr int NKI = (C + RPI - 1) / RPI;        // K row loads per chunk
+    static constexpr int NKH = (NKI + NHW - 1) / NHW;      // ... per helper
+    static constexpr int QR = RPI > 16 ? RPI : 16;         // staged Q rows per row tile
+    static constexpr int NQI = QR / RPI;                   // Q row loads per row tile
+    // The V block (16 channels of a token): LPT lanes per token, TPI tokens per load.
+    static constexpr int LPT = ES;
+    static constexpr int TPI = 64 / LPT;
+    static constexpr int NVI = (C + TPI - 1) / TPI;
+    static constexpr int VS = G::CP + 4;                   // LDS row stride of the V block
+    static constexpr size_t K_BYTES = (size_t)G::NS * G::CP * ROWB;
+    static constexpr size_t QH_BYTES = (size_t)RTH * QR * ROWB;  // one helper's Q rows
+    static constexpr size_t BASE = 2 * K_BYTES + (size_t)2 * 16 * VS * 4 + (size_t)4 * 256 * 4 +
+                                   (size_t)2 * NSW * G::RT * 1024 + (size_t)2 * G::KTC * 2048 +
+                                   (size_t)2 * G::RT * 1024 + (size_t)2 * G::KTD * 2048;
+    static constexpr size_t LIM = 160 * 1024;
+    // H, T' and (bf16) Q rows are staged in LDS in that order of priority while they fit;
+    // otherwise H and T' are read from the workspace by the chain wave and Q fragments are
+    // loaded directly by the helpers.
+    static constexpr bool HLDS = BASE + 2 * G::H_BYTES <= LIM;
+    static constexpr size_t AFTER_H = BASE + (HLDS ? 2 * G::H_BYTES : 0);
+    static constexpr bool TLDS = AFTER_H + 2 * G::TRI_BYTES <= LIM;
+    static constexpr size_t AFTER_T = AFTER_H + (TLDS ? 2 * G::TRI_BYTES : 0);
+    static constexpr bool QST = ES == 2 && AFTER_T + NHW * QH_BYTES <= LIM;
+};
+
+// Granule swizzle of the staged rows. A fragment read (16 consecutive rows, one granule)
+// and a transposing read (4 consecutive rows x 4 consecutive granules per 16 lanes) then
+// each touch 16 distinct 16-byte bank groups.
+template <int RPB>
+__device__ __forceinline__ int swz(int r)
+{
+    return ((r >> 2) & 3) | (((r & 3) / RPB) << 2);
+}
+
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+
+// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group, output lane j
+// receives in slot p element (j mod 4) of the 8 bytes addressed by lane 4 p + j / 4 of the
+// group (established with an in-bounds probe of the instruction).
+__device__ __forceinline__ bf16x4 lds_read_tr16(const void* p)
+{
+    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf16;
+    const v4bf16 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) v4bf16*)(p));
+    return __builtin_bit_cast(bf16x4, r);
+}
+
+template <int D, int C, typename TIn>
+__global__ void __launch_bounds__((ScanGeo<D, C, TIn>::THREADS))
+chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+                  const char* __restrict__ ws, ChunkWs L, const float* state_in,
+                  float* __restrict__ out, float* state_out, int64_t T, int h_qk, int h_v,
+                  int64_t nblocks)
+{
+    constexpr bool F32IN = std::is_same<TIn, float>::value;
+    using G = Geo<D, C, F32IN>;
+    using SG = ScanGeo<D, C, TIn>;
+    using Raw = typename RawFrag<TIn>::type;
+    constexpr int CP = G::CP, RT = G::RT, KTC = G::KTC, KTD = G::KTD, NS = G::NS;
+    constexpr int NTRI = G::NTRI, NHF = G::NHF;
+    constexpr int NSW = SG::NSW, KPS = SG::KPS, NHW = SG::NHW;
+    constexpr int ROWB = SG::ROWB, RPB = SG::RPB, LPR = SG::LPR, RPI = SG::RPI;
+    constexpr int NKI = SG::NKI, NKH = SG::NKH, QR = SG::QR, NQI = SG::NQI;
+    constexpr int LPT = SG::LPT, TPI = SG::TPI, NVI = SG::NVI;
+    constexpr int ES = SG::ES;
+    constexpr bool HLDS = SG::HLDS, TLDS = SG::TLDS, QST = SG::QST;
+
+    // LDS (parity = chunk index mod 2):
+    //   s_k   K rows of a chunk (NS bf16 planes, swizzled granules), by parity
+    //   s_q   each helper's Q rows (bf16 inputs)
+    //   s_h   H of a chunk (A fragments hi, lo), by parity
+    //   s_tf  T' of a chunk, s_vt its V block (channel-major fp32), by parity
+    //   s_sc  the scalars of a chunk (a, s, o, Gamma_C as laid out in the workspace), by
+    //         chunk mod 4
+    //   s_p   each state wave's part of Gamma_c P_{c+1}, by parity of c + 1
+    //   s_wf  W as B fragments (hi, lo), s_uf U (fp32, accumulator layout), by parity
+    //   s_mf  the state entering a chunk as B fragments (hi, lo), by parity
+    __shared__ __align__(16) char s_k[2][SG::K_BYTES];
+    __shared__ __align__(16) char s_q[QST ? NHW * SG::QH_BYTES : 16];
+    __shared__ __align__(16) bf16x8 s_h[HLDS ? 2 : 1][HLDS ? 2 * NHF : 1][64];
+    __shared__ __align__(16) bf16x8 s_tf[TLDS ? 2 : 1][TLDS ? 2 * NTRI : 1][64];
+    __shared__ __align__(16) float s_vt[2][16][SG::VS];
+    __shared__ __align__(16) float s_sc[4][256];
+    __shared__ __align__(16) floatx4 s_p[2][NSW][RT][64];
+    __shared__ __align__(16) bf16x8 s_wf[2][KTC][2][64];
+    __shared__ __align__(16) floatx4 s_uf[2][RT][64];
+    __shared__ __align__(16) bf16x8 s_mf[2][KTD][2][64];
+
+    // Workgroups that share a QK head run on the same XCD (blockIdx % 8 picks the XCD), so
+    // their common K/Q/H/T'/Ptil reads meet in one L2.
+    int64_t lin = blockIdx.x;
+    if (nblocks % 8 == 0) lin = (int64_t)(blockIdx.x % 8) * (nblocks / 8) + blockIdx.x / 8;
+    const int cb = (int)(lin % (D / 16));
+    const int64_t nh = lin / (D / 16);
+    const int64_t seq = nh / h_v;
+    const int h = (int)(nh - seq * h_v);
+    const int hq = h / (h_v / h_qk);
+    const int tid = threadIdx.x, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+    const int64_t nch = L.nch;
+    const int64_t cend = -2 + ((nch + 3) & ~(int64_t)1);  // windows -2 .. cend - 1, an even count
+
+    // Byte strides between consecutive tokens of q/k, v and out.
+    const int64_t row_qk = (int64_t)h_qk * D * ES;
+    const int64_t row_v = (int64_t)h_v * D * ES;
+    const int64_t row_o = (int64_t)h_v * D * 4;
+    auto par = [](int64_t c) { return (int)(c & 1); };
+    auto clampc = [&](int64_t c) { return c < 0 ? 0 : (c < nch ? c : nch - 1); };
+    auto tok0_of = [&](int64_t c) { return seq * T + c * C; };
+    auto rows_of = [&](int64_t c) { return (T - c * C) < C ? (T - c * C) : (int64_t)C; };
+    auto vh_of = [&](int64_t c) { return (size_t)((seq * nch + c) * h_v + h); };
+    auto sc_rsrc = [&](int64_t c) { return make_rsrc(ws + L.sc + vh_of(c) * G::SC_BYTES, G::SC_BYTES); };
+    auto ws_rsrc = [&](size_t region, size_t bytes, int64_t c, bool on) {
+        return make_rsrc(ws + region + vh_of(c) * bytes, on ? (int64_t)bytes : 0);
+    };
+    // q or k rows of chunk c (rows past the sequence read zero)
+    auto qk_rsrc = [&](const TIn* base, int64_t c) {
+        return make_rsrc(base + (tok0_of(c) * h_qk + hq) * (int64_t)D, (rows_of(c) - 1) * row_qk + D * ES);
+    };
+    // A lane-dependent condition selects between two constants and is added, rather than
+    // guarding the address computation: lane-divergent branches anywhere in this kernel
+    // would let the register allocator place copies under a partial exec mask.
+    auto pad_if = [&](bool in_range) { return in_range ? 0u : OOR; };
+    // Byte offset of granule j of staged row r.
+    auto srow = [&](int r, int j) { return r * ROWB + 16 * (j ^ swz<RPB>(r)); };
+    // A full wait: nothing left in flight, so the compiler's wait bookkeeping starts clean.
+    auto settle = [&]() { __builtin_amdgcn_s_waitcnt(0); };
+    // Four consecutive staged values of accumulator rows 4 lg .. 4 lg + 3 of row tile rt.
+    auto vt4 = [&](int p, int rt) { return *reinterpret_cast<const floatx4*>(&s_vt[p][lr][16 * rt + 4 * lg]); };
+    auto sc4 = [&](int64_t c, int off) { return *reinterpret_cast<const floatx4*>(&s_sc[c & 3][off + 4 * lg]); };
+    auto gc_of = [&](int64_t c) { return s_sc[c & 3][3 * CP]; };
+
+    if (w == 0) {
+        // ======================================================= chain wave
+        __syncthreads();  // the helpers have cleared the staged-row buffers
+        bf16x8 xf[KTC][2];  // X of the latest chunk as B fragments (hi, lo)
+#pragma unroll
+        for (int kt = 0; kt < KTC; ++kt) xf[kt][0] = xf[kt][1] = bf16x8{};
+#pragma unroll 1
+        for (int64_t c = -2; c < cend; ++c) {
+            __syncthreads();
+            if (c < -1 || c + 1 >= nch) continue;  // wave-uniform
+            const int pn = par(c + 1), pc = par(c);
+            // Z = Gamma_c P_{c+1} (the state waves' parts summed in wave order) + H_c X_c
+            floatx4 z[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                z[rt] = s_p[pn][0][rt][l];
+#pragma unroll
+                for (int sw = 1; sw < NSW; ++sw) z[rt] += s_p[pn][sw][rt][l];
+            }
+            if (c >= 0) {
+                const auto r_h = ws_rsrc(L.hh, G::H_BYTES, c, !HLDS);
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                    for (int kt = 0; kt < KTC; ++kt) {
+                        const int fi = rt * KTC + kt;
+                        bf16x8 hf[2];
+#pragma unroll
+                        for (int p = 0; p < 2; ++p) {
+                            if constexpr (HLDS)
+                                hf[p] = s_h[pc][2 * fi + p][l];
+                            else
+                                hf[p] = buf_bf16x8(r_h, (2 * fi + p) * 1024 + l * 16);
+                        }
+                        z[rt] = mfma_split<2, 2>(hf, xf[kt], z[rt]);
+                    }
+            }
+            // X_{c+1} = V - diag(a) Z
+            floatx4 xv[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) xv[rt] = vt4(pn, rt) - sc4(c + 1, 16 * rt) * z[rt];
+            rows_to_frags<RT, KTC>(xv, xf);
+            // U = T' X (lower triangular: row tile rt uses token k tiles 0 .. rt / 2)
+            const auto r_t = ws_rsrc(L.tt, G::TRI_BYTES, c + 1, !TLDS);
+            floatx4 u[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kt = 0; 2 * kt <= rt; ++kt) {
+                    const int pi = 2 * (tri_off(rt) + kt);
+                    bf16x8 tf[2];
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) {
+                        if constexpr (TLDS)
+                            tf[p] = s_tf[pn][pi + p][l];
+                        else
+                            tf[p] = buf_bf16x8(r_t, (pi + p) * 1024 + l * 16);
+                    }
+                    acc = mfma_split<2, 2>(tf, xf[kt], acc);
+                }
+                u[rt] = acc;
+            }
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) s_uf[pn][rt][l] = u[rt];
+            // W = diag(s) U for the state waves
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) u[rt] *= sc4(c + 1, CP + 16 * rt);
+            bf16x8 wf[KTC][2];
+            rows_to_frags<RT, KTC>(u, wf);
+#pragma unroll
+            for (int kt = 0; kt < KTC; ++kt)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) s_wf[pn][kt][p][l] = wf[kt][p];
+        }
+    } else if (w <= NSW) {
+        // ======================================================= state wave sw
+        // State tiles 2 KPS sw .. 2 KPS (sw + 1) - 1, i.e. d_k tiles KPS sw .. KPS (sw + 1) - 1.
+        const int sw = w - 1;
+        const int64_t sbase = nh * (int64_t)D * D;
+        // The state block through buffer resources: padded features (D = 16) fall outside
+        // the range, and a missing initial state is an empty range, so both read zero.
+        auto st_off = [&](int mt, int e) {
+            const int f = feat_of(mt, 4 * lg + e);
+            return (int)((uint32_t)((f * D + cb * 16 + lr) * 4) + pad_if(f < D));
+        };
+        floatx4 macc[2 * KPS];
+        {
+            const auto r = make_rsrc(state_in + (state_in ? sbase : 0), state_in ? (int64_t)D * D * 4 : 0);
+#pragma unroll
+            for (int i = 0; i < 2 * KPS; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) macc[i][e] = buf_elem<float>(r, st_off(2 * KPS * sw + i, e));
+        }
+        bf16x8 mf[KPS][2];  // this wave's d_k tiles of the state as B fragments (hi, lo)
+        auto split_publish = [&](int p) {
+#pragma unroll
+            for (int kk = 0; kk < KPS; ++kk) {
+                pair_to_frag(macc[2 * kk], macc[2 * kk + 1], mf[kk][0], mf[kk][1]);
+#pragma unroll
+                for (int pp = 0; pp < 2; ++pp) s_mf[p][KPS * sw + kk][pp][l] = mf[kk][pp];
+            }
+        };
+        split_publish(0);  // the state entering chunk 0, for the helpers
+        __syncthreads();   // the helpers have cleared the staged-row buffers
+
+        // K^T A fragments of a chunk for this wave's state tiles, read two windows before the
+        // state update that uses them (so the staged K rows need only two buffers). Fragment
+        // (i, kt): two transposing reads (token slots 0..3, 4..7); lane lr of group lg
+        // addresses token row 32 kt + 16 h + 4 lg + lr / 4 and features
+        // 32 (KPS sw + i / 2) + 8 (lr % 4) + 4 (i % 2) + 0..3.
+        bf16x8 ktA[2 * KPS][KTC][NS], ktB[2 * KPS][KTC][NS];
+        auto read_kt = [&](bf16x8 (*kts)[KTC][NS], int p) {
+#pragma unroll
+            for (int i = 0; i < 2 * KPS; ++i)
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt)
+#pragma unroll
+                    for (int part = 0; part < NS; ++part) {
+                        const int r = 32 * kt + 4 * lg + (lr >> 2);
+                        const int j = 4 * (KPS * sw + (i >> 1)) + (lr & 3);
+                        const char* base = s_k[p] + part * CP * ROWB + 8 * (i & 1);
+                        const bf16x4 a = lds_read_tr16(base + srow(r, j));
+                        const bf16x4 b = lds_read_tr16(base + srow(r + 16, j));
+                        kts[i][kt][part] = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+                    }
+        };
+        auto window = [&](int64_t c, bf16x8 (*kts)[KTC][NS]) {
+            __syncthreads();
+            if (c >= 0 && c < nch) {
+                // M_{c+1} = Gamma_c M_c + K_c^T W_c
+                const int pc = par(c);
+                const float gcc = gc_of(c);
+                bf16x8 wf[KTC][2];
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) wf[kt][p] = s_wf[pc][kt][p][l];
+#pragma unroll
+                for (int i = 0; i < 2 * KPS; ++i) {
+                    floatx4 acc = gcc * macc[i];
+#pragma unroll
+                    for (int kt = 0; kt < KTC; ++kt) acc = mfma_split<NS, 2>(kts[i][kt], wf[kt], acc);
+                    macc[i] = acc;
+                }
+                split_publish(par(c + 1));  // the state entering chunk c + 1, for the helpers
+            }
+            if (c + 2 < nch) {
+                // Gamma_{c+1} K_{c+2} M_{c+1} over this wave's features (unscaled for chunk 0)
+                const int p2 = par(c + 2);
+                const float scale = c >= -1 ? gc_of(c + 1) : 1.f;
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) {
+                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kk = 0; kk < KPS; ++kk) {
+                        bf16x8 ka[NS];
+#pragma unroll
+                        for (int part = 0; part < NS; ++part)
+                            ka[part] = *reinterpret_cast<const bf16x8*>(
+                                s_k[p2] + part * CP * ROWB + srow(16 * rt + lr, 4 * (KPS * sw + kk) + lg));
+                        acc = mfma_split<NS, 2>(ka, mf[kk], acc);
+                    }
+                    s_p[p2][sw][rt][l] = scale * acc;
+                }
+                read_kt(kts, p2);  // K^T of chunk c + 2 replaces K^T of chunk c
+            }
+        };
+        // Chunk parity alternates between windows, and so do the two K^T register sets.
+#pragma unroll 1
+        for (int64_t c = -2; c < cend; c += 2) {
+            window(c, ktA);
+            window(c + 1, ktB);
+        }
+
+        {
+            const auto r = make_rsrc(state_out + sbase, (int64_t)D * D * 4);
+#pragma unroll
+            for (int i = 0; i < 2 * KPS; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) {
+                    const float val = macc[i][e];
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(val), r, st_off(2 * KPS * sw + i, e), 0, 0);
+                }
+        }
+    } else {
+        // ======================================================= helper wave hw
+        // Row tiles hw, hw + 4, ... of the outputs, and shares of the staging. Each helper
+        // runs code specialised for its index, so its sequence of vector memory operations has
+        // no branches: the compiler then counts exactly which loads are still in flight and
+        // waits only for the operand set it uses, not for the one loaded after it.
+        const int hw = w - 1 - NSW;
+
+        // Clear the staged rows once: rows past a short chunk and features past D are never
+        // written afterwards and must read as zero. (The sizes are multiples of 1 KB, so
+        // every lane makes the same number of trips.)
+        for (int o = 1024 * hw; o < (int)(2 * SG::K_BYTES); o += 1024 * NHW)
+            *reinterpret_cast<u32x4*>(&s_k[0][0] + o + 16 * l) = u32x4{0u, 0u, 0u, 0u};
+        if constexpr (QST) {
+            for (int o = 0; o < (int)SG::QH_BYTES; o += 1024)
+                *reinterpret_cast<u32x4*>(s_q + hw * SG::QH_BYTES + o + 16 * l) = u32x4{0u, 0u, 0u, 0u};
+        }
+        __syncthreads();
+
+        auto helper = [&](auto hw_const) {
+            constexpr int HW = decltype(hw_const)::value;
+            // Helpers 0 .. NOH - 1 form the outputs. The staging (K rows, H and T' pieces) is
+            // spread over the helpers without output rows where there are such (C <= 32),
+            // otherwise over all four; the V block and the scalars come from the last two.
+            constexpr int NOH = RT < NHW ? RT : NHW;
+            constexpr int SH0 = NOH < NHW ? NOH : 0, NSH = NHW - SH0;
+            constexpr int HS = HW - SH0;  // index among the staging helpers (< 0: none)
+            constexpr bool VST = HW == NHW - 2, SST = HW == NHW - 1;
+            constexpr int NRT = RT > HW ? (RT - HW + NHW - 1) / NHW : 0;  // this helper's row tiles
+            constexpr auto share = [](int n, int j, int of) { return j >= 0 && n > j ? (n - j + of - 1) / of : 0; };
+            constexpr int NKM = share(NKI, HS, NSH);       // its K row loads
+            constexpr int NHM = share(2 * NHF, HS, NSH);   // its H pieces
+            constexpr int NTM = share(2 * NTRI, HS, NSH);  // its T' pieces
+            char* const s_qh = s_q + (QST ? HW * SG::QH_BYTES : 0);
+
+            // ---- the operand set of window c; two sets alternate, each loaded two windows
+            //      ahead
+            struct HSet {
+                u32x4 kr[NKM > 0 ? NKM : 1];                    // K rows of chunk c + 3
+                bf16x8 hs[NHM > 0 ? NHM : 1];                   // H pieces of chunk c + 1
+                bf16x8 tst[NTM > 0 ? NTM : 1];                  // T' pieces of chunk c + 2
+                u32x4 vr[VST ? NVI : 1];                        // V block of chunk c + 2
+                u32x4 scv;                                      // scalars of chunk c + 2
+                u32x4 qrw[QST && NRT > 0 ? NRT : 1][QST ? NQI : 1];  // Q rows of chunk c + 1,
+                Raw qf[!QST && NRT > 0 ? NRT : 1][QST ? 1 : KTD];    //   or Q fragments of c
+                bf16x8 pf[NRT > 0 ? NRT : 1][KTC][2];           // Ptil^T fragments of chunk c
+            };
+            auto ld_k = [&](u32x4* kr, int64_t c) {
+                const auto r = qk_rsrc(k, clampc(c));
+#pragma unroll
+                for (int m = 0; m < NKM; ++m) {
+                    const int row = RPI * (HS + NSH * m) + l / LPR;
+                    kr[m] = __builtin_amdgcn_raw_buffer_load_b128(
+                        r, (int)((uint32_t)(row * row_qk) + (uint32_t)(16 * (l % LPR)) + pad_if(row < C)), 0, 0);
+                }
+            };
+            // K rows into s_k[p] (bf16 pieces; fp32 rows are split into hi and lo planes)
+            auto st_k = [&](const u32x4* kr, int p) {
+#pragma unroll
+                for (int m = 0; m < NKM; ++m) {
+                    const int row = RPI * (HS + NSH * m) + l / LPR, g = l % LPR;
+                    if constexpr (ES == 2) {
+                        *reinterpret_cast<u32x4*>(s_k[p] + srow(row, g)) = kr[m];
+                    } else {
+                        const floatx4 x = __builtin_bit_cast(floatx4, kr[m]);
+                        uint32_t hi[2], lo[2];
+                        split2(x[0], x[1], &hi[0], &lo[0]);
+                        split2(x[2], x[3], &hi[1], &lo[1]);
+                        const int o = srow(row, g >> 1) + 8 * (g & 1);
+                        *reinterpret_cast<uint2*>(s_k[p] + o) = uint2{hi[0], hi[1]};
+                        *reinterpret_cast<uint2*>(s_k[p] + CP * ROWB + o) = uint2{lo[0], lo[1]};
+                    }
+                }
+            };
+            auto load_set = [&](HSet& x, int64_t c) {
+                ld_k(x.kr, c + 3);
+                if constexpr (HLDS) {
+                    const auto r = ws_rsrc(L.hh, G::H_BYTES, clampc(c + 1), true);
+#pragma unroll
+                    for (int m = 0; m < NHM; ++m) x.hs[m] = buf_bf16x8(r, (HS + NSH * m) * 1024 + l * 16);
+                }
+                if constexpr (TLDS) {
+                    const auto r = ws_rsrc(L.tt, G::TRI_BYTES, clampc(c + 2), true);
+#pragma unroll
+                    for (int m = 0; m < NTM; ++m) x.tst[m] = buf_bf16x8(r, (HS + NSH * m) * 1024 + l * 16);
+                }
+                const int64_t c2 = clampc(c + 2);
+                if constexpr (VST) {
+                    const auto r_v = make_rsrc(v + (tok0_of(c2) * h_v + h) * (int64_t)D + cb * 16,
+                                               (rows_of(c2) - 1) * row_v + 16 * ES);
+#pragma unroll
+                    for (int m = 0; m < NVI; ++m) {
+                        const int t = TPI * m + l / LPT;
+                        x.vr[m] = __builtin_amdgcn_raw_buffer_load_b128(
+                            r_v, (int)((uint32_t)(t * row_v) + (uint32_t)(16 * (l % LPT)) + pad_if(t < C)), 0, 0);
+                    }
+                }
+                if constexpr (SST)
+                    x.scv = __builtin_amdgcn_raw_buffer_load_b128(sc_rsrc(c2), 16 * l, 0, 0);
+#pragma unroll
+                for (int i = 0; i < NRT; ++i) {
+                    const int rt = HW + NHW * i;
+                    if constexpr (QST) {
+                        const auto r = qk_rsrc(q, clampc(c + 1));
+#pragma unroll
+                        for (int m = 0; m < NQI; ++m) {
+                            const int rl = RPI * m + l / LPR;
+                            x.qrw[i][m] = __builtin_amdgcn_raw_buffer_load_b128(
+                                r, (int)((uint32_t)((16 * rt + rl) * row_qk) + (uint32_t)(16 * (l % LPR)) + pad_if(rl < 16)),
+                                0, 0);
+                        }
+                    } else {
+                        const auto r = qk_rsrc(q, clampc(c));
+#pragma unroll
+                        for (int kt = 0; kt < KTD; ++kt) {
+                            const int f = 32 * kt + 8 * lg;
+                            x.qf[i][kt] = buf_raw_frag<TIn>(
+                                r, (int)((uint32_t)((16 * rt + lr) * row_qk) + (uint32_t)(f * ES) + pad_if(f < D)));
+                        }
+                    }
+                    const auto r = ws_rsrc(L.pt, G::TRI_BYTES, clampc(c), true);
+#pragma unroll
+                    for (int kt = 0; 2 * kt <= rt; ++kt) {
+                        const int o = (tri_off(rt) + kt) * 2048 + l * 16;
+                        x.pf[i][kt][0] = buf_bf16x8(r, o);
+                        x.pf[i][kt][1] = buf_bf16x8(r, o + 1024);
+                    }
+                }
+            };
+            // The staging writes of window c.
+            auto store_set = [&](const HSet& x, int64_t c) {
+                if (c + 3 < nch) st_k(x.kr, par(c + 3));
+                if constexpr (HLDS) {
+                    if (c + 1 >= 0 && c + 1 < nch) {
+#pragma unroll
+                        for (int m = 0; m < NHM; ++m) s_h[par(c + 1)][HS + NSH * m][l] = x.hs[m];
+                    }
+                }
+                if (c + 2 < nch) {
+                    const int p = par(c + 2);
+                    if constexpr (TLDS) {
+#pragma unroll
+                        for (int m = 0; m < NTM; ++m) s_tf[p][HS + NSH * m][l] = x.tst[m];
+                    }
+                    if constexpr (VST) {
+#pragma unroll
+                        for (int m = 0; m < NVI; ++m) {
+                            const int t = TPI * m + l / LPT;  // < CP
+                            if constexpr (ES == 2) {
+                                const bf16x8 y = __builtin_bit_cast(bf16x8, x.vr[m]);
+#pragma unroll
+                                for (int e = 0; e < 8; ++e) s_vt[p][8 * (l % LPT) + e][t] = (float)y[e];
+                            } else {
+                                const floatx4 y = __builtin_bit_cast(floatx4, x.vr[m]);
+#pragma unroll
+                                for (int e = 0; e < 4; ++e) s_vt[p][4 * (l % LPT) + e][t] = y[e];
+                            }
+                        }
+                    }
+                    // the scalar block (lanes past it carry whatever lies beyond; never read)
+                    if constexpr (SST) *reinterpret_cast<u32x4*>(&s_sc[(c + 2) & 3][4 * l]) = x.scv;
+                }
+                // Q rows of chunk c + 1, after this window's reads of chunk c's
+                if constexpr (QST) {
+                    if (c + 1 >= 0 && c + 1 < nch) {
+#pragma unroll
+                        for (int i = 0; i < NRT; ++i)
+#pragma unroll
+                            for (int m = 0; m < NQI; ++m)
+                                *reinterpret_cast<u32x4*>(s_qh + i * QR * ROWB + srow(RPI * m + l / LPR, l % LPR)) =
+                                    x.qrw[i][m];
+                    }
+                }
+            };
+            // Outputs of chunk c, formed transposed: O^T = (Q M_c)^T diag(o) + U^T Ptil^T as 16
+            // value channels x 16 tokens tiles; the state and U fragments serve unchanged as A
+            // operands, the Q row fragments and Ptil^T as B operands, and each lane ends up with
+            // four consecutive channels of one token (one 16-byte store). Windows outside the
+            // chunks store out of range.
+            auto do_output = [&](const HSet& x, int64_t c) {
+                if constexpr (NRT > 0) {
+                    const bool live = c >= 0 && c < nch;  // wave-uniform
+                    c = clampc(c);
+                    const int pc = par(c);
+                    bf16x8 mfr[KTD][2];
+#pragma unroll
+                    for (int kt = 0; kt < KTD; ++kt)
+#pragma unroll
+                        for (int p = 0; p < 2; ++p) mfr[kt][p] = s_mf[pc][kt][p][l];
+                    floatx4 urow[RT];
+#pragma unroll
+                    for (int rt = 0; rt < RT; ++rt) urow[rt] = s_uf[pc][rt][l];
+                    bf16x8 ufr[KTC][2];
+                    rows_to_frags<RT, KTC>(urow, ufr);
+                    const auto r_o = make_rsrc(out + (tok0_of(c) * h_v + h) * (int64_t)D + cb * 16,
+                                               (rows_of(c) - 1) * row_o + 64);
+#pragma unroll
+                    for (int i = 0; i < NRT; ++i) {
+                        const int rt = HW + NHW * i;
+                        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                        for (int kt = 0; kt < KTD; ++kt) {
+                            bf16x8 qa[NS];
+                            if constexpr (QST)
+                                qa[0] = *reinterpret_cast<const bf16x8*>(s_qh + i * QR * ROWB + srow(lr, 4 * kt + lg));
+                            else
+                                to_pieces(x.qf[i][kt], qa);
+                            acc = mfma_split<2, NS>(mfr[kt], qa, acc);
+                        }
+                        acc *= s_sc[c & 3][2 * CP + 16 * rt + lr];  // o of token 16 rt + lr
+#pragma unroll
+                        for (int kt = 0; 2 * kt <= rt; ++kt) acc = mfma_split<2, 2>(ufr[kt], x.pf[i][kt], acc);
+                        __builtin_amdgcn_raw_buffer_store_b128(
+                            __builtin_bit_cast(u32x4, acc), r_o,
+                            (int)((uint32_t)((16 * rt + lr) * row_o) + (uint32_t)(lg * 16) + pad_if(live)), 0, 0);
+                    }
+                }
+            };
+
+            // Prologue: K rows of chunk 0 into LDS; the sets of windows -2 and -1 in flight.
+            {
+                u32x4 kr0[NKM > 0 ? NKM : 1];
+                ld_k(kr0, 0);
+                settle();
+                st_k(kr0, par(0));
+            }
+            HSet A, B;
+            load_set(A, -2);
+            load_set(B, -1);
+            auto window = [&](HSet& x, int64_t c) {
+                __syncthreads();
+                do_output(x, c);
+                store_set(x, c);
+                __builtin_amdgcn_sched_barrier(0);
+                load_set(x, c + 2);
+            };
+#pragma unroll 1
+            for (int64_t c = -2; c < cend; c += 2) {
+                window(A, c);
+                window(B, c + 1);
+            }
+            settle();
+        };
+        static_assert(NHW == 4, "the helper dispatch below covers four helpers");
+        switch (hw) {
+            case 0: helper(std::integral_constant<int, 0>{}); break;
+            case 1: helper(std::integral_constant<int, 1>{}); break;
+            case 2: helper(std::integral_constant<int, 2>{}); break;
+            default: helper(std::integral_constant<int, 3>{}); break;
+        }
+    }
+}
+
+// ======================================================================= scan, C = 128
+// At C = 128 the pipeline above does not fit LDS (its double-buffered exchange state alone
+// exceeds 160 KB at d = 128). This variant keeps the state in two "chain" waves (halves of
+// d_k), which run the recurrence with one exchange of partial K M0 products per chunk, while
+// two "output" waves stage T', V and the scalars and form the outputs one chunk behind.
+template <int D, int C, typename TIn>
+struct WideGeo {
     using G = Geo<D, C, std::is_same<TIn, float>::value>;
     // Two operand sets alternate (the next chunk's loads fly while this chunk computes)
     // when both fit the register file; at C = 128 one set is loaded per chunk.
@@ -679,29 +1393,17 @@ struct ScanGeo {
 
 // Operands a chain wave loads for chunk c: the K rows of chunk c + 1.
 template <int D, int C, typename TIn>
-struct ChainSet {
+struct WideChainSet {
     using G = Geo<D, C, std::is_same<TIn, float>::value>;
     typename RawFrag<TIn>::type kr[G::RT][G::KTH];  // K rows of chunk c + 1 (A fragments)
 };
 
-typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
-
-// Transposing LDS read (gfx950 ds_read_b64_tr_b16). Within each 16-lane group, output
-// lane j receives in slot p element (j mod 4) of the 8 bytes addressed by lane
-// 4 p + j / 4 of the group (established with an in-bounds probe of the instruction).
-__device__ __forceinline__ bf16x4 lds_read_tr16(const __bf16* p)
-{
-    typedef __attribute__((__vector_size__(4 * sizeof(__bf16)))) __bf16 v4bf16;
-    const v4bf16 r = __builtin_amdgcn_ds_read_tr16_b64_v4bf16((__attribute__((address_space(3))) v4bf16*)(p));
-    return __builtin_bit_cast(bf16x4, r);
-}
-
 // Operands an output wave loads for window j (finishing chunk j - 1, starting chunk j),
 // and what it stages for the chain waves' chunk j + 1.
 template <int D, int C, typename TIn>
-struct OutSet {
+struct WideOutSet {
     using G = Geo<D, C, std::is_same<TIn, float>::value>;
-    using SG = ScanGeo<D, C, TIn>;
+    using SG = WideGeo<D, C, TIn>;
     typename RawFrag<TIn>::type qr[G::RTO][G::KTD];  // Q rows of chunk j (A fragments)
     bf16x8 pf[G::RTO][G::KTC][2];                     // Ptil^T of chunk j - 1 (B fragments)
     float ov[G::RTO];                                 // scalar o of token lr of each row tile
@@ -722,17 +1424,17 @@ __device__ __forceinline__ float elem_f32(const floatx8& r, int e)
 
 template <int D, int C, typename TIn>
 __global__ void __launch_bounds__(256)
-chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
+chunk_scan_wide_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
                   const char* __restrict__ ws, ChunkWs L, const float* state_in,
                   float* __restrict__ out, float* state_out, int64_t T, int h_qk, int h_v,
                   int64_t nblocks)
 {
     constexpr bool F32IN = std::is_same<TIn, float>::value;
     using G = Geo<D, C, F32IN>;
-    using SG = ScanGeo<D, C, TIn>;
+    using SG = WideGeo<D, C, TIn>;
     using Raw = typename RawFrag<TIn>::type;
-    using CS = ChainSet<D, C, TIn>;
-    using OS = OutSet<D, C, TIn>;
+    using CS = WideChainSet<D, C, TIn>;
+    using OS = WideOutSet<D, C, TIn>;
     constexpr int CP = G::CP, RT = G::RT, KTC = G::KTC, KTD = G::KTD, NS = G::NS;
     constexpr int NTRI = G::NTRI, NCH = G::NCH, KTH = G::KTH, MTH = G::MTH;
     constexpr int NOW = G::NOW, RTO = G::RTO, NTS = SG::NTS, CPV = SG::CPV, TPL = SG::TPL;
@@ -1171,9 +1873,15 @@ hipError_t launch_chunked_t(const Call& cl)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t scan_blocks = cl.n * cl.h_v * (D / 16);
-    hipLaunchKernelGGL((chunk_scan_kernel<D, C, TIn>), dim3((unsigned)scan_blocks), dim3(256), 0,
-                       cl.stream, q, k, v, ws, L, cl.state_in, cl.out, cl.state_out, cl.t,
-                       cl.h_qk, cl.h_v, scan_blocks);
+    if constexpr (C <= 64) {
+        hipLaunchKernelGGL((chunk_scan_kernel<D, C, TIn>), dim3((unsigned)scan_blocks),
+                           dim3(ScanGeo<D, C, TIn>::THREADS), 0, cl.stream, q, k, v, ws, L,
+                           cl.state_in, cl.out, cl.state_out, cl.t, cl.h_qk, cl.h_v, scan_blocks);
+    } else {
+        hipLaunchKernelGGL((chunk_scan_wide_kernel<D, C, TIn>), dim3((unsigned)scan_blocks), dim3(256), 0,
+                           cl.stream, q, k, v, ws, L, cl.state_in, cl.out, cl.state_out, cl.t,
+                           cl.h_qk, cl.h_v, scan_blocks);
+    }
     return hipGetLastError();
 }
 
