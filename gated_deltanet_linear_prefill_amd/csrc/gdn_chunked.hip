@@ -140,7 +140,7 @@ struct Geo {
     static constexpr int NOW = 4 - NCH;         // output waves
     static constexpr int RTO = (RT + NOW - 1) / NOW;  // row tiles per output wave
     static constexpr int NHF = RT * KTC;        // A fragments of the full C x C matrix H
-    static constexpr bool WITH_H = C <= 64;     // H is prepared for the scan kernel that uses it
+    static constexpr bool WITH_H = C <= 32;     // H is prepared for the scan kernel that uses it
     static constexpr size_t TRI_BYTES = (size_t)NTRI * 2 * 1024;      // per (chunk, V head)
     static constexpr size_t H_BYTES = WITH_H ? (size_t)NHF * 2 * 1024 : 0;  // per (chunk, V head)
     static constexpr size_t SC_BYTES = (size_t)3 * CP * 4 + 16;       // per (chunk, V head)
@@ -164,7 +164,7 @@ ChunkWs chunk_ws(int64_t n, int64_t t, int32_t h_qk, int32_t h_v, int32_t d, int
     (void)f32in;
     const int cp = chunk < 32 ? 32 : chunk;
     const size_t tri_bytes = (size_t)tri_off(chunk / 16) * 2 * 1024;
-    const size_t h_bytes = chunk <= 64 ? (size_t)(chunk / 16) * (cp / 32) * 2 * 1024 : 0;
+    const size_t h_bytes = chunk <= 32 ? (size_t)(chunk / 16) * (cp / 32) * 2 * 1024 : 0;
     const size_t sc_bytes = (size_t)3 * cp * 4 + 16;
     ChunkWs w;
     w.nch = (t + chunk - 1) / chunk;
@@ -749,7 +749,8 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 }
 
 // =============================================================================== scan
-// Scan workgroup: one "chain" wave, NSW "state" waves and four "helper" waves.
+// Scan workgroup (chunks of up to 32 tokens): one "chain" wave, NSW "state" waves and four
+// "helper" waves.
 //
 // The recursion the chain wave runs involves only X, the residuals V - diag(a) K M of a
 // chunk:
@@ -760,61 +761,63 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 // split over d_k, form it (with the reduction over d_k) a chunk before it is used: no
 // exchange over d_k sits on the chain's path. The chain wave also forms U = T' X and
 // W = diag(s) U; the state waves apply M_{c+1} = Gamma_c M_c + K_c^T W_c one chunk later,
-// and the helpers form the outputs O_c = diag(o) Q_c M_c + Ptil_c U_c. The helpers also
-// move every input into LDS ahead of its use: global loads are the scarce resource here
-// (a load whose lanes cover 16 rows of 64 bytes, the MFMA fragment shape of a bf16 row,
-// runs at about a third of the rate of one covering whole 128-byte lines), so K and Q are
-// loaded as whole token rows and rewritten in LDS, where both K fragments and transposed
-// K^T fragments are read from the same copy.
+// and the first helpers form the outputs O_c = diag(o) Q_c M_c + Ptil_c U_c.
+//
+// The other helpers move every input into LDS two windows ahead of its use, with loads
+// that write LDS directly (each lane's 16 bytes land at the destination base plus 16 bytes
+// per lane): global loads are the scarce resource here, and this way the data never passes
+// through registers. K and Q arrive as whole token rows (a load whose lanes cover 16 rows of
+// 64 bytes, the MFMA fragment shape of a bf16 row, runs at about a third of the rate of one
+// covering whole 128-byte lines), with their 16-byte granules swizzled so that fragment and
+// transposing reads of the same copy are free of bank conflicts. fp32 rows (which are split
+// into bf16 hi/lo planes) and d = 16 rows (shorter than a staged row) go through registers.
 //
 // Time advances in windows c = -2, -1, ..., nch - 1 (and one idle window more when that
 // count is odd, so that the two-window loops below have no conditional half), each opened
 // by a workgroup barrier:
-//   chain   window c: X_{c+1}, U_{c+1}, W_{c+1}        (c >= -1)
-//   state   window c: M_{c+1} (c >= 0); Gamma_{c+1} P_{c+2} and K_{c+2}^T fragments
-//   helpers window c: outputs of chunk c (c >= 0); stage K_{c+3}, H_{c+1}, and T', the V
-//                     block and the scalars a, s, o, Gamma_C of chunk c + 2
-// Each exchange buffer is double-buffered by chunk parity (the scalars by chunk mod 4).
+//   chain    window c: X_{c+1}, U_{c+1}, W_{c+1}        (c >= -1)
+//   state    window c: M_{c+1} (c >= 0); Gamma_{c+1} P_{c+2} and K_{c+2}^T fragments
+//   output   window c: outputs of chunk c                 (c >= 0)
+//   staging  window c: issue K_{c+4}, T', V and scalars of chunk c + 3, H, Q and Ptil of
+//                      chunk c + 2; wait for those issued in window c - 1
+// Staged inputs sit in rings of three chunks (the scalars in four); exchanges between the
+// compute waves are double-buffered by chunk parity.
 template <int D, int C, typename TIn>
 struct ScanGeo {
+    static_assert(C <= 32, "longer chunks use the wide-chunk kernel");
     using G = Geo<D, C, std::is_same<TIn, float>::value>;
     static constexpr int ES = sizeof(TIn);
     static constexpr int NSW = G::KTD >= 2 ? 2 : 1;       // state waves
     static constexpr int KPS = G::KTD / NSW;               // d_k tiles per state wave
     static constexpr int NHW = 4;                          // helper waves
     static constexpr int THREADS = 64 * (1 + NSW + NHW);
-    static constexpr int RTH = (G::RT + NHW - 1) / NHW;    // output row tiles per helper
+    static constexpr int NOH = G::RT;                      // output helpers, one row tile each
+    static constexpr int NSH = NHW - NOH;                  // staging helpers
+    static constexpr int NR = 3;                           // ring depth of the staged inputs
     // Staged rows: one bf16 piece of DP features in 16-byte granules; granule j of row r sits
     // at position j ^ swz(r).
     static constexpr int ROWB = G::DP * 2;                 // bytes per staged row
     static constexpr int RPB = 256 / ROWB;                 // staged rows per 64 LDS banks
+    static constexpr int NG = ROWB / 16;                   // granules per staged row
     // Raw q/k rows: RB bytes, loaded as LPR lanes of 16 bytes, RPI rows per instruction.
     static constexpr int RB = D * ES;
     static constexpr int LPR = RB / 16;
     static constexpr int RPI = 64 / LPR;
-    static constexpr int NKI = (C + RPI - 1) / RPI;        // K row loads per chunk
-    static constexpr int NKH = (NKI + NHW - 1) / NHW;      // ... per helper
-    static constexpr int QR = RPI > 16 ? RPI : 16;         // staged Q rows per row tile
-    static constexpr int NQI = QR / RPI;                   // Q row loads per row tile
-    // The V block (16 channels of a token): LPT lanes per token, TPI tokens per load.
-    static constexpr int LPT = ES;
-    static constexpr int TPI = 64 / LPT;
+    static constexpr int NKI = (C + RPI - 1) / RPI;        // row loads per chunk
+    // K and Q rows load straight into LDS when a load's 64 lanes fill 1 KB of staged rows
+    // (bf16 and d >= 32); otherwise K goes through registers and the output helpers load Q
+    // fragments themselves.
+    static constexpr bool DQK = ES == 2 && D >= 32;
+    // The V block (16 channels of a token): bf16 rows straight into LDS (read back with
+    // transposing reads); fp32 through registers, transposed to channel-major.
+    static constexpr bool DV = ES == 2;
+    static constexpr int LPT = ES;                         // lanes per token of a V load
+    static constexpr int TPI = 64 / LPT;                   // tokens per V load
     static constexpr int NVI = (C + TPI - 1) / TPI;
-    static constexpr int VS = G::CP + 4;                   // LDS row stride of the V block
+    static constexpr int VS = G::CP + 4;                   // LDS row stride of a transposed V block
     static constexpr size_t K_BYTES = (size_t)G::NS * G::CP * ROWB;
-    static constexpr size_t QH_BYTES = (size_t)RTH * QR * ROWB;  // one helper's Q rows
-    static constexpr size_t BASE = 2 * K_BYTES + (size_t)2 * 16 * VS * 4 + (size_t)4 * 256 * 4 +
-                                   (size_t)2 * NSW * G::RT * 1024 + (size_t)2 * G::KTC * 2048 +
-                                   (size_t)2 * G::RT * 1024 + (size_t)2 * G::KTD * 2048;
-    static constexpr size_t LIM = 160 * 1024;
-    // H, T' and (bf16) Q rows are staged in LDS in that order of priority while they fit;
-    // otherwise H and T' are read from the workspace by the chain wave and Q fragments are
-    // loaded directly by the helpers.
-    static constexpr bool HLDS = BASE + 2 * G::H_BYTES <= LIM;
-    static constexpr size_t AFTER_H = BASE + (HLDS ? 2 * G::H_BYTES : 0);
-    static constexpr bool TLDS = AFTER_H + 2 * G::TRI_BYTES <= LIM;
-    static constexpr size_t AFTER_T = AFTER_H + (TLDS ? 2 * G::TRI_BYTES : 0);
-    static constexpr bool QST = ES == 2 && AFTER_T + NHW * QH_BYTES <= LIM;
+    static constexpr size_t Q_BYTES = DQK ? (size_t)G::CP * ROWB : 16;
+    static constexpr size_t V_BYTES = DV ? (size_t)G::CP * 32 : (size_t)16 * VS * 4;
 };
 
 // Granule swizzle of the staged rows. A fragment read (16 consecutive rows, one granule)
@@ -838,6 +841,29 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* p)
     return __builtin_bit_cast(bf16x4, r);
 }
 
+// A 16-byte-per-lane buffer load that writes LDS directly: lane l's bytes land at
+// lds + 16 l (established with an in-bounds probe of the instruction).
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, int off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+
+// A workgroup barrier that waits only for this wave's LDS operations. (__syncthreads()
+// would also wait for every load that writes LDS directly; the staging helpers wait for
+// those explicitly, two windows after issue.)
+__device__ __forceinline__ void barrier_lds_only()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Wait until at most n vector memory operations of this wave are in flight.
+template <int N>
+__device__ __forceinline__ void wait_vm()
+{
+    static_assert(N >= 0 && N < 64, "vmcnt range");
+    __builtin_amdgcn_s_waitcnt((N & 15) | (7 << 4) | (15 << 8) | ((N >> 4) << 14));
+}
+
 template <int D, int C, typename TIn>
 __global__ void __launch_bounds__((ScanGeo<D, C, TIn>::THREADS))
 chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
@@ -851,28 +877,28 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     using Raw = typename RawFrag<TIn>::type;
     constexpr int CP = G::CP, RT = G::RT, KTC = G::KTC, KTD = G::KTD, NS = G::NS;
     constexpr int NTRI = G::NTRI, NHF = G::NHF;
-    constexpr int NSW = SG::NSW, KPS = SG::KPS, NHW = SG::NHW;
-    constexpr int ROWB = SG::ROWB, RPB = SG::RPB, LPR = SG::LPR, RPI = SG::RPI;
-    constexpr int NKI = SG::NKI, NKH = SG::NKH, QR = SG::QR, NQI = SG::NQI;
+    constexpr int NSW = SG::NSW, KPS = SG::KPS, NHW = SG::NHW, NOH = SG::NOH, NSH = SG::NSH;
+    constexpr int NR = SG::NR, ROWB = SG::ROWB, RPB = SG::RPB, NG = SG::NG;
+    constexpr int LPR = SG::LPR, RPI = SG::RPI, NKI = SG::NKI;
     constexpr int LPT = SG::LPT, TPI = SG::TPI, NVI = SG::NVI;
     constexpr int ES = SG::ES;
-    constexpr bool HLDS = SG::HLDS, TLDS = SG::TLDS, QST = SG::QST;
+    constexpr bool DQK = SG::DQK, DV = SG::DV;
 
-    // LDS (parity = chunk index mod 2):
-    //   s_k   K rows of a chunk (NS bf16 planes, swizzled granules), by parity
-    //   s_q   each helper's Q rows (bf16 inputs)
-    //   s_h   H of a chunk (A fragments hi, lo), by parity
-    //   s_tf  T' of a chunk, s_vt its V block (channel-major fp32), by parity
-    //   s_sc  the scalars of a chunk (a, s, o, Gamma_C as laid out in the workspace), by
-    //         chunk mod 4
+    // LDS (ring slots by chunk mod NR, the scalars by chunk mod 4, exchanges by parity):
+    //   s_k   K rows of a chunk (NS bf16 planes, swizzled granules)
+    //   s_q   Q rows of a chunk (bf16, swizzled granules)
+    //   s_pt  Ptil^T, s_h H, s_tf T' of a chunk (fragments, hi and lo pieces)
+    //   s_v   the V block of a chunk: bf16 rows, or channel-major fp32
+    //   s_sc  the scalars of a chunk (a, s, o, Gamma_C as laid out in the workspace)
     //   s_p   each state wave's part of Gamma_c P_{c+1}, by parity of c + 1
     //   s_wf  W as B fragments (hi, lo), s_uf U (fp32, accumulator layout), by parity
     //   s_mf  the state entering a chunk as B fragments (hi, lo), by parity
-    __shared__ __align__(16) char s_k[2][SG::K_BYTES];
-    __shared__ __align__(16) char s_q[QST ? NHW * SG::QH_BYTES : 16];
-    __shared__ __align__(16) bf16x8 s_h[HLDS ? 2 : 1][HLDS ? 2 * NHF : 1][64];
-    __shared__ __align__(16) bf16x8 s_tf[TLDS ? 2 : 1][TLDS ? 2 * NTRI : 1][64];
-    __shared__ __align__(16) float s_vt[2][16][SG::VS];
+    __shared__ __align__(16) char s_k[NR][SG::K_BYTES];
+    __shared__ __align__(16) char s_q[DQK ? NR : 1][SG::Q_BYTES];
+    __shared__ __align__(16) bf16x8 s_pt[NR][2 * NTRI][64];
+    __shared__ __align__(16) bf16x8 s_h[NR][2 * NHF][64];
+    __shared__ __align__(16) bf16x8 s_tf[NR][2 * NTRI][64];
+    __shared__ __align__(16) char s_v[NR][SG::V_BYTES];
     __shared__ __align__(16) float s_sc[4][256];
     __shared__ __align__(16) floatx4 s_p[2][NSW][RT][64];
     __shared__ __align__(16) bf16x8 s_wf[2][KTC][2][64];
@@ -898,13 +924,14 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     const int64_t row_v = (int64_t)h_v * D * ES;
     const int64_t row_o = (int64_t)h_v * D * 4;
     auto par = [](int64_t c) { return (int)(c & 1); };
+    auto ring = [](int64_t c) { return (int)(c % NR); };  // c >= 0
     auto clampc = [&](int64_t c) { return c < 0 ? 0 : (c < nch ? c : nch - 1); };
     auto tok0_of = [&](int64_t c) { return seq * T + c * C; };
     auto rows_of = [&](int64_t c) { return (T - c * C) < C ? (T - c * C) : (int64_t)C; };
     auto vh_of = [&](int64_t c) { return (size_t)((seq * nch + c) * h_v + h); };
     auto sc_rsrc = [&](int64_t c) { return make_rsrc(ws + L.sc + vh_of(c) * G::SC_BYTES, G::SC_BYTES); };
-    auto ws_rsrc = [&](size_t region, size_t bytes, int64_t c, bool on) {
-        return make_rsrc(ws + region + vh_of(c) * bytes, on ? (int64_t)bytes : 0);
+    auto ws_rsrc = [&](size_t region, size_t bytes, int64_t c) {
+        return make_rsrc(ws + region + vh_of(c) * bytes, (int64_t)bytes);
     };
     // q or k rows of chunk c (rows past the sequence read zero)
     auto qk_rsrc = [&](const TIn* base, int64_t c) {
@@ -919,13 +946,23 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     // A full wait: nothing left in flight, so the compiler's wait bookkeeping starts clean.
     auto settle = [&]() { __builtin_amdgcn_s_waitcnt(0); };
     // Four consecutive staged values of accumulator rows 4 lg .. 4 lg + 3 of row tile rt.
-    auto vt4 = [&](int p, int rt) { return *reinterpret_cast<const floatx4*>(&s_vt[p][lr][16 * rt + 4 * lg]); };
     auto sc4 = [&](int64_t c, int off) { return *reinterpret_cast<const floatx4*>(&s_sc[c & 3][off + 4 * lg]); };
     auto gc_of = [&](int64_t c) { return s_sc[c & 3][3 * CP]; };
+    // V of tokens 16 rt + 4 lg + 0..3, channel lr (bf16 rows: one transposing read in which
+    // lane 4 p + q of each 16-lane group addresses token 16 rt + 4 lg + p, channels 4 q ..)
+    auto vt4 = [&](int64_t c, int rt) {
+        const char* base = s_v[ring(c)];
+        if constexpr (DV) {
+            const bf16x4 x = lds_read_tr16(base + (16 * rt + 4 * lg + (lr >> 2)) * 32 + 8 * (lr & 3));
+            return floatx4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+        } else {
+            return *reinterpret_cast<const floatx4*>(base + (lr * SG::VS + 16 * rt + 4 * lg) * 4);
+        }
+    };
 
     if (w == 0) {
         // ======================================================= chain wave
-        __syncthreads();  // the helpers have cleared the staged-row buffers
+        __syncthreads();  // the staged-row buffers are cleared and the first inputs staged
         bf16x8 xf[KTC][2];  // X of the latest chunk as B fragments (hi, lo)
 #pragma unroll
         for (int kt = 0; kt < KTC; ++kt) xf[kt][0] = xf[kt][1] = bf16x8{};
@@ -933,7 +970,7 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
         for (int64_t c = -2; c < cend; ++c) {
             __syncthreads();
             if (c < -1 || c + 1 >= nch) continue;  // wave-uniform
-            const int pn = par(c + 1), pc = par(c);
+            const int pn = par(c + 1);
             // Z = Gamma_c P_{c+1} (the state waves' parts summed in wave order) + H_c X_c
             floatx4 z[RT];
 #pragma unroll
@@ -943,30 +980,21 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                 for (int sw = 1; sw < NSW; ++sw) z[rt] += s_p[pn][sw][rt][l];
             }
             if (c >= 0) {
-                const auto r_h = ws_rsrc(L.hh, G::H_BYTES, c, !HLDS);
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
                     for (int kt = 0; kt < KTC; ++kt) {
                         const int fi = rt * KTC + kt;
-                        bf16x8 hf[2];
-#pragma unroll
-                        for (int p = 0; p < 2; ++p) {
-                            if constexpr (HLDS)
-                                hf[p] = s_h[pc][2 * fi + p][l];
-                            else
-                                hf[p] = buf_bf16x8(r_h, (2 * fi + p) * 1024 + l * 16);
-                        }
+                        const bf16x8 hf[2] = {s_h[ring(c)][2 * fi][l], s_h[ring(c)][2 * fi + 1][l]};
                         z[rt] = mfma_split<2, 2>(hf, xf[kt], z[rt]);
                     }
             }
             // X_{c+1} = V - diag(a) Z
             floatx4 xv[RT];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) xv[rt] = vt4(pn, rt) - sc4(c + 1, 16 * rt) * z[rt];
+            for (int rt = 0; rt < RT; ++rt) xv[rt] = vt4(c + 1, rt) - sc4(c + 1, 16 * rt) * z[rt];
             rows_to_frags<RT, KTC>(xv, xf);
             // U = T' X (lower triangular: row tile rt uses token k tiles 0 .. rt / 2)
-            const auto r_t = ws_rsrc(L.tt, G::TRI_BYTES, c + 1, !TLDS);
             floatx4 u[RT];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
@@ -974,14 +1002,7 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
 #pragma unroll
                 for (int kt = 0; 2 * kt <= rt; ++kt) {
                     const int pi = 2 * (tri_off(rt) + kt);
-                    bf16x8 tf[2];
-#pragma unroll
-                    for (int p = 0; p < 2; ++p) {
-                        if constexpr (TLDS)
-                            tf[p] = s_tf[pn][pi + p][l];
-                        else
-                            tf[p] = buf_bf16x8(r_t, (pi + p) * 1024 + l * 16);
-                    }
+                    const bf16x8 tf[2] = {s_tf[ring(c + 1)][pi][l], s_tf[ring(c + 1)][pi + 1][l]};
                     acc = mfma_split<2, 2>(tf, xf[kt], acc);
                 }
                 u[rt] = acc;
@@ -1026,16 +1047,15 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                 for (int pp = 0; pp < 2; ++pp) s_mf[p][KPS * sw + kk][pp][l] = mf[kk][pp];
             }
         };
-        split_publish(0);  // the state entering chunk 0, for the helpers
-        __syncthreads();   // the helpers have cleared the staged-row buffers
+        split_publish(0);  // the state entering chunk 0, for the output helpers
+        __syncthreads();   // the staged-row buffers are cleared and the first inputs staged
 
         // K^T A fragments of a chunk for this wave's state tiles, read two windows before the
-        // state update that uses them (so the staged K rows need only two buffers). Fragment
-        // (i, kt): two transposing reads (token slots 0..3, 4..7); lane lr of group lg
-        // addresses token row 32 kt + 16 h + 4 lg + lr / 4 and features
-        // 32 (KPS sw + i / 2) + 8 (lr % 4) + 4 (i % 2) + 0..3.
+        // state update that uses them. Fragment (i, kt): two transposing reads (token slots
+        // 0..3, 4..7); lane lr of group lg addresses token row 32 kt + 16 h + 4 lg + lr / 4 and
+        // features 32 (KPS sw + i / 2) + 8 (lr % 4) + 4 (i % 2) + 0..3.
         bf16x8 ktA[2 * KPS][KTC][NS], ktB[2 * KPS][KTC][NS];
-        auto read_kt = [&](bf16x8 (*kts)[KTC][NS], int p) {
+        auto read_kt = [&](bf16x8 (*kts)[KTC][NS], int slot) {
 #pragma unroll
             for (int i = 0; i < 2 * KPS; ++i)
 #pragma unroll
@@ -1044,7 +1064,7 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                     for (int part = 0; part < NS; ++part) {
                         const int r = 32 * kt + 4 * lg + (lr >> 2);
                         const int j = 4 * (KPS * sw + (i >> 1)) + (lr & 3);
-                        const char* base = s_k[p] + part * CP * ROWB + 8 * (i & 1);
+                        const char* base = s_k[slot] + part * CP * ROWB + 8 * (i & 1);
                         const bf16x4 a = lds_read_tr16(base + srow(r, j));
                         const bf16x4 b = lds_read_tr16(base + srow(r + 16, j));
                         kts[i][kt][part] = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
@@ -1072,7 +1092,7 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
             }
             if (c + 2 < nch) {
                 // Gamma_{c+1} K_{c+2} M_{c+1} over this wave's features (unscaled for chunk 0)
-                const int p2 = par(c + 2);
+                const int slot = ring(c + 2), p2 = par(c + 2);
                 const float scale = c >= -1 ? gc_of(c + 1) : 1.f;
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) {
@@ -1083,12 +1103,12 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
 #pragma unroll
                         for (int part = 0; part < NS; ++part)
                             ka[part] = *reinterpret_cast<const bf16x8*>(
-                                s_k[p2] + part * CP * ROWB + srow(16 * rt + lr, 4 * (KPS * sw + kk) + lg));
+                                s_k[slot] + part * CP * ROWB + srow(16 * rt + lr, 4 * (KPS * sw + kk) + lg));
                         acc = mfma_split<NS, 2>(ka, mf[kk], acc);
                     }
                     s_p[p2][sw][rt][l] = scale * acc;
                 }
-                read_kt(kts, p2);  // K^T of chunk c + 2 replaces K^T of chunk c
+                read_kt(kts, slot);  // K^T of chunk c + 2 replaces K^T of chunk c
             }
         };
         // Chunk parity alternates between windows, and so do the two K^T register sets.
@@ -1110,175 +1130,31 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
         }
     } else {
         // ======================================================= helper wave hw
-        // Row tiles hw, hw + 4, ... of the outputs, and shares of the staging. Each helper
-        // runs code specialised for its index, so its sequence of vector memory operations has
-        // no branches: the compiler then counts exactly which loads are still in flight and
-        // waits only for the operand set it uses, not for the one loaded after it.
+        // Helpers 0 .. NOH - 1 form the outputs of row tile hw; the others stage the inputs.
+        // Each helper runs code specialised for its index, so its sequence of vector memory
+        // operations has no branches and the waits below count exactly.
         const int hw = w - 1 - NSW;
 
         // Clear the staged rows once: rows past a short chunk and features past D are never
-        // written afterwards and must read as zero. (The sizes are multiples of 1 KB, so
-        // every lane makes the same number of trips.)
-        for (int o = 1024 * hw; o < (int)(2 * SG::K_BYTES); o += 1024 * NHW)
+        // written afterwards and must read as zero. (The size is a multiple of 1 KB, so every
+        // lane makes the same number of trips.)
+        for (int o = 1024 * hw; o < (int)(NR * SG::K_BYTES); o += 1024 * NHW)
             *reinterpret_cast<u32x4*>(&s_k[0][0] + o + 16 * l) = u32x4{0u, 0u, 0u, 0u};
-        if constexpr (QST) {
-            for (int o = 0; o < (int)SG::QH_BYTES; o += 1024)
-                *reinterpret_cast<u32x4*>(s_q + hw * SG::QH_BYTES + o + 16 * l) = u32x4{0u, 0u, 0u, 0u};
-        }
         __syncthreads();
 
-        auto helper = [&](auto hw_const) {
-            constexpr int HW = decltype(hw_const)::value;
-            // Helpers 0 .. NOH - 1 form the outputs. The staging (K rows, H and T' pieces) is
-            // spread over the helpers without output rows where there are such (C <= 32),
-            // otherwise over all four; the V block and the scalars come from the last two.
-            constexpr int NOH = RT < NHW ? RT : NHW;
-            constexpr int SH0 = NOH < NHW ? NOH : 0, NSH = NHW - SH0;
-            constexpr int HS = HW - SH0;  // index among the staging helpers (< 0: none)
-            constexpr bool VST = HW == NHW - 2, SST = HW == NHW - 1;
-            constexpr int NRT = RT > HW ? (RT - HW + NHW - 1) / NHW : 0;  // this helper's row tiles
-            constexpr auto share = [](int n, int j, int of) { return j >= 0 && n > j ? (n - j + of - 1) / of : 0; };
-            constexpr int NKM = share(NKI, HS, NSH);       // its K row loads
-            constexpr int NHM = share(2 * NHF, HS, NSH);   // its H pieces
-            constexpr int NTM = share(2 * NTRI, HS, NSH);  // its T' pieces
-            char* const s_qh = s_q + (QST ? HW * SG::QH_BYTES : 0);
-
-            // ---- the operand set of window c; two sets alternate, each loaded two windows
-            //      ahead
-            struct HSet {
-                u32x4 kr[NKM > 0 ? NKM : 1];                    // K rows of chunk c + 3
-                bf16x8 hs[NHM > 0 ? NHM : 1];                   // H pieces of chunk c + 1
-                bf16x8 tst[NTM > 0 ? NTM : 1];                  // T' pieces of chunk c + 2
-                u32x4 vr[VST ? NVI : 1];                        // V block of chunk c + 2
-                u32x4 scv;                                      // scalars of chunk c + 2
-                u32x4 qrw[QST && NRT > 0 ? NRT : 1][QST ? NQI : 1];  // Q rows of chunk c + 1,
-                Raw qf[!QST && NRT > 0 ? NRT : 1][QST ? 1 : KTD];    //   or Q fragments of c
-                bf16x8 pf[NRT > 0 ? NRT : 1][KTC][2];           // Ptil^T fragments of chunk c
-            };
-            auto ld_k = [&](u32x4* kr, int64_t c) {
-                const auto r = qk_rsrc(k, clampc(c));
+        auto output_helper = [&](auto hw_const) {
+            constexpr int RTO = decltype(hw_const)::value;  // the row tile of this helper
+            // Q fragments are loaded here when they are not staged (two sets alternate,
+            // each loaded two windows ahead)
+            struct QSet { Raw qf[DQK ? 1 : KTD]; };
+            auto load_q = [&](QSet& x, int64_t c) {
+                if constexpr (!DQK) {
+                    const auto r = qk_rsrc(q, clampc(c));
 #pragma unroll
-                for (int m = 0; m < NKM; ++m) {
-                    const int row = RPI * (HS + NSH * m) + l / LPR;
-                    kr[m] = __builtin_amdgcn_raw_buffer_load_b128(
-                        r, (int)((uint32_t)(row * row_qk) + (uint32_t)(16 * (l % LPR)) + pad_if(row < C)), 0, 0);
-                }
-            };
-            // K rows into s_k[p] (bf16 pieces; fp32 rows are split into hi and lo planes)
-            auto st_k = [&](const u32x4* kr, int p) {
-#pragma unroll
-                for (int m = 0; m < NKM; ++m) {
-                    const int row = RPI * (HS + NSH * m) + l / LPR, g = l % LPR;
-                    if constexpr (ES == 2) {
-                        *reinterpret_cast<u32x4*>(s_k[p] + srow(row, g)) = kr[m];
-                    } else {
-                        const floatx4 x = __builtin_bit_cast(floatx4, kr[m]);
-                        uint32_t hi[2], lo[2];
-                        split2(x[0], x[1], &hi[0], &lo[0]);
-                        split2(x[2], x[3], &hi[1], &lo[1]);
-                        const int o = srow(row, g >> 1) + 8 * (g & 1);
-                        *reinterpret_cast<uint2*>(s_k[p] + o) = uint2{hi[0], hi[1]};
-                        *reinterpret_cast<uint2*>(s_k[p] + CP * ROWB + o) = uint2{lo[0], lo[1]};
-                    }
-                }
-            };
-            auto load_set = [&](HSet& x, int64_t c) {
-                ld_k(x.kr, c + 3);
-                if constexpr (HLDS) {
-                    const auto r = ws_rsrc(L.hh, G::H_BYTES, clampc(c + 1), true);
-#pragma unroll
-                    for (int m = 0; m < NHM; ++m) x.hs[m] = buf_bf16x8(r, (HS + NSH * m) * 1024 + l * 16);
-                }
-                if constexpr (TLDS) {
-                    const auto r = ws_rsrc(L.tt, G::TRI_BYTES, clampc(c + 2), true);
-#pragma unroll
-                    for (int m = 0; m < NTM; ++m) x.tst[m] = buf_bf16x8(r, (HS + NSH * m) * 1024 + l * 16);
-                }
-                const int64_t c2 = clampc(c + 2);
-                if constexpr (VST) {
-                    const auto r_v = make_rsrc(v + (tok0_of(c2) * h_v + h) * (int64_t)D + cb * 16,
-                                               (rows_of(c2) - 1) * row_v + 16 * ES);
-#pragma unroll
-                    for (int m = 0; m < NVI; ++m) {
-                        const int t = TPI * m + l / LPT;
-                        x.vr[m] = __builtin_amdgcn_raw_buffer_load_b128(
-                            r_v, (int)((uint32_t)(t * row_v) + (uint32_t)(16 * (l % LPT)) + pad_if(t < C)), 0, 0);
-                    }
-                }
-                if constexpr (SST)
-                    x.scv = __builtin_amdgcn_raw_buffer_load_b128(sc_rsrc(c2), 16 * l, 0, 0);
-#pragma unroll
-                for (int i = 0; i < NRT; ++i) {
-                    const int rt = HW + NHW * i;
-                    if constexpr (QST) {
-                        const auto r = qk_rsrc(q, clampc(c + 1));
-#pragma unroll
-                        for (int m = 0; m < NQI; ++m) {
-                            const int rl = RPI * m + l / LPR;
-                            x.qrw[i][m] = __builtin_amdgcn_raw_buffer_load_b128(
-                                r, (int)((uint32_t)((16 * rt + rl) * row_qk) + (uint32_t)(16 * (l % LPR)) + pad_if(rl < 16)),
-                                0, 0);
-                        }
-                    } else {
-                        const auto r = qk_rsrc(q, clampc(c));
-#pragma unroll
-                        for (int kt = 0; kt < KTD; ++kt) {
-                            const int f = 32 * kt + 8 * lg;
-                            x.qf[i][kt] = buf_raw_frag<TIn>(
-                                r, (int)((uint32_t)((16 * rt + lr) * row_qk) + (uint32_t)(f * ES) + pad_if(f < D)));
-                        }
-                    }
-                    const auto r = ws_rsrc(L.pt, G::TRI_BYTES, clampc(c), true);
-#pragma unroll
-                    for (int kt = 0; 2 * kt <= rt; ++kt) {
-                        const int o = (tri_off(rt) + kt) * 2048 + l * 16;
-                        x.pf[i][kt][0] = buf_bf16x8(r, o);
-                        x.pf[i][kt][1] = buf_bf16x8(r, o + 1024);
-                    }
-                }
-            };
-            // The staging writes of window c.
-            auto store_set = [&](const HSet& x, int64_t c) {
-                if (c + 3 < nch) st_k(x.kr, par(c + 3));
-                if constexpr (HLDS) {
-                    if (c + 1 >= 0 && c + 1 < nch) {
-#pragma unroll
-                        for (int m = 0; m < NHM; ++m) s_h[par(c + 1)][HS + NSH * m][l] = x.hs[m];
-                    }
-                }
-                if (c + 2 < nch) {
-                    const int p = par(c + 2);
-                    if constexpr (TLDS) {
-#pragma unroll
-                        for (int m = 0; m < NTM; ++m) s_tf[p][HS + NSH * m][l] = x.tst[m];
-                    }
-                    if constexpr (VST) {
-#pragma unroll
-                        for (int m = 0; m < NVI; ++m) {
-                            const int t = TPI * m + l / LPT;  // < CP
-                            if constexpr (ES == 2) {
-                                const bf16x8 y = __builtin_bit_cast(bf16x8, x.vr[m]);
-#pragma unroll
-                                for (int e = 0; e < 8; ++e) s_vt[p][8 * (l % LPT) + e][t] = (float)y[e];
-                            } else {
-                                const floatx4 y = __builtin_bit_cast(floatx4, x.vr[m]);
-#pragma unroll
-                                for (int e = 0; e < 4; ++e) s_vt[p][4 * (l % LPT) + e][t] = y[e];
-                            }
-                        }
-                    }
-                    // the scalar block (lanes past it carry whatever lies beyond; never read)
-                    if constexpr (SST) *reinterpret_cast<u32x4*>(&s_sc[(c + 2) & 3][4 * l]) = x.scv;
-                }
-                // Q rows of chunk c + 1, after this window's reads of chunk c's
-                if constexpr (QST) {
-                    if (c + 1 >= 0 && c + 1 < nch) {
-#pragma unroll
-                        for (int i = 0; i < NRT; ++i)
-#pragma unroll
-                            for (int m = 0; m < NQI; ++m)
-                                *reinterpret_cast<u32x4*>(s_qh + i * QR * ROWB + srow(RPI * m + l / LPR, l % LPR)) =
-                                    x.qrw[i][m];
+                    for (int kt = 0; kt < KTD; ++kt) {
+                        const int f = 32 * kt + 8 * lg;
+                        x.qf[kt] = buf_raw_frag<TIn>(
+                            r, (int)((uint32_t)((16 * RTO + lr) * row_qk) + (uint32_t)(f * ES) + pad_if(f < D)));
                     }
                 }
             };
@@ -1287,62 +1163,218 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
             // operands, the Q row fragments and Ptil^T as B operands, and each lane ends up with
             // four consecutive channels of one token (one 16-byte store). Windows outside the
             // chunks store out of range.
-            auto do_output = [&](const HSet& x, int64_t c) {
-                if constexpr (NRT > 0) {
-                    const bool live = c >= 0 && c < nch;  // wave-uniform
-                    c = clampc(c);
-                    const int pc = par(c);
-                    bf16x8 mfr[KTD][2];
+            auto do_output = [&](const QSet& x, int64_t c) {
+                const bool live = c >= 0 && c < nch;  // wave-uniform
+                c = clampc(c);
+                const int pc = par(c), slot = ring(c);
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-                    for (int kt = 0; kt < KTD; ++kt)
+                for (int kt = 0; kt < KTD; ++kt) {
+                    const bf16x8 mfr[2] = {s_mf[pc][kt][0][l], s_mf[pc][kt][1][l]};
+                    bf16x8 qa[NS];
+                    if constexpr (DQK)
+                        qa[0] = *reinterpret_cast<const bf16x8*>(s_q[slot] + srow(16 * RTO + lr, 4 * kt + lg));
+                    else
+                        to_pieces(x.qf[kt], qa);
+                    acc = mfma_split<2, NS>(mfr, qa, acc);
+                }
+                acc *= s_sc[c & 3][2 * CP + 16 * RTO + lr];  // o of token 16 RTO + lr
+                floatx4 urow[RT];
 #pragma unroll
-                        for (int p = 0; p < 2; ++p) mfr[kt][p] = s_mf[pc][kt][p][l];
-                    floatx4 urow[RT];
+                for (int rt = 0; rt < RT; ++rt) urow[rt] = s_uf[pc][rt][l];
+                bf16x8 ufr[KTC][2];
+                rows_to_frags<RT, KTC>(urow, ufr);
 #pragma unroll
-                    for (int rt = 0; rt < RT; ++rt) urow[rt] = s_uf[pc][rt][l];
-                    bf16x8 ufr[KTC][2];
-                    rows_to_frags<RT, KTC>(urow, ufr);
-                    const auto r_o = make_rsrc(out + (tok0_of(c) * h_v + h) * (int64_t)D + cb * 16,
-                                               (rows_of(c) - 1) * row_o + 64);
+                for (int kt = 0; 2 * kt <= RTO; ++kt) {
+                    const int pi = 2 * (tri_off(RTO) + kt);
+                    const bf16x8 pf[2] = {s_pt[slot][pi][l], s_pt[slot][pi + 1][l]};
+                    acc = mfma_split<2, 2>(ufr[kt], pf, acc);
+                }
+                const auto r_o = make_rsrc(out + (tok0_of(c) * h_v + h) * (int64_t)D + cb * 16,
+                                           (rows_of(c) - 1) * row_o + 64);
+                __builtin_amdgcn_raw_buffer_store_b128(
+                    __builtin_bit_cast(u32x4, acc), r_o,
+                    (int)((uint32_t)((16 * RTO + lr) * row_o) + (uint32_t)(lg * 16) + pad_if(live)), 0, 0);
+            };
+            QSet A, B;
+            load_q(B, -2);
+            load_q(A, -1);
+            auto window = [&](QSet& x, int64_t c) {
+                __syncthreads();
+                do_output(x, c);
+                __builtin_amdgcn_sched_barrier(0);
+                load_q(x, c + 2);
+            };
+#pragma unroll 1
+            for (int64_t c = -2; c < cend; c += 2) {
+                window(B, c);      // window c uses the set of chunk c (loaded two windows ago)
+                window(A, c + 1);
+            }
+            settle();
+        };
+
+        auto staging_helper = [&](auto hs_const) {
+            constexpr int HS = decltype(hs_const)::value;  // index among the staging helpers
+            // This helper's shares: loads m of it cover items HS + NSH m.
+            constexpr auto share = [](int n) { return n > HS ? (n - HS + NSH - 1) / NSH : 0; };
+            constexpr int NKM = share(NKI);                       // K (and Q) row loads
+            constexpr int NTM = share(2 * NTRI), NHM = share(2 * NHF), NPM = share(2 * NTRI);
+            constexpr bool VST = HS == NSH - 1;                   // the V block and the scalars
+            // Register-staged inputs (fp32 or d = 16 K rows; fp32 V): the set of window c holds
+            // K rows of chunk c + 3 and the V block of chunk c + 2, loaded two windows earlier;
+            // two sets alternate.
+            constexpr bool RK = !DQK, RV = !DV && VST;
+            struct RSet {
+                u32x4 kr[RK && NKM > 0 ? NKM : 1];
+                u32x4 vr[RV ? NVI : 1];
+            };
+            // K or Q rows of chunk c straight into ring slot `dst`: load m covers rows
+            // RPI (HS + NSH m) .., whose staged bytes form 1 KB; lane l lands at position l of it.
+            auto dma_rows = [&](const TIn* base, int64_t c, char* dst) {
+                const auto r = qk_rsrc(base, clampc(c));
 #pragma unroll
-                    for (int i = 0; i < NRT; ++i) {
-                        const int rt = HW + NHW * i;
-                        floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+                for (int m = 0; m < NKM; ++m) {
+                    const int mi = HS + NSH * m;
+                    const int row = RPI * mi + l / NG, pos = l % NG;
+                    const int g = pos ^ swz<RPB>(row);
+                    load_to_lds(r, dst + mi * 1024,
+                                (int)((uint32_t)(row * row_qk) + (uint32_t)(16 * g) + pad_if(row < C)));
+                }
+            };
+            // Fragment pieces HS + NSH m (1 KB each) of a workspace block into `dst`.
+            auto dma_pieces = [&](size_t region, size_t bytes, int64_t c, bf16x8 (*dst)[64], int n) {
+                const auto r = ws_rsrc(region, bytes, clampc(c));
 #pragma unroll
-                        for (int kt = 0; kt < KTD; ++kt) {
-                            bf16x8 qa[NS];
-                            if constexpr (QST)
-                                qa[0] = *reinterpret_cast<const bf16x8*>(s_qh + i * QR * ROWB + srow(lr, 4 * kt + lg));
-                            else
-                                to_pieces(x.qf[i][kt], qa);
-                            acc = mfma_split<2, NS>(mfr[kt], qa, acc);
-                        }
-                        acc *= s_sc[c & 3][2 * CP + 16 * rt + lr];  // o of token 16 rt + lr
+                for (int m = 0; HS + NSH * m < n; ++m)
+                    load_to_lds(r, dst[HS + NSH * m], (HS + NSH * m) * 1024 + l * 16);
+            };
+            auto ld_regs = [&](RSet& x, int64_t c) {  // the set of window c
+                if constexpr (RK) {
+                    const auto r = qk_rsrc(k, clampc(c + 3));
 #pragma unroll
-                        for (int kt = 0; 2 * kt <= rt; ++kt) acc = mfma_split<2, 2>(ufr[kt], x.pf[i][kt], acc);
-                        __builtin_amdgcn_raw_buffer_store_b128(
-                            __builtin_bit_cast(u32x4, acc), r_o,
-                            (int)((uint32_t)((16 * rt + lr) * row_o) + (uint32_t)(lg * 16) + pad_if(live)), 0, 0);
+                    for (int m = 0; m < NKM; ++m) {
+                        const int row = RPI * (HS + NSH * m) + l / LPR;
+                        x.kr[m] = __builtin_amdgcn_raw_buffer_load_b128(
+                            r, (int)((uint32_t)(row * row_qk) + (uint32_t)(16 * (l % LPR)) + pad_if(row < C)), 0, 0);
+                    }
+                }
+                if constexpr (RV) {
+                    const int64_t c3 = clampc(c + 2);
+                    const auto r_v = make_rsrc(v + (tok0_of(c3) * h_v + h) * (int64_t)D + cb * 16,
+                                               (rows_of(c3) - 1) * row_v + 16 * ES);
+#pragma unroll
+                    for (int m = 0; m < NVI; ++m) {
+                        const int t = TPI * m + l / LPT;
+                        x.vr[m] = __builtin_amdgcn_raw_buffer_load_b128(
+                            r_v, (int)((uint32_t)(t * row_v) + (uint32_t)(16 * (l % LPT)) + pad_if(t < C)), 0, 0);
                     }
                 }
             };
+            // The register-staged inputs of window c (K of chunk c + 3, V of chunk c + 2).
+            auto st_regs = [&](const RSet& x, int64_t c) {
+                if constexpr (RK) {
+                    if (c + 3 >= 0 && c + 3 < nch) {
+                        char* dst = s_k[ring(c + 3)];
+#pragma unroll
+                        for (int m = 0; m < NKM; ++m) {
+                            const int row = RPI * (HS + NSH * m) + l / LPR, g = l % LPR;
+                            if constexpr (ES == 2) {
+                                *reinterpret_cast<u32x4*>(dst + srow(row, g)) = x.kr[m];
+                            } else {
+                                const floatx4 y = __builtin_bit_cast(floatx4, x.kr[m]);
+                                uint32_t hi[2], lo[2];
+                                split2(y[0], y[1], &hi[0], &lo[0]);
+                                split2(y[2], y[3], &hi[1], &lo[1]);
+                                const int o = srow(row, g >> 1) + 8 * (g & 1);
+                                *reinterpret_cast<uint2*>(dst + o) = uint2{hi[0], hi[1]};
+                                *reinterpret_cast<uint2*>(dst + CP * ROWB + o) = uint2{lo[0], lo[1]};
+                            }
+                        }
+                    }
+                }
+                if constexpr (RV) {
+                    if (c + 2 >= 0 && c + 2 < nch) {
+                        float* dst = reinterpret_cast<float*>(s_v[ring(c + 2)]);
+#pragma unroll
+                        for (int m = 0; m < NVI; ++m) {
+                            const int t = TPI * m + l / LPT;  // < CP
+                            const floatx4 y = __builtin_bit_cast(floatx4, x.vr[m]);
+#pragma unroll
+                            for (int e = 0; e < 4; ++e) dst[(4 * (l % LPT) + e) * SG::VS + t] = y[e];
+                        }
+                    }
+                }
+            };
+            // The loads straight into LDS issued in window c (clamped chunks beyond the
+            // sequence land in ring slots nobody reads any more).
+            auto issue = [&](int64_t c) {
+                if constexpr (DQK) dma_rows(k, c + 4, s_k[ring(c + 4)]);
+                dma_pieces(L.tt, G::TRI_BYTES, c + 3, s_tf[ring(c + 3)], 2 * NTRI);
+                if constexpr (VST) {
+                    const int64_t c3 = clampc(c + 3);
+                    if constexpr (DV) {
+                        const auto r_v = make_rsrc(v + (tok0_of(c3) * h_v + h) * (int64_t)D + cb * 16,
+                                                   (rows_of(c3) - 1) * row_v + 32);
+#pragma unroll
+                        for (int m = 0; m < NVI; ++m) {
+                            const int t = TPI * m + l / 2;
+                            load_to_lds(r_v, s_v[ring(c + 3)] + m * 1024,
+                                        (int)((uint32_t)(t * row_v) + (uint32_t)(16 * (l & 1)) + pad_if(t < C)));
+                        }
+                    }
+                    load_to_lds(sc_rsrc(c3), s_sc[(c + 3) & 3], 16 * l);
+                }
+                dma_pieces(L.hh, G::H_BYTES, c + 2, s_h[ring(c + 2)], 2 * NHF);
+                if constexpr (DQK) dma_rows(q, c + 2, s_q[ring(c + 2)]);
+                dma_pieces(L.pt, G::TRI_BYTES, c + 2, s_pt[ring(c + 2)], 2 * NTRI);
+            };
+            // Vector memory operations one window issues: the loads straight into LDS, then
+            // the register loads. Loads complete in order, so the straight loads of window c - 1
+            // have landed once no more than those issued after them (the register loads of
+            // windows c - 1 and c and the straight loads of window c) are in flight.
+            constexpr int NDMA = (DQK ? 2 * NKM : 0) + NTM + NHM + NPM + (VST ? (DV ? NVI : 0) + 1 : 0);
+            constexpr int NREG = (RK ? NKM : 0) + (RV ? NVI : 0);
+            constexpr int NVM = NDMA + 2 * NREG;
 
-            // Prologue: K rows of chunk 0 into LDS; the sets of windows -2 and -1 in flight.
+            // Prologue: K rows of chunk 0 (and 1 when they load straight into LDS) and the
+            // chain's inputs of chunk 0 in place; window -2 writes the register-staged K rows of
+            // chunk 1 and V block of chunk 0.
             {
-                u32x4 kr0[NKM > 0 ? NKM : 1];
-                ld_k(kr0, 0);
+                if constexpr (DQK) {
+                    dma_rows(k, 0, s_k[ring(0)]);
+                    dma_rows(k, 1, s_k[ring(1)]);
+                } else {
+                    RSet x0;
+                    ld_regs(x0, -3);  // K rows of chunk 0
+                    settle();
+                    st_regs(x0, -3);
+                }
+                dma_pieces(L.tt, G::TRI_BYTES, 0, s_tf[ring(0)], 2 * NTRI);
+                if constexpr (VST) {
+                    if constexpr (DV) {
+                        const auto r_v = make_rsrc(v + (tok0_of(0) * h_v + h) * (int64_t)D + cb * 16,
+                                                   (rows_of(0) - 1) * row_v + 32);
+#pragma unroll
+                        for (int m = 0; m < NVI; ++m) {
+                            const int t = TPI * m + l / 2;
+                            load_to_lds(r_v, s_v[ring(0)] + m * 1024,
+                                        (int)((uint32_t)(t * row_v) + (uint32_t)(16 * (l & 1)) + pad_if(t < C)));
+                        }
+                    }
+                    load_to_lds(sc_rsrc(0), s_sc[0], 16 * l);
+                }
                 settle();
-                st_k(kr0, par(0));
             }
-            HSet A, B;
-            load_set(A, -2);
-            load_set(B, -1);
-            auto window = [&](HSet& x, int64_t c) {
-                __syncthreads();
-                do_output(x, c);
-                store_set(x, c);
+            RSet A, B;
+            ld_regs(A, -2);
+            ld_regs(B, -1);
+            auto window = [&](RSet& x, int64_t c) {
+                barrier_lds_only();
+                st_regs(x, c);
+                issue(c);
                 __builtin_amdgcn_sched_barrier(0);
-                load_set(x, c + 2);
+                ld_regs(x, c + 2);
+                wait_vm<NVM>();  // the loads straight into LDS issued in window c - 1 have landed
             };
 #pragma unroll 1
             for (int64_t c = -2; c < cend; c += 2) {
@@ -1351,19 +1383,23 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
             }
             settle();
         };
-        static_assert(NHW == 4, "the helper dispatch below covers four helpers");
+
+        static_assert(NHW == 4 && NOH >= 1 && NOH <= 2, "helper dispatch below");
         switch (hw) {
-            case 0: helper(std::integral_constant<int, 0>{}); break;
-            case 1: helper(std::integral_constant<int, 1>{}); break;
-            case 2: helper(std::integral_constant<int, 2>{}); break;
-            default: helper(std::integral_constant<int, 3>{}); break;
+            case 0: output_helper(std::integral_constant<int, 0>{}); break;
+            case 1:
+                if constexpr (NOH > 1) output_helper(std::integral_constant<int, 1>{});
+                else staging_helper(std::integral_constant<int, 0>{});
+                break;
+            case 2: staging_helper(std::integral_constant<int, 2 - NOH>{}); break;
+            default: staging_helper(std::integral_constant<int, 3 - NOH>{}); break;
         }
     }
 }
 
-// ======================================================================= scan, C = 128
-// At C = 128 the pipeline above does not fit LDS (its double-buffered exchange state alone
-// exceeds 160 KB at d = 128). This variant keeps the state in two "chain" waves (halves of
+// ============================================================ scan, chunks of 64 and 128 tokens
+// For longer chunks the pipeline above does not fit LDS (its staging rings and exchange
+// buffers grow with the chunk). This variant keeps the state in two "chain" waves (halves of
 // d_k), which run the recurrence with one exchange of partial K M0 products per chunk, while
 // two "output" waves stage T', V and the scalars and form the outputs one chunk behind.
 template <int D, int C, typename TIn>
@@ -1873,7 +1909,7 @@ hipError_t launch_chunked_t(const Call& cl)
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int64_t scan_blocks = cl.n * cl.h_v * (D / 16);
-    if constexpr (C <= 64) {
+    if constexpr (C <= 32) {
         hipLaunchKernelGGL((chunk_scan_kernel<D, C, TIn>), dim3((unsigned)scan_blocks),
                            dim3(ScanGeo<D, C, TIn>::THREADS), 0, cl.stream, q, k, v, ws, L,
                            cl.state_in, cl.out, cl.state_out, cl.t, cl.h_qk, cl.h_v, scan_blocks);
