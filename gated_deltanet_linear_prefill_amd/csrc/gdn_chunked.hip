@@ -25,12 +25,14 @@
 //    inverse norms, gate prefix sums, the Gram matrices K K^T and Q K^T (MFMA, once per QK
 //    head), then per V head A, T = (I + A)^-1 by blocked forward substitution in LDS, and
 //    the per-token scalars. T' and Ptil go to the workspace as hi/lo bf16 MFMA A-operand
-//    tiles (lower-triangular tiles only), K^T as A-operand tiles.
+//    tiles (lower-triangular tiles only); for chunks of up to 32 tokens also the chunk
+//    coupling H = K_next K^T diag(s) T' that the scan's chain recursion uses.
 //  * chunk_scan_kernel (one workgroup per sequence, V head and 16 value channels;
-//    sequential over chunks). Two "chain" waves each keep half of the state's d_k rows in
-//    MFMA accumulators and run the recurrence; per chunk they exchange one partial
-//    product K M0 through LDS, with a single workgroup barrier per chunk. The other waves
-//    form the outputs O of the previous chunk from the state and U the chain waves publish.
+//    sequential over chunks). For chunks of up to 32 tokens a chain wave runs the
+//    recursion over the residuals X alone, state waves keep the state in MFMA accumulators
+//    a chunk behind, and helper waves form the outputs and stage every input in LDS ahead of
+//    use (the scan section below). Chunks of 64 and 128 tokens use a variant with two chain
+//    waves that each hold half of the state and exchange one partial product per chunk.
 //
 // Operand order. Contractions over d_k and over chunk tokens both use k tiles of 32. The
 // state's accumulator rows hold features in a permuted order (tile mt, row 4a + e holds

@@ -95,43 +95,56 @@ def test_chunked_head_groups():
         assert_parity(out, st, o_ref, s_ref, f"chunked h_qk={h_qk} h_v={h_v}")
 
 
-def test_chunked_in_place_empty_deterministic():
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunked_in_place_empty_deterministic(chunk):
     shape = Shape(n=1, t=200, h_qk=2, h_v=4, d=128)
     c = gdn_inputs.make_case(shape, seed=9, device=DEV, s0_std=0.2)
-    o1, s1 = gdn.gdn_prefill_chunked(**c, chunk=64)
+    o1, s1 = gdn.gdn_prefill_chunked(**c, chunk=chunk)
     st = c["state_in"].clone()
     o2, _ = gdn.gdn_prefill_chunked(c["q"], c["k"], c["v"], c["g"], c["beta"], st, state_out=st,
-                                    chunk=64)
+                                    chunk=chunk)
     torch.cuda.synchronize()
     assert torch.equal(o1, o2) and torch.equal(s1, st)  # bitwise run to run, in place
     e = {key: (val[:, :0].contiguous() if key != "state_in" else val) for key, val in c.items()}
-    _, s0 = gdn.gdn_prefill_chunked(**e, chunk=64)
-    _, z0 = gdn.gdn_prefill_chunked(**dict(e, state_in=None), chunk=64)
+    _, s0 = gdn.gdn_prefill_chunked(**e, chunk=chunk)
+    _, z0 = gdn.gdn_prefill_chunked(**dict(e, state_in=None), chunk=chunk)
     torch.cuda.synchronize()
     assert torch.equal(s0, c["state_in"]) and torch.count_nonzero(z0) == 0
 
 
-def test_chunked_retrieval_and_column_independence():
+@pytest.mark.parametrize("chunk", [16, 32, 64])
+def test_chunked_retrieval_and_column_independence(chunk):
     shape = Shape(n=1, t=256, h_qk=2, h_v=4, d=128)
     c = gdn_inputs.make_case(shape, seed=11, device=DEV, retrieval=True)
-    out, _ = gdn.gdn_prefill_chunked(c["k"], c["k"], c["v"], c["g"], c["beta"], l2_eps=0.0, chunk=64)
+    out, _ = gdn.gdn_prefill_chunked(c["k"], c["k"], c["v"], c["g"], c["beta"], l2_eps=0.0,
+                                     chunk=chunk)
     torch.cuda.synchronize()
     assert out_error(out, c["v"]) < 2e-3
     c = gdn_inputs.make_case(shape, seed=12, device=DEV, s0_std=0.1)
     c["v"][..., 77] = 0
     c["state_in"][..., 77] = 0
-    out, st = gdn.gdn_prefill_chunked(**c, chunk=64)
+    out, st = gdn.gdn_prefill_chunked(**c, chunk=chunk)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out[..., 77]) == 0 and torch.count_nonzero(st[..., 77]) == 0
 
 
 # ------------------------------------------------------------------------ full sizes
-def test_chunked_prefill_4k():
-    """The 4096-token prefill workload (16 QK / 32 V heads, d=128, bf16, S0=0, chunk 64),
-    in the launch configuration the benchmark times: every output and the final state of
-    a sample of V heads against the oracle; all heads against the direct scan."""
+def bench_chunk(shape):
+    """The method gdn_prefill picks for a shape (what the benchmark times); chunked here."""
+    chunk = gdn.gdn_prefill_choose(shape.t, shape.h_qk, shape.h_v, shape.d, shape.n, shape.dtype)
+    assert chunk > 0, chunk
+    return chunk
+
+
+@pytest.mark.parametrize("which", ["dispatch", "C=64"])
+def test_chunked_prefill_4k(which):
+    """The 4096-token prefill workload (16 QK / 32 V heads, d=128, bf16, S0=0) in the launch
+    configuration the benchmark times (the chunk gdn_prefill picks, 32 on MI355X) and at
+    chunk 64: every output and the final state of a sample of V heads against the oracle;
+    all heads against the direct scan."""
     c = gdn_inputs.make_case(gdn_inputs.PREFILL_4K, seed=2, device=DEV)
-    out, st = gdn.gdn_prefill_chunked(**c, chunk=64)
+    chunk = bench_chunk(gdn_inputs.PREFILL_4K) if which == "dispatch" else 64
+    out, st = gdn.gdn_prefill_chunked(**c, chunk=chunk)
     out_s, st_s = gdn.gdn_prefill_scan(**c)
     torch.cuda.synchronize()
     heads = [0, 5, 18, 31]
@@ -144,20 +157,21 @@ def test_chunked_prefill_4k():
 
 def test_chunked_long_131072_segments():
     """The long-prefill workload: T = 131072 as 32 segments of 4096 with the state carried
-    between calls (chunk 64). Per-segment outputs and the final state of sampled V heads
-    against one single-pass oracle run."""
+    between calls, with the chunk gdn_prefill picks for a segment. Per-segment outputs and
+    the final state of sampled V heads against one single-pass oracle run."""
     seg_t, nseg = gdn_inputs.LONG_SEGMENT.t, gdn_inputs.LONG_SEGMENTS
     heads = [3, 28]
     st = torch.zeros(1, 32, 128, 128, device=DEV)
     host = {key: [] for key in ("q", "k", "v", "g", "beta")}
     outs = []
-    ws = torch.empty(gdn.gdn_workspace_bytes(1, seg_t, 16, 32, 128, chunk=64), device=DEV,
+    chunk = bench_chunk(gdn_inputs.LONG_SEGMENT)
+    ws = torch.empty(gdn.gdn_workspace_bytes(1, seg_t, 16, 32, 128, chunk=chunk), device=DEV,
                      dtype=torch.uint8)
     out = torch.empty(1, seg_t, 32, 128, device=DEV)
     for s in range(nseg):
         c = gdn_inputs.make_case(gdn_inputs.LONG_SEGMENT, seed=4000 + s, device=DEV)
         gdn.gdn_prefill_chunked(c["q"], c["k"], c["v"], c["g"], c["beta"], st, out=out,
-                                state_out=st, workspace=ws, chunk=64)
+                                state_out=st, workspace=ws, chunk=chunk)
         sl = head_slice(c, heads, 2)
         for key in host:
             host[key].append(sl[key])
@@ -178,16 +192,18 @@ def test_chunked_long_131072_segments():
 
 @pytest.mark.parametrize("t", gdn_inputs.SWEEP_T)
 def test_sweep_grid_parity(t):
-    """The scan-versus-chunk sweep grid at one length: chunk 32, 64 and 128 and the direct
-    scan against one oracle run of sampled heads; then the retrieval inputs (g = 0,
-    beta = 1) at the same length, where the same bar applies."""
+    """The scan-versus-chunk sweep grid at one length: chunk 16, 32, 64 and 128, the direct
+    scan and the dispatching gdn_prefill against one oracle run of sampled heads; then the
+    retrieval inputs (g = 0, beta = 1) at the same length, where the same bar applies."""
     shape = Shape(n=1, t=t, **FULL)
     for retrieval in (False, True):
         c = gdn_inputs.make_case(shape, seed=5000 + t, device=DEV, retrieval=retrieval)
         heads = [7, 24]
         ref = oracle_heads(c, heads, 2)
-        runs = {f"C={cs}": gdn.gdn_prefill_chunked(**c, chunk=cs) for cs in gdn_inputs.SWEEP_CHUNKS}
+        chunks = sorted({16, *gdn_inputs.SWEEP_CHUNKS})
+        runs = {f"C={cs}": gdn.gdn_prefill_chunked(**c, chunk=cs) for cs in chunks}
         runs["scan"] = gdn.gdn_prefill_scan(**c)
+        runs["dispatch"] = gdn.gdn_prefill(**c)
         torch.cuda.synchronize()
         for name, (out, st) in runs.items():
             assert torch.isfinite(out).all() and torch.isfinite(st).all(), name
