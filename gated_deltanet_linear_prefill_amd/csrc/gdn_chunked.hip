@@ -762,8 +762,9 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 // P_{c+1} needs the state of one chunk earlier, so the state waves, which hold the state
 // split over d_k, form it (with the reduction over d_k) a chunk before it is used: no
 // exchange over d_k sits on the chain's path. The chain wave also forms U = T' X and
-// W = diag(s) U; the state waves apply M_{c+1} = Gamma_c M_c + K_c^T W_c one chunk later,
-// and the first helpers form the outputs O_c = diag(o) Q_c M_c + Ptil_c U_c.
+// W = diag(s) U; the state waves apply M_{c+1} = Gamma_c M_c + K_c^T W_c one chunk later and
+// form their parts of Q_{c+1} M_{c+1}, and the first helpers complete the outputs
+// O_c = diag(o) Q_c M_c + Ptil_c U_c.
 //
 // The other helpers move every input into LDS two windows ahead of its use, with loads
 // that write LDS directly (each lane's 16 bytes land at the destination base plus 16 bytes
@@ -777,12 +778,14 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 // Time advances in windows c = -2, -1, ..., nch - 1 (and one idle window more when that
 // count is odd, so that the two-window loops below have no conditional half), each opened
 // by a workgroup barrier:
-//   chain    window c: X_{c+1}, U_{c+1}, W_{c+1}        (c >= -1)
-//   state    window c: M_{c+1} (c >= 0); Gamma_{c+1} P_{c+2} and K_{c+2}^T fragments
+//   chain    window c: X_{c+1}, U_{c+1}, W_{c+1} (c >= -1); H_{c+1} X_{c+1}; reads the
+//                      V block, scalars and T' of chunk c + 2
+//   state    window c: M_{c+1} (c >= 0); (Q_{c+1} M_{c+1})^T; Gamma_{c+1} P_{c+2} and
+//                      K_{c+2}^T fragments
 //   output   window c: outputs of chunk c                 (c >= 0)
-//   staging  window c: issue K_{c+4}, T', V and scalars of chunk c + 3, H, Q and Ptil of
-//                      chunk c + 2; wait for those issued in window c - 1
-// Staged inputs sit in rings of three chunks (the scalars in four); exchanges between the
+//   staging  window c: issue K_{c+4}, T', V and scalars of chunk c + 4, H_{c+3}, Q_{c+3},
+//                      Ptil_{c+2}; wait for those issued in window c - 1
+// Staged inputs sit in rings of three chunks (the scalars in eight); exchanges between the
 // compute waves are double-buffered by chunk parity.
 template <int D, int C, typename TIn>
 struct ScanGeo {
@@ -807,9 +810,11 @@ struct ScanGeo {
     static constexpr int RPI = 64 / LPR;
     static constexpr int NKI = (C + RPI - 1) / RPI;        // row loads per chunk
     // K and Q rows load straight into LDS when a load's 64 lanes fill 1 KB of staged rows
-    // (bf16 and d >= 32); otherwise K goes through registers and the output helpers load Q
-    // fragments themselves.
+    // (bf16 and d >= 32); otherwise they go through registers.
     static constexpr bool DQK = ES == 2 && D >= 32;
+    // Q ring depth: rows loaded straight into LDS are issued two windows before use (three
+    // slots); rows written from registers one window before (two slots).
+    static constexpr int NRQ = DQK ? NR : 2;
     // The V block (16 channels of a token): bf16 rows straight into LDS (read back with
     // transposing reads); fp32 through registers, transposed to channel-major.
     static constexpr bool DV = ES == 2;
@@ -818,7 +823,7 @@ struct ScanGeo {
     static constexpr int NVI = (C + TPI - 1) / TPI;
     static constexpr int VS = G::CP + 4;                   // LDS row stride of a transposed V block
     static constexpr size_t K_BYTES = (size_t)G::NS * G::CP * ROWB;
-    static constexpr size_t Q_BYTES = DQK ? (size_t)G::CP * ROWB : 16;
+    static constexpr size_t Q_BYTES = K_BYTES;
     static constexpr size_t V_BYTES = DV ? (size_t)G::CP * 32 : (size_t)16 * VS * 4;
 };
 
@@ -867,7 +872,7 @@ __device__ __forceinline__ void wait_vm()
 }
 
 template <int D, int C, typename TIn>
-__global__ void __launch_bounds__((ScanGeo<D, C, TIn>::THREADS))
+__global__ void __launch_bounds__((ScanGeo<D, C, TIn>::THREADS)) __attribute__((amdgpu_waves_per_eu(1, 2)))
 chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
                   const char* __restrict__ ws, ChunkWs L, const float* state_in,
                   float* __restrict__ out, float* state_out, int64_t T, int h_qk, int h_v,
@@ -885,27 +890,28 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     constexpr int LPT = SG::LPT, TPI = SG::TPI, NVI = SG::NVI;
     constexpr int ES = SG::ES;
     constexpr bool DQK = SG::DQK, DV = SG::DV;
+    constexpr int NSC = 8;  // scalar ring depth (chunk mod 8)
 
-    // LDS (ring slots by chunk mod NR, the scalars by chunk mod 4, exchanges by parity):
+    // LDS (ring slots by chunk mod NR, the scalars by chunk mod NSC, exchanges by parity):
     //   s_k   K rows of a chunk (NS bf16 planes, swizzled granules)
-    //   s_q   Q rows of a chunk (bf16, swizzled granules)
+    //   s_q   Q rows of a chunk (as s_k)
     //   s_pt  Ptil^T, s_h H, s_tf T' of a chunk (fragments, hi and lo pieces)
     //   s_v   the V block of a chunk: bf16 rows, or channel-major fp32
     //   s_sc  the scalars of a chunk (a, s, o, Gamma_C as laid out in the workspace)
     //   s_p   each state wave's part of Gamma_c P_{c+1}, by parity of c + 1
     //   s_wf  W as B fragments (hi, lo), s_uf U (fp32, accumulator layout), by parity
-    //   s_mf  the state entering a chunk as B fragments (hi, lo), by parity
+    //   s_qm  each state wave's part of (Q M)^T for a chunk's outputs, by parity
     __shared__ __align__(16) char s_k[NR][SG::K_BYTES];
-    __shared__ __align__(16) char s_q[DQK ? NR : 1][SG::Q_BYTES];
+    __shared__ __align__(16) char s_q[SG::NRQ][SG::Q_BYTES];
     __shared__ __align__(16) bf16x8 s_pt[NR][2 * NTRI][64];
     __shared__ __align__(16) bf16x8 s_h[NR][2 * NHF][64];
     __shared__ __align__(16) bf16x8 s_tf[NR][2 * NTRI][64];
     __shared__ __align__(16) char s_v[NR][SG::V_BYTES];
-    __shared__ __align__(16) float s_sc[4][256];
+    __shared__ __align__(16) float s_sc[NSC][256];
     __shared__ __align__(16) floatx4 s_p[2][NSW][RT][64];
     __shared__ __align__(16) bf16x8 s_wf[2][KTC][2][64];
     __shared__ __align__(16) floatx4 s_uf[2][RT][64];
-    __shared__ __align__(16) bf16x8 s_mf[2][KTD][2][64];
+    __shared__ __align__(16) floatx4 s_qm[2][NSW][RT][64];
 
     // Workgroups that share a QK head run on the same XCD (blockIdx % 8 picks the XCD), so
     // their common K/Q/H/T'/Ptil reads meet in one L2.
@@ -927,6 +933,7 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     const int64_t row_o = (int64_t)h_v * D * 4;
     auto par = [](int64_t c) { return (int)(c & 1); };
     auto ring = [](int64_t c) { return (int)(c % NR); };  // c >= 0
+    auto qslot = [](int64_t c) { return (int)(c % SG::NRQ); };
     auto clampc = [&](int64_t c) { return c < 0 ? 0 : (c < nch ? c : nch - 1); };
     auto tok0_of = [&](int64_t c) { return seq * T + c * C; };
     auto rows_of = [&](int64_t c) { return (T - c * C) < C ? (T - c * C) : (int64_t)C; };
@@ -948,32 +955,51 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     // A full wait: nothing left in flight, so the compiler's wait bookkeeping starts clean.
     auto settle = [&]() { __builtin_amdgcn_s_waitcnt(0); };
     // Four consecutive staged values of accumulator rows 4 lg .. 4 lg + 3 of row tile rt.
-    auto sc4 = [&](int64_t c, int off) { return *reinterpret_cast<const floatx4*>(&s_sc[c & 3][off + 4 * lg]); };
-    auto gc_of = [&](int64_t c) { return s_sc[c & 3][3 * CP]; };
+    auto sc4 = [&](int64_t c, int off) { return *reinterpret_cast<const floatx4*>(&s_sc[c & (NSC - 1)][off + 4 * lg]); };
+    auto gc_of = [&](int64_t c) { return s_sc[c & (NSC - 1)][3 * CP]; };
     // V of tokens 16 rt + 4 lg + 0..3, channel lr (bf16 rows: one transposing read in which
     // lane 4 p + q of each 16-lane group addresses token 16 rt + 4 lg + p, channels 4 q ..)
-    auto vt4 = [&](int64_t c, int rt) {
+    using VRaw = typename std::conditional<DV, bf16x4, floatx4>::type;
+    auto vt4 = [&](int64_t c, int rt) -> VRaw {
         const char* base = s_v[ring(c)];
-        if constexpr (DV) {
-            const bf16x4 x = lds_read_tr16(base + (16 * rt + 4 * lg + (lr >> 2)) * 32 + 8 * (lr & 3));
-            return floatx4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
-        } else {
+        if constexpr (DV)
+            return lds_read_tr16(base + (16 * rt + 4 * lg + (lr >> 2)) * 32 + 8 * (lr & 3));
+        else
             return *reinterpret_cast<const floatx4*>(base + (lr * SG::VS + 16 * rt + 4 * lg) * 4);
-        }
+    };
+    auto vf4 = [](const VRaw& x) {
+        if constexpr (DV) return floatx4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
+        else return x;
     };
 
     if (w == 0) {
         // ======================================================= chain wave
+        // Window c forms X_{c+1}, U_{c+1}, W_{c+1} from inputs read in window c - 1 (V, a, s
+        // and T' of chunk c + 1) and from H_c X_c, formed in window c - 1 as soon as X_c was
+        // known; so after the barrier only the state waves' partials are awaited.
+        struct CIn { VRaw v[RT]; floatx4 a[RT], s[RT]; bf16x8 tf[2 * NTRI]; };
+        auto fetch = [&](CIn& x, int64_t j) {  // inputs of chunk j
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                x.v[rt] = vt4(j, rt);
+                x.a[rt] = sc4(j, 16 * rt);
+                x.s[rt] = sc4(j, CP + 16 * rt);
+            }
+#pragma unroll
+            for (int pi = 0; pi < 2 * NTRI; ++pi) x.tf[pi] = s_tf[ring(j)][pi][l];
+        };
         __syncthreads();  // the staged-row buffers are cleared and the first inputs staged
         bf16x8 xf[KTC][2];  // X of the latest chunk as B fragments (hi, lo)
+        floatx4 hx[RT];     // H_c X_c for the next window
 #pragma unroll
-        for (int kt = 0; kt < KTC; ++kt) xf[kt][0] = xf[kt][1] = bf16x8{};
-#pragma unroll 1
-        for (int64_t c = -2; c < cend; ++c) {
+        for (int rt = 0; rt < RT; ++rt) hx[rt] = floatx4{0.f, 0.f, 0.f, 0.f};
+        // A window has no branches, so that the compiler keeps every LDS read right after the
+        // barrier: slots of chunks that do not exist are read too (any contents do), and their
+        // products land in exchange buffers that nobody reads. X of such a window is set to
+        // zero, which keeps H X of the first window zero.
+        auto window = [&](int64_t c, const CIn& cur, CIn& nxt) {
             __syncthreads();
-            if (c < -1 || c + 1 >= nch) continue;  // wave-uniform
             const int pn = par(c + 1);
-            // Z = Gamma_c P_{c+1} (the state waves' parts summed in wave order) + H_c X_c
             floatx4 z[RT];
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) {
@@ -981,20 +1007,24 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
 #pragma unroll
                 for (int sw = 1; sw < NSW; ++sw) z[rt] += s_p[pn][sw][rt][l];
             }
-            if (c >= 0) {
+            const int hs = ring(c + 1 < 0 ? 0 : c + 1);
+            bf16x8 hf[RT][KTC][2];
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt)
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                    for (int kt = 0; kt < KTC; ++kt) {
-                        const int fi = rt * KTC + kt;
-                        const bf16x8 hf[2] = {s_h[ring(c)][2 * fi][l], s_h[ring(c)][2 * fi + 1][l]};
-                        z[rt] = mfma_split<2, 2>(hf, xf[kt], z[rt]);
-                    }
-            }
-            // X_{c+1} = V - diag(a) Z
+                for (int kt = 0; kt < KTC; ++kt)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) hf[rt][kt][p] = s_h[hs][2 * (rt * KTC + kt) + p][l];
+            fetch(nxt, c + 2 < 0 ? 0 : c + 2);
+            const bool live = c >= -1 && c + 1 < nch;  // wave-uniform
+            // X_{c+1} = V - diag(a) (Gamma_c P_{c+1} + H_c X_c)
             floatx4 xv[RT];
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) xv[rt] = vt4(c + 1, rt) - sc4(c + 1, 16 * rt) * z[rt];
+            for (int rt = 0; rt < RT; ++rt) {
+                const floatx4 x = vf4(cur.v[rt]) - cur.a[rt] * (z[rt] + hx[rt]);
+#pragma unroll
+                for (int e = 0; e < 4; ++e) xv[rt][e] = live ? x[e] : 0.f;
+            }
             rows_to_frags<RT, KTC>(xv, xf);
             // U = T' X (lower triangular: row tile rt uses token k tiles 0 .. rt / 2)
             floatx4 u[RT];
@@ -1004,22 +1034,37 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
 #pragma unroll
                 for (int kt = 0; 2 * kt <= rt; ++kt) {
                     const int pi = 2 * (tri_off(rt) + kt);
-                    const bf16x8 tf[2] = {s_tf[ring(c + 1)][pi][l], s_tf[ring(c + 1)][pi + 1][l]};
-                    acc = mfma_split<2, 2>(tf, xf[kt], acc);
+                    acc = mfma_split<2, 2>(&cur.tf[pi], xf[kt], acc);
                 }
                 u[rt] = acc;
+            }
+            // H_{c+1} X_{c+1} for the next window
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt) acc = mfma_split<2, 2>(hf[rt][kt], xf[kt], acc);
+                hx[rt] = acc;
             }
 #pragma unroll
             for (int rt = 0; rt < RT; ++rt) s_uf[pn][rt][l] = u[rt];
             // W = diag(s) U for the state waves
 #pragma unroll
-            for (int rt = 0; rt < RT; ++rt) u[rt] *= sc4(c + 1, CP + 16 * rt);
+            for (int rt = 0; rt < RT; ++rt) u[rt] *= cur.s[rt];
             bf16x8 wf[KTC][2];
             rows_to_frags<RT, KTC>(u, wf);
 #pragma unroll
             for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
                 for (int p = 0; p < 2; ++p) s_wf[pn][kt][p][l] = wf[kt][p];
+        };
+        // Chunk parity alternates between windows, and so do the two input sets: window c
+        // uses the set of chunk c + 1 and fills that of chunk c + 2.
+        CIn A, B;
+#pragma unroll 1
+        for (int64_t c = -2; c < cend; c += 2) {
+            window(c, B, A);
+            window(c + 1, A, B);
         }
     } else if (w <= NSW) {
         // ======================================================= state wave sw
@@ -1041,22 +1086,33 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                 for (int e = 0; e < 4; ++e) macc[i][e] = buf_elem<float>(r, st_off(2 * KPS * sw + i, e));
         }
         bf16x8 mf[KPS][2];  // this wave's d_k tiles of the state as B fragments (hi, lo)
-        auto split_publish = [&](int p) {
+        auto split = [&]() {
 #pragma unroll
-            for (int kk = 0; kk < KPS; ++kk) {
-                pair_to_frag(macc[2 * kk], macc[2 * kk + 1], mf[kk][0], mf[kk][1]);
-#pragma unroll
-                for (int pp = 0; pp < 2; ++pp) s_mf[p][KPS * sw + kk][pp][l] = mf[kk][pp];
-            }
+            for (int kk = 0; kk < KPS; ++kk) pair_to_frag(macc[2 * kk], macc[2 * kk + 1], mf[kk][0], mf[kk][1]);
         };
-        split_publish(0);  // the state entering chunk 0, for the output helpers
-        __syncthreads();   // the staged-row buffers are cleared and the first inputs staged
+        split();          // the state entering chunk 0
+        __syncthreads();  // the staged-row buffers are cleared and the first inputs staged
+        // A fragment pieces of staged rows (K or Q of a chunk): rows 16 rt + 0..15, the features
+        // of this wave's d_k tile kk.
+        auto row_frag = [&](const char* rows, int rt, int kk, bf16x8* a) {
+#pragma unroll
+            for (int part = 0; part < NS; ++part)
+                a[part] = *reinterpret_cast<const bf16x8*>(
+                    rows + part * CP * ROWB + srow(16 * rt + lr, 4 * (KPS * sw + kk) + lg));
+        };
 
         // K^T A fragments of a chunk for this wave's state tiles, read two windows before the
-        // state update that uses them. Fragment (i, kt): two transposing reads (token slots
+        // state update that uses them (when the chunk's rows are first used for P; the ring
+        // slot is refilled before the update). Fragment (i, kt): two transposing reads (token slots
         // 0..3, 4..7); lane lr of group lg addresses token row 32 kt + 16 h + 4 lg + lr / 4 and
         // features 32 (KPS sw + i / 2) + 8 (lr % 4) + 4 (i % 2) + 0..3.
         bf16x8 ktA[2 * KPS][KTC][NS], ktB[2 * KPS][KTC][NS];
+#pragma unroll
+        for (int i = 0; i < 2 * KPS; ++i)
+#pragma unroll
+            for (int kt = 0; kt < KTC; ++kt)
+#pragma unroll
+                for (int part = 0; part < NS; ++part) ktA[i][kt][part] = ktB[i][kt][part] = bf16x8{};
         auto read_kt = [&](bf16x8 (*kts)[KTC][NS], int slot) {
 #pragma unroll
             for (int i = 0; i < 2 * KPS; ++i)
@@ -1072,46 +1128,68 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                         kts[i][kt][part] = bf16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
                     }
         };
+        // Every LDS read of a window is issued right after its barrier, so that the state
+        // update, the split and the products wait for one round of reads; the window has no
+        // branches, so the compiler keeps the reads there. Slots are read even when their
+        // chunk does not exist (any contents do), and the products of such windows land in
+        // exchange buffers nobody reads. Without a chunk the update is M <- 1 * M + K^T 0,
+        // exact, with W selected to zero and K^T finite (staged rows or zero).
         auto window = [&](int64_t c, bf16x8 (*kts)[KTC][NS]) {
             __syncthreads();
-            if (c >= 0 && c < nch) {
-                // M_{c+1} = Gamma_c M_c + K_c^T W_c
-                const int pc = par(c);
-                const float gcc = gc_of(c);
-                bf16x8 wf[KTC][2];
+            const int64_t c1 = c + 1 < 0 ? 0 : c + 1, c2 = c + 2 < 0 ? 0 : c + 2;
+            bf16x8 wf[KTC][2];
 #pragma unroll
-                for (int kt = 0; kt < KTC; ++kt)
+            for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
-                    for (int p = 0; p < 2; ++p) wf[kt][p] = s_wf[pc][kt][p][l];
+                for (int p = 0; p < 2; ++p) wf[kt][p] = s_wf[par(c)][kt][p][l];
+            bf16x8 qa[RT][KPS][NS], ka[RT][KPS][NS];
 #pragma unroll
-                for (int i = 0; i < 2 * KPS; ++i) {
-                    floatx4 acc = gcc * macc[i];
+            for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-                    for (int kt = 0; kt < KTC; ++kt) acc = mfma_split<NS, 2>(kts[i][kt], wf[kt], acc);
-                    macc[i] = acc;
+                for (int kk = 0; kk < KPS; ++kk) {
+                    row_frag(s_q[qslot(c1)], rt, kk, qa[rt][kk]);
+                    row_frag(s_k[ring(c2)], rt, kk, ka[rt][kk]);
                 }
-                split_publish(par(c + 1));  // the state entering chunk c + 1, for the helpers
-            }
-            if (c + 2 < nch) {
-                // Gamma_{c+1} K_{c+2} M_{c+1} over this wave's features (unscaled for chunk 0)
-                const int slot = ring(c + 2), p2 = par(c + 2);
-                const float scale = c >= -1 ? gc_of(c + 1) : 1.f;
+            const bool upd = c >= 0 && c < nch;  // wave-uniform
+            const float gcc = upd ? gc_of(c) : 1.f, gc1 = gc_of(c1);
 #pragma unroll
-                for (int rt = 0; rt < RT; ++rt) {
-                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+            for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
-                    for (int kk = 0; kk < KPS; ++kk) {
-                        bf16x8 ka[NS];
+                for (int p = 0; p < 2; ++p) {
+                    u32x4 x = __builtin_bit_cast(u32x4, wf[kt][p]);
 #pragma unroll
-                        for (int part = 0; part < NS; ++part)
-                            ka[part] = *reinterpret_cast<const bf16x8*>(
-                                s_k[slot] + part * CP * ROWB + srow(16 * rt + lr, 4 * (KPS * sw + kk) + lg));
-                        acc = mfma_split<NS, 2>(ka, mf[kk], acc);
-                    }
-                    s_p[p2][sw][rt][l] = scale * acc;
+                    for (int e = 0; e < 4; ++e) x[e] = upd ? x[e] : 0u;
+                    wf[kt][p] = __builtin_bit_cast(bf16x8, x);
                 }
-                read_kt(kts, slot);  // K^T of chunk c + 2 replaces K^T of chunk c
+            // M_{c+1} = Gamma_c M_c + K_c^T W_c
+#pragma unroll
+            for (int i = 0; i < 2 * KPS; ++i) {
+                floatx4 acc = gcc * macc[i];
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt) acc = mfma_split<NS, 2>(kts[i][kt], wf[kt], acc);
+                macc[i] = acc;
             }
+            split();  // the state entering chunk c + 1
+            // (Q_{c+1} M_{c+1})^T over this wave's features, for the output helpers: the state
+            // fragments serve as A operands and the Q row fragments as B operands, so each lane
+            // ends up with four value channels of one token
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KPS; ++kk) acc = mfma_split<2, NS>(mf[kk], qa[rt][kk], acc);
+                s_qm[par(c1)][sw][rt][l] = acc;
+            }
+            // Gamma_{c+1} K_{c+2} M_{c+1} over this wave's features (unscaled for chunk 0)
+            const float scale = c >= -1 ? gc1 : 1.f;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KPS; ++kk) acc = mfma_split<NS, 2>(ka[rt][kk], mf[kk], acc);
+                s_p[par(c2)][sw][rt][l] = scale * acc;
+            }
+            read_kt(kts, ring(c2));  // K^T of chunk c + 2 replaces K^T of chunk c
         };
         // Chunk parity alternates between windows, and so do the two K^T register sets.
 #pragma unroll 1
@@ -1142,75 +1220,48 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
         // lane makes the same number of trips.)
         for (int o = 1024 * hw; o < (int)(NR * SG::K_BYTES); o += 1024 * NHW)
             *reinterpret_cast<u32x4*>(&s_k[0][0] + o + 16 * l) = u32x4{0u, 0u, 0u, 0u};
+        for (int o = 1024 * hw; o < (int)(SG::NRQ * SG::Q_BYTES); o += 1024 * NHW)
+            *reinterpret_cast<u32x4*>(&s_q[0][0] + o + 16 * l) = u32x4{0u, 0u, 0u, 0u};
         __syncthreads();
 
         auto output_helper = [&](auto hw_const) {
             constexpr int RTO = decltype(hw_const)::value;  // the row tile of this helper
-            // Q fragments are loaded here when they are not staged (two sets alternate,
-            // each loaded two windows ahead)
-            struct QSet { Raw qf[DQK ? 1 : KTD]; };
-            auto load_q = [&](QSet& x, int64_t c) {
-                if constexpr (!DQK) {
-                    const auto r = qk_rsrc(q, clampc(c));
-#pragma unroll
-                    for (int kt = 0; kt < KTD; ++kt) {
-                        const int f = 32 * kt + 8 * lg;
-                        x.qf[kt] = buf_raw_frag<TIn>(
-                            r, (int)((uint32_t)((16 * RTO + lr) * row_qk) + (uint32_t)(f * ES) + pad_if(f < D)));
-                    }
-                }
-            };
             // Outputs of chunk c, formed transposed: O^T = (Q M_c)^T diag(o) + U^T Ptil^T as 16
-            // value channels x 16 tokens tiles; the state and U fragments serve unchanged as A
-            // operands, the Q row fragments and Ptil^T as B operands, and each lane ends up with
-            // four consecutive channels of one token (one 16-byte store). Windows outside the
-            // chunks store out of range.
-            auto do_output = [&](const QSet& x, int64_t c) {
+            // value channels x 16 tokens tiles. The state waves' parts of (Q M_c)^T are summed;
+            // the U fragments serve as A operands and Ptil^T as B operands, and each lane ends
+            // up with four consecutive channels of one token (one 16-byte store). Windows
+            // outside the chunks store out of range.
+            auto do_output = [&](int64_t c) {
                 const bool live = c >= 0 && c < nch;  // wave-uniform
                 c = clampc(c);
                 const int pc = par(c), slot = ring(c);
-                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-                for (int kt = 0; kt < KTD; ++kt) {
-                    const bf16x8 mfr[2] = {s_mf[pc][kt][0][l], s_mf[pc][kt][1][l]};
-                    bf16x8 qa[NS];
-                    if constexpr (DQK)
-                        qa[0] = *reinterpret_cast<const bf16x8*>(s_q[slot] + srow(16 * RTO + lr, 4 * kt + lg));
-                    else
-                        to_pieces(x.qf[kt], qa);
-                    acc = mfma_split<2, NS>(mfr, qa, acc);
-                }
-                acc *= s_sc[c & 3][2 * CP + 16 * RTO + lr];  // o of token 16 RTO + lr
                 floatx4 urow[RT];
 #pragma unroll
                 for (int rt = 0; rt < RT; ++rt) urow[rt] = s_uf[pc][rt][l];
+                floatx4 qm = s_qm[pc][0][RTO][l];
+#pragma unroll
+                for (int sw = 1; sw < NSW; ++sw) qm += s_qm[pc][sw][RTO][l];
+                const float o = s_sc[c & (NSC - 1)][2 * CP + 16 * RTO + lr];  // o of token 16 RTO + lr
                 bf16x8 ufr[KTC][2];
                 rows_to_frags<RT, KTC>(urow, ufr);
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
                 for (int kt = 0; 2 * kt <= RTO; ++kt) {
                     const int pi = 2 * (tri_off(RTO) + kt);
                     const bf16x8 pf[2] = {s_pt[slot][pi][l], s_pt[slot][pi + 1][l]};
                     acc = mfma_split<2, 2>(ufr[kt], pf, acc);
                 }
+                acc += o * qm;
                 const auto r_o = make_rsrc(out + (tok0_of(c) * h_v + h) * (int64_t)D + cb * 16,
                                            (rows_of(c) - 1) * row_o + 64);
                 __builtin_amdgcn_raw_buffer_store_b128(
                     __builtin_bit_cast(u32x4, acc), r_o,
                     (int)((uint32_t)((16 * RTO + lr) * row_o) + (uint32_t)(lg * 16) + pad_if(live)), 0, 0);
             };
-            QSet A, B;
-            load_q(B, -2);
-            load_q(A, -1);
-            auto window = [&](QSet& x, int64_t c) {
-                __syncthreads();
-                do_output(x, c);
-                __builtin_amdgcn_sched_barrier(0);
-                load_q(x, c + 2);
-            };
 #pragma unroll 1
-            for (int64_t c = -2; c < cend; c += 2) {
-                window(B, c);      // window c uses the set of chunk c (loaded two windows ago)
-                window(A, c + 1);
+            for (int64_t c = -2; c < cend; ++c) {
+                __syncthreads();
+                do_output(c);
             }
             settle();
         };
@@ -1222,12 +1273,13 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
             constexpr int NKM = share(NKI);                       // K (and Q) row loads
             constexpr int NTM = share(2 * NTRI), NHM = share(2 * NHF), NPM = share(2 * NTRI);
             constexpr bool VST = HS == NSH - 1;                   // the V block and the scalars
-            // Register-staged inputs (fp32 or d = 16 K rows; fp32 V): the set of window c holds
-            // K rows of chunk c + 3 and the V block of chunk c + 2, loaded two windows earlier;
-            // two sets alternate.
+            // Register-staged inputs (fp32 or d = 16 K and Q rows; fp32 V): the set of window c
+            // holds the K rows and the V block of chunk c + 3 and the Q rows of chunk c + 2,
+            // loaded two windows earlier; two sets alternate.
             constexpr bool RK = !DQK, RV = !DV && VST;
             struct RSet {
                 u32x4 kr[RK && NKM > 0 ? NKM : 1];
+                u32x4 qr[RK && NKM > 0 ? NKM : 1];
                 u32x4 vr[RV ? NVI : 1];
             };
             // K or Q rows of chunk c straight into ring slot `dst`: load m covers rows
@@ -1250,18 +1302,22 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                 for (int m = 0; HS + NSH * m < n; ++m)
                     load_to_lds(r, dst[HS + NSH * m], (HS + NSH * m) * 1024 + l * 16);
             };
+            auto ld_rows = [&](const TIn* base, int64_t c, u32x4* dst) {
+                const auto r = qk_rsrc(base, clampc(c));
+#pragma unroll
+                for (int m = 0; m < NKM; ++m) {
+                    const int row = RPI * (HS + NSH * m) + l / LPR;
+                    dst[m] = __builtin_amdgcn_raw_buffer_load_b128(
+                        r, (int)((uint32_t)(row * row_qk) + (uint32_t)(16 * (l % LPR)) + pad_if(row < C)), 0, 0);
+                }
+            };
             auto ld_regs = [&](RSet& x, int64_t c) {  // the set of window c
                 if constexpr (RK) {
-                    const auto r = qk_rsrc(k, clampc(c + 3));
-#pragma unroll
-                    for (int m = 0; m < NKM; ++m) {
-                        const int row = RPI * (HS + NSH * m) + l / LPR;
-                        x.kr[m] = __builtin_amdgcn_raw_buffer_load_b128(
-                            r, (int)((uint32_t)(row * row_qk) + (uint32_t)(16 * (l % LPR)) + pad_if(row < C)), 0, 0);
-                    }
+                    ld_rows(k, c + 3, x.kr);
+                    ld_rows(q, c + 2, x.qr);
                 }
                 if constexpr (RV) {
-                    const int64_t c3 = clampc(c + 2);
+                    const int64_t c3 = clampc(c + 3);
                     const auto r_v = make_rsrc(v + (tok0_of(c3) * h_v + h) * (int64_t)D + cb * 16,
                                                (rows_of(c3) - 1) * row_v + 16 * ES);
 #pragma unroll
@@ -1272,31 +1328,33 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                     }
                 }
             };
-            // The register-staged inputs of window c (K of chunk c + 3, V of chunk c + 2).
-            auto st_regs = [&](const RSet& x, int64_t c) {
-                if constexpr (RK) {
-                    if (c + 3 >= 0 && c + 3 < nch) {
-                        char* dst = s_k[ring(c + 3)];
+            // Register-loaded rows into staged rows (fp32 split into hi and lo planes).
+            auto st_rows = [&](const u32x4* src, char* dst) {
 #pragma unroll
-                        for (int m = 0; m < NKM; ++m) {
-                            const int row = RPI * (HS + NSH * m) + l / LPR, g = l % LPR;
-                            if constexpr (ES == 2) {
-                                *reinterpret_cast<u32x4*>(dst + srow(row, g)) = x.kr[m];
-                            } else {
-                                const floatx4 y = __builtin_bit_cast(floatx4, x.kr[m]);
-                                uint32_t hi[2], lo[2];
-                                split2(y[0], y[1], &hi[0], &lo[0]);
-                                split2(y[2], y[3], &hi[1], &lo[1]);
-                                const int o = srow(row, g >> 1) + 8 * (g & 1);
-                                *reinterpret_cast<uint2*>(dst + o) = uint2{hi[0], hi[1]};
-                                *reinterpret_cast<uint2*>(dst + CP * ROWB + o) = uint2{lo[0], lo[1]};
-                            }
-                        }
+                for (int m = 0; m < NKM; ++m) {
+                    const int row = RPI * (HS + NSH * m) + l / LPR, g = l % LPR;
+                    if constexpr (ES == 2) {
+                        *reinterpret_cast<u32x4*>(dst + srow(row, g)) = src[m];
+                    } else {
+                        const floatx4 y = __builtin_bit_cast(floatx4, src[m]);
+                        uint32_t hi[2], lo[2];
+                        split2(y[0], y[1], &hi[0], &lo[0]);
+                        split2(y[2], y[3], &hi[1], &lo[1]);
+                        const int o = srow(row, g >> 1) + 8 * (g & 1);
+                        *reinterpret_cast<uint2*>(dst + o) = uint2{hi[0], hi[1]};
+                        *reinterpret_cast<uint2*>(dst + CP * ROWB + o) = uint2{lo[0], lo[1]};
                     }
                 }
+            };
+            // The register-staged inputs of window c (K and V of chunk c + 3, Q of chunk c + 2).
+            auto st_regs = [&](const RSet& x, int64_t c) {
+                if constexpr (RK) {
+                    if (c + 3 >= 0 && c + 3 < nch) st_rows(x.kr, s_k[ring(c + 3)]);
+                    if (c + 2 >= 0 && c + 2 < nch) st_rows(x.qr, s_q[qslot(c + 2)]);
+                }
                 if constexpr (RV) {
-                    if (c + 2 >= 0 && c + 2 < nch) {
-                        float* dst = reinterpret_cast<float*>(s_v[ring(c + 2)]);
+                    if (c + 3 >= 0 && c + 3 < nch) {
+                        float* dst = reinterpret_cast<float*>(s_v[ring(c + 3)]);
 #pragma unroll
                         for (int m = 0; m < NVI; ++m) {
                             const int t = TPI * m + l / LPT;  // < CP
@@ -1309,25 +1367,29 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
             };
             // The loads straight into LDS issued in window c (clamped chunks beyond the
             // sequence land in ring slots nobody reads any more).
-            auto issue = [&](int64_t c) {
-                if constexpr (DQK) dma_rows(k, c + 4, s_k[ring(c + 4)]);
-                dma_pieces(L.tt, G::TRI_BYTES, c + 3, s_tf[ring(c + 3)], 2 * NTRI);
+            // The chain's inputs of chunk j (T', the V block, the scalars).
+            auto dma_chain = [&](int64_t j) {
+                dma_pieces(L.tt, G::TRI_BYTES, j, s_tf[ring(j)], 2 * NTRI);
                 if constexpr (VST) {
-                    const int64_t c3 = clampc(c + 3);
+                    const int64_t jc = clampc(j);
                     if constexpr (DV) {
-                        const auto r_v = make_rsrc(v + (tok0_of(c3) * h_v + h) * (int64_t)D + cb * 16,
-                                                   (rows_of(c3) - 1) * row_v + 32);
+                        const auto r_v = make_rsrc(v + (tok0_of(jc) * h_v + h) * (int64_t)D + cb * 16,
+                                                   (rows_of(jc) - 1) * row_v + 32);
 #pragma unroll
                         for (int m = 0; m < NVI; ++m) {
                             const int t = TPI * m + l / 2;
-                            load_to_lds(r_v, s_v[ring(c + 3)] + m * 1024,
+                            load_to_lds(r_v, s_v[ring(j)] + m * 1024,
                                         (int)((uint32_t)(t * row_v) + (uint32_t)(16 * (l & 1)) + pad_if(t < C)));
                         }
                     }
-                    load_to_lds(sc_rsrc(c3), s_sc[(c + 3) & 3], 16 * l);
+                    load_to_lds(sc_rsrc(jc), s_sc[j & (NSC - 1)], 16 * l);
                 }
-                dma_pieces(L.hh, G::H_BYTES, c + 2, s_h[ring(c + 2)], 2 * NHF);
-                if constexpr (DQK) dma_rows(q, c + 2, s_q[ring(c + 2)]);
+            };
+            auto issue = [&](int64_t c) {
+                if constexpr (DQK) dma_rows(k, c + 4, s_k[ring(c + 4)]);
+                dma_chain(c + 4);
+                dma_pieces(L.hh, G::H_BYTES, c + 3, s_h[ring(c + 3)], 2 * NHF);
+                if constexpr (DQK) dma_rows(q, c + 3, s_q[qslot(c + 3)]);
                 dma_pieces(L.pt, G::TRI_BYTES, c + 2, s_pt[ring(c + 2)], 2 * NTRI);
             };
             // Vector memory operations one window issues: the loads straight into LDS, then
@@ -1335,36 +1397,26 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
             // have landed once no more than those issued after them (the register loads of
             // windows c - 1 and c and the straight loads of window c) are in flight.
             constexpr int NDMA = (DQK ? 2 * NKM : 0) + NTM + NHM + NPM + (VST ? (DV ? NVI : 0) + 1 : 0);
-            constexpr int NREG = (RK ? NKM : 0) + (RV ? NVI : 0);
+            constexpr int NREG = (RK ? 2 * NKM : 0) + (RV ? NVI : 0);
             constexpr int NVM = NDMA + 2 * NREG;
 
-            // Prologue: K rows of chunk 0 (and 1 when they load straight into LDS) and the
-            // chain's inputs of chunk 0 in place; window -2 writes the register-staged K rows of
-            // chunk 1 and V block of chunk 0.
+            // Prologue: K rows of chunk 0 (and of chunk 1 and Q rows of chunk 0 when they load
+            // straight into LDS), the chain's inputs of chunks 0 and 1 and H_0 in place; window
+            // -2 writes the register-staged K rows and V block of chunk 1 and Q rows of chunk 0.
             {
                 if constexpr (DQK) {
                     dma_rows(k, 0, s_k[ring(0)]);
                     dma_rows(k, 1, s_k[ring(1)]);
+                    dma_rows(q, 0, s_q[qslot(0)]);
                 } else {
                     RSet x0;
-                    ld_regs(x0, -3);  // K rows of chunk 0
+                    ld_regs(x0, -3);  // K rows and V block of chunk 0
                     settle();
                     st_regs(x0, -3);
                 }
-                dma_pieces(L.tt, G::TRI_BYTES, 0, s_tf[ring(0)], 2 * NTRI);
-                if constexpr (VST) {
-                    if constexpr (DV) {
-                        const auto r_v = make_rsrc(v + (tok0_of(0) * h_v + h) * (int64_t)D + cb * 16,
-                                                   (rows_of(0) - 1) * row_v + 32);
-#pragma unroll
-                        for (int m = 0; m < NVI; ++m) {
-                            const int t = TPI * m + l / 2;
-                            load_to_lds(r_v, s_v[ring(0)] + m * 1024,
-                                        (int)((uint32_t)(t * row_v) + (uint32_t)(16 * (l & 1)) + pad_if(t < C)));
-                        }
-                    }
-                    load_to_lds(sc_rsrc(0), s_sc[0], 16 * l);
-                }
+                dma_chain(0);
+                dma_chain(1);
+                dma_pieces(L.hh, G::H_BYTES, 0, s_h[ring(0)], 2 * NHF);
                 settle();
             }
             RSet A, B;
