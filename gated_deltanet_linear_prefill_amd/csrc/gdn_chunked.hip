@@ -347,7 +347,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     // The K and Q chunks (first phases) and the A / T matrices (later phases) share one
     // buffer; the Gram matrices live in registers in between.
     __shared__ __align__(16) char s_buf[U_LDS];
-    __shared__ float s_rk[CP], s_rq[CP], s_gam[CP], s_beta[CP];
+    __shared__ float s_rk[CP], s_rq[CP], s_gam[CP], s_beta[CP], s_sv[CP];
     __shared__ float s_x[4][16][17];  // per-wave 16x16 scratch
     auto s_kq = [&](int which, int part, int r, int f) -> __bf16& {
         return reinterpret_cast<__bf16*>(s_buf)[(((size_t)which * NS + part) * CP + r) * KS + f];
@@ -583,9 +583,11 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             if (tid < CP) {
                 const int i = tid;
                 const float Gi = expf(s_gam[i]);
+                const float si = s_rk[i] * expf(gam_c - s_gam[i]);
                 scp[i] = Gi * s_rk[i];
-                scp[CP + i] = s_rk[i] * expf(gam_c - s_gam[i]);
+                scp[CP + i] = si;
                 scp[2 * CP + i] = Gi * s_rq[i];
+                s_sv[i] = si;  // for H below
             }
             if (tid == 0) scp[3 * CP] = expf(gam_c);
         }
@@ -708,7 +710,6 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         //      have the same registers as the B fragments of diag(s) T'.
         if constexpr (G::WITH_H) {
             char* hh_base = ws + L.hh + (size_t)vh * G::H_BYTES;
-            const float gam_c = s_gam[CP - 1];
 #pragma unroll
             for (int i = 0; i < NIT; ++i) {
                 const int it = w + 4 * i;
@@ -726,7 +727,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 #pragma unroll
                         for (int q = 0; q < 8; ++q) {
                             const int m = tok_of(kt, lg, q);
-                            val[q] = (m >= j && m < C) ? s_rk[m] * expf(gam_c - s_gam[m]) * s_t[m][j] * s_beta[j] : 0.f;
+                            val[q] = (m >= j && m < C) ? s_sv[m] * s_t[m][j] * s_beta[j] : 0.f;
                         }
                         uint32_t hi[4], lo[4];
 #pragma unroll
@@ -861,6 +862,17 @@ __device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, void* lds,
 __device__ __forceinline__ void barrier_lds_only()
 {
     asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// Calls f(std::integral_constant<int, i>) for the wave-uniform index i in [I, N), so that the
+// callee is specialised for each index.
+template <int I, int N, typename F>
+__device__ __forceinline__ void dispatch_index(int i, F&& f)
+{
+    if constexpr (I < N) {
+        if (i == I) f(std::integral_constant<int, I>{});
+        else dispatch_index<I + 1, N>(i, f);
+    }
 }
 
 // Wait until at most n vector memory operations of this wave are in flight.
@@ -1438,16 +1450,12 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
             settle();
         };
 
-        static_assert(NHW == 4 && NOH >= 1 && NOH <= 2, "helper dispatch below");
-        switch (hw) {
-            case 0: output_helper(std::integral_constant<int, 0>{}); break;
-            case 1:
-                if constexpr (NOH > 1) output_helper(std::integral_constant<int, 1>{});
-                else staging_helper(std::integral_constant<int, 0>{});
-                break;
-            case 2: staging_helper(std::integral_constant<int, 2 - NOH>{}); break;
-            default: staging_helper(std::integral_constant<int, 3 - NOH>{}); break;
-        }
+        static_assert(NOH >= 1 && NSH >= 1, "helper roles");
+        dispatch_index<0, NHW>(hw, [&](auto ic) {
+            constexpr int i = decltype(ic)::value;
+            if constexpr (i < NOH) output_helper(ic);
+            else staging_helper(std::integral_constant<int, i - NOH>{});
+        });
     }
 }
 
