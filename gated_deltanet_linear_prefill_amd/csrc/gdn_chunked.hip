@@ -752,8 +752,8 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 }
 
 // =============================================================================== scan
-// Scan workgroup (chunks of up to 32 tokens): one "chain" wave, NSW "state" waves and four
-// "helper" waves.
+// Scan workgroup (chunks of up to 32 tokens): one "chain" wave, NSW "state" waves and
+// "helper" waves (one output helper per 16-token row tile, three staging helpers).
 //
 // The recursion the chain wave runs involves only X, the residuals V - diag(a) K M of a
 // chunk:
@@ -795,10 +795,10 @@ struct ScanGeo {
     static constexpr int ES = sizeof(TIn);
     static constexpr int NSW = G::KTD >= 2 ? 2 : 1;       // state waves
     static constexpr int KPS = G::KTD / NSW;               // d_k tiles per state wave
-    static constexpr int NHW = 4;                          // helper waves
-    static constexpr int THREADS = 64 * (1 + NSW + NHW);
     static constexpr int NOH = G::RT;                      // output helpers, one row tile each
-    static constexpr int NSH = NHW - NOH;                  // staging helpers
+    static constexpr int NSH = 3;                          // staging helpers
+    static constexpr int NHW = NOH + NSH;                  // helper waves
+    static constexpr int THREADS = 64 * (1 + NSW + NHW);
     static constexpr int NR = 3;                           // ring depth of the staged inputs
     // Staged rows: one bf16 piece of DP features in 16-byte granules; granule j of row r sits
     // at position j ^ swz(r).
@@ -1451,10 +1451,14 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
         };
 
         static_assert(NOH >= 1 && NSH >= 1, "helper roles");
+        // Output helpers come first and last, staging helpers in between: wave w runs on SIMD
+        // w mod 4, so with two output helpers they share one SIMD and each staging helper
+        // shares one with the chain or a state wave.
         dispatch_index<0, NHW>(hw, [&](auto ic) {
             constexpr int i = decltype(ic)::value;
-            if constexpr (i < NOH) output_helper(ic);
-            else staging_helper(std::integral_constant<int, i - NOH>{});
+            if constexpr (i == 0) output_helper(std::integral_constant<int, 0>{});
+            else if constexpr (NOH == 2 && i == NHW - 1) output_helper(std::integral_constant<int, 1>{});
+            else staging_helper(std::integral_constant<int, i - 1>{});
         });
     }
 }
