@@ -1181,6 +1181,9 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                 for (int kt = 0; kt < KTC; ++kt) acc = mfma_split<NS, 2>(kts[i][kt], wf[kt], acc);
                 macc[i] = acc;
             }
+            // K^T of chunk c + 2 replaces K^T of chunk c as soon as the update has issued, so
+            // the reads overlap the split and the products below.
+            read_kt(kts, ring(c2));
             split();  // the state entering chunk c + 1
             // (Q_{c+1} M_{c+1})^T over this wave's features, for the output helpers: the state
             // fragments serve as A operands and the Q row fragments as B operands, so each lane
@@ -1201,7 +1204,6 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
                 for (int kk = 0; kk < KPS; ++kk) acc = mfma_split<NS, 2>(ka[rt][kk], mf[kk], acc);
                 s_p[par(c2)][sw][rt][l] = scale * acc;
             }
-            read_kt(kts, ring(c2));  // K^T of chunk c + 2 replaces K^T of chunk c
         };
         // Chunk parity alternates between windows, and so do the two K^T register sets.
 #pragma unroll 1
