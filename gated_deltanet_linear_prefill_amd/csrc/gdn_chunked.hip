@@ -983,6 +983,56 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
         if constexpr (DV) return floatx4{(float)x[0], (float)x[1], (float)x[2], (float)x[3]};
         else return x;
     };
+    // Cache-line touches: one 128-byte line per lane of a chunk's inputs (its K and Q rows
+    // go round the workgroups of the QK head, its workspace blocks and V rows round the
+    // workgroups of the V head; lanes past this workgroup's share touch lane 0's line), so
+    // that the staging loads of the chunk find the lines in L2 rather than all waiting on the
+    // same misses. A lane's line moves by a fixed stride from chunk to chunk: touch_base and
+    // touch_step are its address in chunk 0 and that stride (for full chunks; a partial last
+    // chunk is touched as the chunk before it, or not at all when it is the only one).
+    // Lane-dependent choices blend precomputed values with masks (no branches).
+    uint64_t touch_base, touch_step;
+    {
+        constexpr int LPR128 = (D * ES + 127) / 128;  // cache lines per q/k/v row
+        constexpr int NCB = D / 16;
+        constexpr int TL = (int)(G::TRI_BYTES / 128), HL = (int)(G::H_BYTES / 128);
+        constexpr int SCL = (int)((G::SC_BYTES + 127) / 128) - 1;  // lines starting inside
+        constexpr int NWS = 2 * TL + HL + SCL;
+        constexpr int HALF = C * LPR128;
+        auto pick = [](bool cond, uint64_t x, uint64_t y) {
+            const uint64_t m = 0 - (uint64_t)cond;
+            return (x & m) | (y & ~m);
+        };
+        const int grp = h_v / h_qk, nbq = grp * NCB, iq = (h % grp) * NCB + cb;
+        const int nq_mine = (2 * HALF - iq + nbq - 1) / nbq;
+        const int nv_mine = (NWS + HALF - cb + NCB - 1) / NCB;
+        const int li = l < nq_mine + nv_mine ? l : 0;
+        const bool isq = li < nq_mine;
+        const int lq = iq + nbq * li, rq = lq < HALF ? lq : lq - HALF;
+        const uint64_t q0 = pick(lq < HALF, (uint64_t)k, (uint64_t)q) +
+                            (uint64_t)(((seq * T + rq / LPR128) * h_qk + hq) * (int64_t)D * ES + 128 * (rq % LPR128));
+        const uint64_t qs = (uint64_t)C * h_qk * D * ES;
+        const int lv = isq ? 0 : cb + NCB * (li - nq_mine);
+        const uint64_t vh0 = (uint64_t)(seq * nch * h_v + h), wsb = (uint64_t)ws;
+        const uint64_t w_tt = wsb + L.tt + vh0 * G::TRI_BYTES + 128 * lv;
+        const uint64_t w_pt = wsb + L.pt + vh0 * G::TRI_BYTES + 128 * (lv - TL);
+        const uint64_t w_hh = wsb + L.hh + vh0 * G::H_BYTES + 128 * (lv - 2 * TL);
+        const uint64_t w_sc = wsb + L.sc + vh0 * G::SC_BYTES + 128 * (lv - 2 * TL - HL);
+        uint64_t w0 = pick(lv < 2 * TL + HL, w_hh, w_sc);
+        uint64_t ws_step = pick(lv < 2 * TL + HL, (uint64_t)h_v * G::H_BYTES, (uint64_t)h_v * G::SC_BYTES);
+        w0 = pick(lv < 2 * TL, w_pt, w0);
+        w0 = pick(lv < TL, w_tt, w0);
+        ws_step = pick(lv < 2 * TL, (uint64_t)h_v * G::TRI_BYTES, ws_step);
+        const int rv = lv - NWS;
+        const uint64_t v0 = (uint64_t)v + (uint64_t)(((seq * T + rv / LPR128) * h_v + h) * (int64_t)D * ES + 128 * (rv % LPR128));
+        const uint64_t vs = (uint64_t)C * h_v * D * ES;
+        touch_base = pick(isq, q0, pick(lv < NWS, w0, v0));
+        touch_step = pick(isq, qs, pick(lv < NWS, ws_step, vs));
+    }
+    auto touch_ptr = [&](int64_t j) -> const uint32_t* {
+        const int64_t jj = rows_of(j) == C ? j : j - 1;
+        return reinterpret_cast<const uint32_t*>(jj >= 0 ? touch_base + (uint64_t)jj * touch_step : (uint64_t)ws);
+    };
 
     if (w == 0) {
         // ======================================================= chain wave
@@ -1009,7 +1059,7 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
         // barrier: slots of chunks that do not exist are read too (any contents do), and their
         // products land in exchange buffers that nobody reads. X of such a window is set to
         // zero, which keeps H X of the first window zero.
-        auto window = [&](int64_t c, const CIn& cur, CIn& nxt) {
+        auto window = [&](int64_t c, const CIn& cur, CIn& nxt, uint32_t& touched) {
             __syncthreads();
             const int pn = par(c + 1);
             floatx4 z[RT];
@@ -1069,14 +1119,20 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
             for (int kt = 0; kt < KTC; ++kt)
 #pragma unroll
                 for (int p = 0; p < 2; ++p) s_wf[pn][kt][p][l] = wf[kt][p];
+            // Touch the cache lines of chunk c + 8 (the staging loads of a chunk start four
+            // windows before its use), after waiting for the touch of window c - 2: this wave
+            // issues no other vector memory operations, so the wait counts exactly.
+            asm volatile("" ::"v"(touched));
+            touched = *(const __attribute__((address_space(1))) uint32_t*)touch_ptr(clampc(c + 8));
         };
         // Chunk parity alternates between windows, and so do the two input sets: window c
         // uses the set of chunk c + 1 and fills that of chunk c + 2.
         CIn A, B;
+        uint32_t ta = 0, tb = 0;
 #pragma unroll 1
         for (int64_t c = -2; c < cend; c += 2) {
-            window(c, B, A);
-            window(c + 1, A, B);
+            window(c, B, A, ta);
+            window(c + 1, A, B, tb);
         }
     } else if (w <= NSW) {
         // ======================================================= state wave sw
