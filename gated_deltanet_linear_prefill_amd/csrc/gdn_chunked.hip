@@ -321,8 +321,10 @@ __device__ __forceinline__ void tri_frag(int fi, int& rt, int& kt)
     kt = fi - tri_off(rt);
 }
 
+// Four waves per SIMD (registers for four resident workgroups per CU): the kernel is bound by
+// latency, and the register allocation fits without spills.
 template <int D, int C, typename TIn>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ g,
                   const float* __restrict__ beta, char* __restrict__ ws, ChunkWs L, int64_t T,
                   int h_qk, int h_v, float eps)
@@ -334,26 +336,30 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     constexpr int NB = RT;        // 16x16 diagonal blocks of T
     constexpr int KS = DP + 8;    // LDS row stride of the K / Q pieces (bf16)
     constexpr int CS = CP + 4;    // LDS row stride of the CP x CP fp32 matrices
+    // The V heads of the QK head are taken NHP at a time, NWH waves each: for chunks of up to
+    // 32 tokens two heads side by side (the diagonal solve needs one wave, the other writes
+    // Ptil meanwhile), longer chunks one head with all four waves.
+    constexpr int NWH = C <= 32 ? 2 : 4;           // waves per V head
+    constexpr int NHP = 4 / NWH;                   // V heads per pass
     constexpr size_t KQ_LDS = (size_t)2 * NS * CP * KS * 2;
-    constexpr size_t AT_LDS = (size_t)2 * CP * CS * 4;
+    constexpr size_t AT_LDS = (size_t)NHP * 2 * CP * CS * 4;
     constexpr size_t U_LDS = KQ_LDS > AT_LDS ? KQ_LDS : AT_LDS;
-    // Waves that solve the diagonal blocks (one lane per column); the others write Ptil
-    // meanwhile (all waves when the diagonal blocks take all four).
+    // Waves of a head that solve its diagonal blocks (one lane per column); the others write
+    // Ptil meanwhile (all of the head's waves when the diagonal blocks take them all).
     constexpr int NBW = (NB * 16 + 63) / 64;
-    constexpr int PW0 = NBW < 4 ? NBW : 0;        // first Ptil wave
-    constexpr int NPW = 4 - PW0;                  // Ptil waves
+    constexpr int PW0 = NBW < NWH ? NBW : 0;      // first Ptil wave of a head
+    constexpr int NPW = NWH - PW0;                // Ptil waves per head
     constexpr int NFW = (NTRI + NPW - 1) / NPW;   // Ptil fragments per Ptil wave
 
     // The K and Q chunks (first phases) and the A / T matrices (later phases) share one
     // buffer; the Gram matrices live in registers in between.
     __shared__ __align__(16) char s_buf[U_LDS];
-    __shared__ float s_rk[CP], s_rq[CP], s_gam[CP], s_beta[CP], s_sv[CP];
+    __shared__ float s_rk[CP], s_rq[CP];
+    __shared__ float s_gam[NHP][CP], s_beta[NHP][CP], s_sv[NHP][CP];
     __shared__ float s_x[4][16][17];  // per-wave 16x16 scratch
     auto s_kq = [&](int which, int part, int r, int f) -> __bf16& {
         return reinterpret_cast<__bf16*>(s_buf)[(((size_t)which * NS + part) * CP + r) * KS + f];
     };
-    float(*s_a)[CS] = reinterpret_cast<float(*)[CS]>(s_buf);
-    float(*s_t)[CS] = reinterpret_cast<float(*)[CS]>(s_buf + (size_t)CP * CS * 4);
 
     const int64_t nch = L.nch;
     const int hq = (int)(blockIdx.x % h_qk);
@@ -363,11 +369,18 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     const int Cr = (int)((T - c0) < C ? (T - c0) : C);
     const int tid = threadIdx.x, l = tid & 63, lr = l & 15, lg = l >> 4;
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
+    const int pm = w / NWH, wl = w % NWH;  // the head slot of this wave, its index there
+    const int pt = tid - 64 * NWH * pm;    // thread index within the head slot
     const int grp = h_v / h_qk;
     const int64_t tok0 = seq * T + c0;  // flattened token index of the chunk's first token
+    float(*s_a)[CS] = reinterpret_cast<float(*)[CS]>(s_buf + (size_t)pm * 2 * CP * CS * 4);
+    float(*s_t)[CS] = reinterpret_cast<float(*)[CS]>(s_buf + ((size_t)pm * 2 + 1) * CP * CS * 4);
+    // V head of slot pm in the pass starting at head g0 (a slot past the QK head's V heads
+    // repeats the pass's first head: the same values are computed and written twice)
+    auto head_of = [&](int g0) { return hq * grp + (g0 + pm < grp ? g0 + pm : g0); };
 
-    // Gate and write strength of one V head for this chunk (wave 0; E tokens per lane),
-    // loaded one V head ahead of their use.
+    // Gate and write strength of one V head for this chunk (the first wave of each head
+    // slot; E tokens per lane), loaded one pass ahead of their use.
     constexpr int E = (CP + 63) / 64;
     float gv[E], bv[E];
     auto load_gb = [&](int hv) {
@@ -381,7 +394,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             bv[e] = ok ? b_in : 0.f;
         }
     };
-    if (w == 0) load_gb(hq * grp);
+    if (wl == 0) load_gb(head_of(0));
 
     // ---- phase 0: inverse norms of the q and k rows; both chunks into LDS as bf16 pieces
     //      (rows past the chunk and padded features are zero). The loads of a batch of
@@ -450,7 +463,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     //    lane holds in the two tiles are the eight k slots (permuted token order) of the
     //    B fragment of Ptil^T the scan kernel multiplies U^T with.
     constexpr int NTL = RT * (RT + 1) / 2;
-    constexpr int NTW = (NTL + 3) / 4;   // K K^T tiles per wave
+    constexpr int NTW = (NTL + NWH - 1) / NWH;  // K K^T tiles per wave (each head slot has all)
     constexpr int NPG = NS == 1 ? 1 : 3; // split passes of a Gram product
     // Gram tile: rows of chunk `wa` (0 = K, 1 = Q) tile ta against rows of chunk `wb` tile tb.
     auto gram = [&](int wa, int ta, int wb, int tb) {
@@ -476,7 +489,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
         gk[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-        const int ti = w + 4 * i;
+        const int ti = wl + NWH * i;
         if (ti < NTL) {
             int rt, ct;
             tri_tile(ti, rt, ct);
@@ -487,8 +500,8 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 #pragma unroll
     for (int i = 0; i < NFW; ++i) {
         gp[i][0] = gp[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-        const int fi = w - PW0 + NPW * i;
-        if (w >= PW0 && fi < NTRI) {
+        const int fi = wl - PW0 + NPW * i;
+        if (wl >= PW0 && fi < NTRI) {
             int rt, kt;
             tri_frag(fi, rt, kt);
             gp[i][0] = gram(0, 2 * kt, 1, rt);
@@ -496,10 +509,11 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         }
     }
     // K_c K_{c+1}^T against the next chunk's keys (zero past the sequence), for
-    // H = K_{c+1} K_c^T diag(s) T': wave w takes the rows of H in row tiles it = w, w + 4, ...
+    // H = K_{c+1} K_c^T diag(s) T': wave wl of a head slot takes the rows of H in row tiles
+    // it = wl, wl + NWH, ...
     // The tile pairs over K_c's tokens m are kept as B fragments (k slots m in the permuted
     // token order, columns the tokens i of chunk c + 1).
-    constexpr int NIT = G::WITH_H ? (RT + 3) / 4 : 0;
+    constexpr int NIT = G::WITH_H ? (RT + NWH - 1) / NWH : 0;
     bf16x8 gnb[NIT > 0 ? NIT : 1][KTC][2];
     if constexpr (G::WITH_H) {
         const int64_t rows_next = T - (c0 + C) < C ? T - (c0 + C) : (int64_t)C;  // may be <= 0
@@ -507,7 +521,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         const auto r = make_rsrc(rows_next > 0 ? kn : k, rows_next > 0 ? (rows_next - 1) * h_qk * D * (int64_t)sizeof(TIn) + D * (int64_t)sizeof(TIn) : 0);
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
-            const int it = w + 4 * i;
+            const int it = wl + NWH * i;
             floatx4 gt[2 * KTC];
 #pragma unroll
             for (int mt = 0; mt < 2 * KTC; ++mt) gt[mt] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -543,13 +557,13 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     }
     __syncthreads();  // the K / Q buffer becomes A / T below
 
-    for (int gi = 0; gi < grp; ++gi) {
-        const int hv = hq * grp + gi;
+    for (int g0 = 0; g0 < grp; g0 += NHP) {
+        const int hv = head_of(g0);
         const int64_t vh = (seq * nch + c) * h_v + hv;
 
-        // ---- phase 3: gate prefix sums gamma (wave 0), write strengths; the next V head's
-        //      gate and write strength are loaded meanwhile
-        if (w == 0) {
+        // ---- phase 3: gate prefix sums gamma (first wave of the slot), write strengths; the
+        //      next pass's gate and write strength are loaded meanwhile
+        if (wl == 0) {
             float run = 0.f, gs[E];
 #pragma unroll
             for (int e = 0; e < E; ++e) {
@@ -567,11 +581,11 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             for (int e = 0; e < E; ++e) {
                 const int i = l * E + e;
                 if (i < CP) {
-                    s_gam[i] = gs[e] + excl;
-                    s_beta[i] = bv[e];
+                    s_gam[pm][i] = gs[e] + excl;
+                    s_beta[pm][i] = bv[e];
                 }
             }
-            if (gi + 1 < grp) load_gb(hv + 1);
+            if (g0 + NHP < grp) load_gb(head_of(g0 + NHP));
         }
         __syncthreads();
 
@@ -579,23 +593,23 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         //      and Gamma_C (padded tokens carry r_k = r_q = 0, so their scalars are zero)
         {
             float* scp = reinterpret_cast<float*>(ws + L.sc + (size_t)vh * G::SC_BYTES);
-            const float gam_c = s_gam[CP - 1];  // padded tokens add g = 0
-            if (tid < CP) {
-                const int i = tid;
-                const float Gi = expf(s_gam[i]);
-                const float si = s_rk[i] * expf(gam_c - s_gam[i]);
+            const float gam_c = s_gam[pm][CP - 1];  // padded tokens add g = 0
+            if (pt < CP) {
+                const int i = pt;
+                const float Gi = expf(s_gam[pm][i]);
+                const float si = s_rk[i] * expf(gam_c - s_gam[pm][i]);
                 scp[i] = Gi * s_rk[i];
                 scp[CP + i] = si;
                 scp[2 * CP + i] = Gi * s_rq[i];
-                s_sv[i] = si;  // for H below
+                s_sv[pm][i] = si;  // for H below
             }
-            if (tid == 0) scp[3 * CP] = expf(gam_c);
+            if (pt == 0) scp[3 * CP] = expf(gam_c);
         }
 
         // ---- phase 4: A = strictly lower (beta_r exp(gamma_r - gamma_s) r_k,r r_k,s k_r . k_s)
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
-            const int ti = w + 4 * i;
+            const int ti = wl + NWH * i;
             if (ti < NTL) {
                 int rt, ct;
                 tri_tile(ti, rt, ct);
@@ -603,7 +617,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
                 for (int e = 0; e < 4; ++e) {
                     const int r = 16 * rt + 4 * lg + e, s = 16 * ct + lr;
                     float a = 0.f;
-                    if (s < r) a = s_beta[r] * __expf(s_gam[r] - s_gam[s]) * s_rk[r] * s_rk[s] * gk[i][e];
+                    if (s < r) a = s_beta[pm][r] * __expf(s_gam[pm][r] - s_gam[pm][s]) * s_rk[r] * s_rk[s] * gk[i][e];
                     s_a[r][s] = a;
                 }
             }
@@ -613,8 +627,8 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         // ---- phase 5: diagonal 16x16 blocks of T by forward substitution, one lane per
         //      column: T[r][s] = delta_rs - sum_{m<r} A[r][m] T[m][s]. The other waves
         //      write Ptil^T meanwhile.
-        if (tid < NB * 16) {
-            const int b = tid >> 4, s = tid & 15;
+        if (pt < NB * 16) {
+            const int b = pt >> 4, s = pt & 15;
             float t[16];
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
@@ -628,11 +642,11 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         }
         // Ptil^T B fragment (rt, kt), hi and lo: slot 4 h + e holds
         // Ptil[16 rt + lr][16 (2 kt + h) + 4 lg + e], which is zero above the diagonal.
-        if (w >= PW0) {
+        if (wl >= PW0) {
             char* pt_base = ws + L.pt + (size_t)vh * G::TRI_BYTES;
 #pragma unroll
             for (int i = 0; i < NFW; ++i) {
-                const int fi = w - PW0 + NPW * i;
+                const int fi = wl - PW0 + NPW * i;
                 if (fi >= NTRI) continue;
                 int rt, kt;
                 tri_frag(fi, rt, kt);
@@ -644,7 +658,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
                     for (int e = 0; e < 4; ++e) {
                         const int s = 32 * kt + 16 * h + 4 * lg + e;
                         float p = 0.f;
-                        if (s <= r) p = __expf(s_gam[r] - s_gam[s]) * s_rq[r] * s_rk[s] * gp[i][h][e];
+                        if (s <= r) p = __expf(s_gam[pm][r] - s_gam[pm][s]) * s_rq[r] * s_rk[s] * gp[i][h][e];
                         val[4 * h + e] = p;
                     }
                 uint32_t hi[4], lo[4];
@@ -659,7 +673,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         // ---- phase 6: off-diagonal blocks, block row by block row:
         //      T_ij = -T_ii (sum_{m=j}^{i-1} A_im T_mj)   (fp32 MFMA)
         for (int i = 1; i < NB; ++i) {
-            for (int j = w; j < i; j += 4) {
+            for (int j = wl; j < i; j += NWH) {
                 floatx4 x = {0.f, 0.f, 0.f, 0.f};
                 for (int m = j; m < i; ++m) {
 #pragma unroll
@@ -685,7 +699,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         //      order in k
         {
             char* tt_base = ws + L.tt + (size_t)vh * G::TRI_BYTES;
-            for (int fi = w; fi < NTRI; fi += 4) {
+            for (int fi = wl; fi < NTRI; fi += NWH) {
                 int rt, kt;
                 tri_frag(fi, rt, kt);
                 const int r = 16 * rt + lr;
@@ -693,7 +707,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int s = tok_of(kt, lg, j);
-                    val[j] = s <= r ? s_t[r][s] * s_beta[s] : 0.f;
+                    val[j] = s <= r ? s_t[r][s] * s_beta[pm][s] : 0.f;
                 }
                 uint32_t hi[4], lo[4];
 #pragma unroll
@@ -712,7 +726,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             char* hh_base = ws + L.hh + (size_t)vh * G::H_BYTES;
 #pragma unroll
             for (int i = 0; i < NIT; ++i) {
-                const int it = w + 4 * i;
+                const int it = wl + NWH * i;
                 if (it >= RT) continue;
                 floatx4 ht[2 * KTC];  // H^T tiles (jt, it)
 #pragma unroll
@@ -727,7 +741,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 #pragma unroll
                         for (int q = 0; q < 8; ++q) {
                             const int m = tok_of(kt, lg, q);
-                            val[q] = (m >= j && m < C) ? s_sv[m] * s_t[m][j] * s_beta[j] : 0.f;
+                            val[q] = (m >= j && m < C) ? s_sv[pm][m] * s_t[m][j] * s_beta[pm][j] : 0.f;
                         }
                         uint32_t hi[4], lo[4];
 #pragma unroll
