@@ -396,6 +396,27 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     };
     if (wl == 0) load_gb(head_of(0));
 
+    // The next chunk's key rows for H (see below), loaded now so that they arrive while the
+    // chunk's own rows are loaded and normalised.
+    constexpr int NIT = G::WITH_H ? (RT + NWH - 1) / NWH : 0;
+    using Raw = typename RawFrag<TIn>::type;
+    Raw bnr[NIT > 0 ? NIT : 1][KTD];
+    if constexpr (G::WITH_H) {
+        const int64_t rows_next = T - (c0 + C) < C ? T - (c0 + C) : (int64_t)C;  // may be <= 0
+        const TIn* kn = k + ((tok0 + C) * h_qk + hq) * (int64_t)D;
+        const auto r = make_rsrc(rows_next > 0 ? kn : k, rows_next > 0 ? (rows_next - 1) * h_qk * D * (int64_t)sizeof(TIn) + D * (int64_t)sizeof(TIn) : 0);
+#pragma unroll
+        for (int i = 0; i < NIT; ++i) {
+            const int it = wl + NWH * i;
+#pragma unroll
+            for (int kt = 0; kt < KTD; ++kt) {
+                const int f = 32 * kt + 8 * lg;
+                const int off = ((16 * it + lr) * h_qk * D + f) * (int)sizeof(TIn);
+                bnr[i][kt] = buf_raw_frag<TIn>(r, f < D && it < RT ? off : (int)OOR);
+            }
+        }
+    }
+
     // ---- phase 0: inverse norms of the q and k rows; both chunks into LDS as bf16 pieces
     //      (rows past the chunk and padded features are zero). The loads of a batch of
     //      rows are all issued before any of them is used.
@@ -513,12 +534,8 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     // it = wl, wl + NWH, ...
     // The tile pairs over K_c's tokens m are kept as B fragments (k slots m in the permuted
     // token order, columns the tokens i of chunk c + 1).
-    constexpr int NIT = G::WITH_H ? (RT + NWH - 1) / NWH : 0;
     bf16x8 gnb[NIT > 0 ? NIT : 1][KTC][2];
     if constexpr (G::WITH_H) {
-        const int64_t rows_next = T - (c0 + C) < C ? T - (c0 + C) : (int64_t)C;  // may be <= 0
-        const TIn* kn = k + ((tok0 + C) * h_qk + hq) * (int64_t)D;
-        const auto r = make_rsrc(rows_next > 0 ? kn : k, rows_next > 0 ? (rows_next - 1) * h_qk * D * (int64_t)sizeof(TIn) + D * (int64_t)sizeof(TIn) : 0);
 #pragma unroll
         for (int i = 0; i < NIT; ++i) {
             const int it = wl + NWH * i;
@@ -528,11 +545,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             if (it < RT) {
                 bf16x8 bn[KTD][NS];
 #pragma unroll
-                for (int kt = 0; kt < KTD; ++kt) {
-                    const int f = 32 * kt + 8 * lg;
-                    const int off = ((16 * it + lr) * h_qk * D + f) * (int)sizeof(TIn);
-                    to_pieces(buf_raw_frag<TIn>(r, f < D ? off : (int)OOR), bn[kt]);
-                }
+                for (int kt = 0; kt < KTD; ++kt) to_pieces(bnr[i][kt], bn[kt]);
 #pragma unroll
                 for (int mt = 0; mt < RT; ++mt) {
                     floatx4 acc[NPG];
