@@ -12,8 +12,10 @@ One step is the whole hot path once:
 `decode_us_per_token` is the decode part. Inputs are resident in HBM before timing starts.
 
 The JSON line also carries decode_cold_us_per_token (the decode step with its states out of
-the MALL) and hbm_copy_GBps (what a 1 GiB device copy reaches; the achievable HBM rate next to
-the 8 TB/s peak), both measured after the timed region, and
+the MALL), decode_per_layer_{eager,graph}_us_per_token (the same token as 30 dependent
+per-layer steps of one sequence each, called one by one or replayed as one recorded HIP
+graph) and hbm_copy_GBps (what a 1 GiB device copy reaches; the achievable HBM rate next to
+the 8 TB/s peak), all measured after the timed region, and
   roofline:     the prefill call (its two kernels) against HBM: algorithmic bytes per call
                 (q, k, v, g, beta read once, out and state_out written once) divided by the
                 mean call duration from HIP events around every timed call, on the stream
@@ -109,6 +111,33 @@ def reference_rates(gdn, dec, dec_out, dev):
     torch.cuda.synchronize()
     cold_us = evs[0].elapsed_time(evs[30]) / 30 * 1e3
     del stacks, calls
+
+    # The same decode token as 30 dependent per-layer steps (one sequence each, the layer
+    # order of a real model): called one by one, and recorded once as a HIP graph.
+    st = torch.zeros(LAYERS, H_V, D, D, device=dev)
+    per = {key: [dec[key][l:l + 1] for l in range(LAYERS)] for key in ("q", "k", "v", "g", "beta")}
+    outs = [dec_out[l:l + 1] for l in range(LAYERS)]
+    sts = [st[l:l + 1] for l in range(LAYERS)]
+    eager = [gdn.bind_decode_step(per["q"][l], per["k"][l], per["v"][l], per["g"][l],
+                                  per["beta"][l], sts[l], outs[l], sts[l]) for l in range(LAYERS)]
+    graph = gdn.DecodeGraph(per["q"], per["k"], per["v"], per["g"], per["beta"], sts, outs,
+                            stream=torch.cuda.Stream())
+
+    def timed(fn, reps=20):
+        fn()
+        torch.cuda.synchronize()
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for _ in range(reps):
+            fn()
+        e0.record()
+        torch.cuda.synchronize()
+        return s0.elapsed_time(e0) / reps * 1e3
+
+    layers_eager_us = timed(lambda: [c() for c in eager])
+    layers_graph_us = timed(graph.launch)
+    graph.close()
+    del st, eager
     a = torch.empty(1 << 28, device=dev)
     b = torch.empty_like(a)
     b.copy_(a)
@@ -119,7 +148,8 @@ def reference_rates(gdn, dec, dec_out, dev):
     e.record()
     torch.cuda.synchronize()
     copy_gbs = 2 * a.numel() * 4 * 5 / (s.elapsed_time(e) * 1e-3) / 1e9
-    return {"decode_cold_us": cold_us, "copy_GBps": copy_gbs}
+    return {"decode_cold_us": cold_us, "copy_GBps": copy_gbs,
+            "layers_eager_us": layers_eager_us, "layers_graph_us": layers_graph_us}
 
 
 def cpu_baseline():
@@ -253,6 +283,8 @@ def main():
         "prefill_us_per_layer": mean_call_s * 1e6,
         "decode_cold_us_per_token": extra["decode_cold_us"],
         "decode_cold_GBps": decode_bytes() / (extra["decode_cold_us"] * 1e-6) / 1e9,
+        "decode_per_layer_eager_us_per_token": extra["layers_eager_us"],
+        "decode_per_layer_graph_us_per_token": extra["layers_graph_us"],
         "hbm_copy_GBps": extra["copy_GBps"],
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,

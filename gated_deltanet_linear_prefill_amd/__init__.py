@@ -18,7 +18,7 @@ __all__ = [
     "GdnError", "gdn_abi_version", "gdn_status_str", "gdn_workspace_bytes",
     "gdn_prefill_chunked", "gdn_prefill_scan", "gdn_decode_step", "gdn_prefill_choose",
     "gdn_prefill", "gdn_prefill_workspace_bytes", "library_path", "Dims", "BoundCall",
-    "bind_prefill_chunked", "bind_prefill_scan", "bind_decode_step",
+    "bind_prefill_chunked", "bind_prefill_scan", "bind_decode_step", "DecodeGraph",
 ]
 
 GDN_F32, GDN_BF16 = 0, 1
@@ -64,6 +64,9 @@ def _load():
         "gdn_prefill_choose": (ctypes.c_int, [D, ctypes.POINTER(i32)]),
         "gdn_prefill_workspace_bytes": (sz, [D]),
         "gdn_prefill": (ctypes.c_int, [D] + [P] * 9 + [sz, P]),
+        "gdn_decode_graph_create": (ctypes.c_int, [D, i32] + [ctypes.POINTER(P)] * 7 + [P, ctypes.POINTER(P)]),
+        "gdn_graph_launch": (ctypes.c_int, [P, P]),
+        "gdn_graph_destroy": (ctypes.c_int, [P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -251,3 +254,48 @@ def bind_decode_step(q, k, v, g, beta, state_in, out, state_out, *, l2_eps=1e-6,
             _ptr(out), _ptr(state_out), _stream(q.device, stream))
     return BoundCall(_load().gdn_decode_step, args, "gdn_decode_step",
                      (dims, q, k, v, g, beta, state_in, out, state_out))
+
+
+class DecodeGraph:
+    """gdn_decode_graph_create / gdn_graph_launch / gdn_graph_destroy: one decode token
+    through len(q) stacked layers as dependent per-layer steps, recorded once as a HIP
+    graph. Each layer's inputs are [n, 1, ...] tensors as for gdn_decode_step; its state
+    (state[i]) is updated in place and its output written to out[i] (allocated when not
+    given). The tensors are referenced by address: write each token's inputs into them in
+    place and call launch(). `stream` (a non-default torch stream) is used only to record.
+    """
+
+    def __init__(self, q, k, v, g, beta, state, out=None, *, l2_eps=1e-6, stream):
+        layers = len(q)
+        if not all(len(x) == layers for x in (k, v, g, beta, state)):
+            raise ValueError("one tensor per layer in every list")
+        if out is None:
+            out = [torch.empty(v[i].shape, device=v[i].device, dtype=torch.float32)
+                   for i in range(layers)]
+        for i in range(layers):
+            _prepare(q[i], k[i], v[i], g[i], beta[i], state[i], out[i], state[i], l2_eps)
+        self.tensors = (list(q), list(k), list(v), list(g), list(beta), list(state), list(out))
+        self.out = self.tensors[6]
+        dims = _dims_of(q[0], v[0], l2_eps) if layers else make_dims(0, 1, 1, 1, 16)
+        arr = lambda xs: (ctypes.c_void_p * max(1, layers))(*[x.data_ptr() for x in xs])
+        self._arrays = [arr(xs) for xs in self.tensors]
+        handle = ctypes.c_void_p()
+        _check(_load().gdn_decode_graph_create(
+            ctypes.byref(dims), layers, *[ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p)) for a in self._arrays],
+            ctypes.c_void_p(stream.cuda_stream), ctypes.byref(handle)), "gdn_decode_graph_create")
+        self._handle = handle
+
+    def launch(self, stream=None):
+        dev = self.tensors[0][0].device if self.tensors[0] else None
+        _check(_load().gdn_graph_launch(self._handle, _stream(dev, stream)), "gdn_graph_launch")
+
+    def close(self):
+        if getattr(self, "_handle", None) is not None and self._handle.value:
+            _check(_load().gdn_graph_destroy(self._handle), "gdn_graph_destroy")
+        self._handle = None
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass

@@ -3,10 +3,16 @@
 //
 // Every check runs on the host before the first HIP call, so each error path is testable
 // without a GPU, and on error nothing is enqueued.
+#include <vector>
 #include <math.h>
 #include <string.h>
 
 #include "gdn_internal.hpp"
+
+// A recorded decode graph: the instantiated HIP graph it replays.
+struct gdn_graph_rec {
+    hipGraphExec_t exec;
+};
 
 namespace gdn {
 namespace {
@@ -258,6 +264,63 @@ gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, cons
     c.stream = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     return finish(launch_decode(c));
+}
+
+gdn_status gdn_decode_graph_create(const gdn_dims* d, int32_t layers, const void* const* q,
+                                   const void* const* k, const void* const* v,
+                                   const float* const* g, const float* const* beta,
+                                   float* const* state, float* const* out, void* stream,
+                                   gdn_graph* graph)
+{
+    if (!graph) return GDN_ERR_NULL;
+    *graph = nullptr;
+    if (!d || !q || !k || !v || !g || !beta || !state || !out || !stream) return GDN_ERR_NULL;
+    if (layers < 0) return GDN_ERR_SHAPE;
+    // Every layer is validated before anything is recorded.
+    std::vector<Call> calls((size_t)layers);
+    for (int32_t i = 0; i < layers; ++i) {
+        gdn_status st = validate(d, -1, q[i], k[i], v[i], g[i], beta[i], state[i], out[i],
+                                 state[i], nullptr, 0, &calls[(size_t)i]);
+        if (st != GDN_OK) return st;
+        calls[(size_t)i].stream = static_cast<hipStream_t>(stream);
+    }
+    (void)hipGetLastError();
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    if (hipStreamBeginCapture(s, hipStreamCaptureModeThreadLocal) != hipSuccess) return GDN_ERR_HIP;
+    hipError_t launch_err = hipSuccess;
+    for (const Call& c : calls)
+        if (c.n > 0 && launch_err == hipSuccess) launch_err = launch_decode(c);
+    hipGraph_t g_rec = nullptr;
+    const hipError_t end_err = hipStreamEndCapture(s, &g_rec);
+    if (launch_err != hipSuccess || end_err != hipSuccess || !g_rec) {
+        if (g_rec) (void)hipGraphDestroy(g_rec);
+        (void)hipGetLastError();
+        return GDN_ERR_HIP;
+    }
+    hipGraphExec_t exec = nullptr;
+    const hipError_t inst_err = hipGraphInstantiate(&exec, g_rec, nullptr, nullptr, 0);
+    (void)hipGraphDestroy(g_rec);
+    if (inst_err != hipSuccess || !exec) {
+        (void)hipGetLastError();
+        return GDN_ERR_HIP;
+    }
+    *graph = new gdn_graph_rec{exec};
+    return GDN_OK;
+}
+
+gdn_status gdn_graph_launch(gdn_graph graph, void* stream)
+{
+    if (!graph) return GDN_ERR_NULL;
+    (void)hipGetLastError();
+    return finish(hipGraphLaunch(graph->exec, static_cast<hipStream_t>(stream)));
+}
+
+gdn_status gdn_graph_destroy(gdn_graph graph)
+{
+    if (!graph) return GDN_OK;
+    const hipError_t e = hipGraphExecDestroy(graph->exec);
+    delete graph;
+    return e == hipSuccess ? GDN_OK : GDN_ERR_HIP;
 }
 
 gdn_status gdn_prefill_choose(const gdn_dims* d, int32_t* chunk_or_zero)

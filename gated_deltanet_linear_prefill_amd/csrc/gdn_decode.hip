@@ -6,7 +6,10 @@
 // MI355X the bytes are the fp32 state: every (sequence, V head) state is read from HBM
 // once and written back once, with 128-bit coalesced accesses.
 //
-// One workgroup per (sequence, V head). With the state stored d_k-major (M = S^T,
+// One workgroup per (sequence, V head), or per (sequence, V head, block of 32 value
+// channels) when there are too few of those to fill the chip (a single sequence): each
+// channel's update is independent, so the blocks need no exchange, and a 32-channel row
+// segment is one whole 128-byte line. With the state stored d_k-major (M = S^T,
 // M[i][j] = S[j][i]), value channel j is column j of M and evolves on its own:
 //   s_k = khat . m_j,  s_q = qhat . m_j,  c_j = beta (v_j - alpha s_k)
 //   o_j = alpha s_q + c_j (qhat . khat),   m_j <- alpha m_j + c_j khat
@@ -18,33 +21,35 @@
 namespace gdn {
 namespace {
 
-template <int D>
+template <int D, int SPLIT>
 struct DecodeCfg {
-    static constexpr int NT = (D * D / 4 >= 256) ? 256 : D * D / 4;  // threads
-    static constexpr int CG = D / 4;                                 // float4 per row
-    static constexpr int RG = NT / CG;                               // row groups
-    static constexpr int RPT = D / RG;                               // rows per thread
+    static constexpr int DC = D / SPLIT;                               // channels per workgroup
+    static constexpr int NT = (D * DC / 4 >= 256) ? 256 : D * DC / 4;  // threads
+    static constexpr int CG = DC / 4;                                  // float4 per row segment
+    static constexpr int RG = NT / CG;                                 // row groups
+    static constexpr int RPT = D / RG;                                 // rows per thread
     static_assert(RG * RPT == D && CG * RG == NT, "decode tiling");
 };
 
-template <int D, typename TIn>
-__global__ void __launch_bounds__(DecodeCfg<D>::NT)
+template <int D, int SPLIT, typename TIn>
+__global__ void __launch_bounds__((DecodeCfg<D, SPLIT>::NT))
 decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* __restrict__ v,
               const float* __restrict__ g, const float* __restrict__ beta,
               const float* state_in, float* __restrict__ out, float* state_out, int h_qk,
               int h_v, float eps)
 {
-    using Cfg = DecodeCfg<D>;
+    using Cfg = DecodeCfg<D, SPLIT>;
     constexpr int CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT;
     __shared__ float s_q[D], s_k[D], s_norm[3];
     __shared__ float4 s_part[RG][CG][2];
 
-    const int64_t nh = blockIdx.x;  // sequence * h_v + V head
+    const int64_t nh = blockIdx.x / SPLIT;  // sequence * h_v + V head
+    const int cb = (int)(blockIdx.x % SPLIT) * Cfg::DC;  // first channel of this workgroup
     const int64_t seq = nh / h_v;
     const int h = (int)(nh - seq * h_v);
     const int hq = h / (h_v / h_qk);
     const int tid = threadIdx.x, cg = tid % CG, rg = tid / CG;
-    const int64_t sbase = nh * (int64_t)D * D;
+    const int64_t sbase = nh * (int64_t)D * D + cb;
 
     // 1. Issue the state loads first: they are the bytes that bound the step.
     float4 m[RPT];
@@ -63,7 +68,7 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* _
         s_q[tid] = load1_f32(q + qk_off + tid);
         s_k[tid] = load1_f32(k + qk_off + tid);
     }
-    const float4 vv = load4_f32(v + nh * (int64_t)D + 4 * cg);
+    const float4 vv = load4_f32(v + nh * (int64_t)D + cb + 4 * cg);
     const float alpha = expf(g[nh]);
     const float b = beta[nh];
     __syncthreads();
@@ -121,7 +126,7 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* _
         o.y = aq * tq.y + c.y * qkh;
         o.z = aq * tq.z + c.z * qkh;
         o.w = aq * tq.w + c.w * qkh;
-        *reinterpret_cast<float4*>(out + nh * (int64_t)D + 4 * cg) = o;
+        *reinterpret_cast<float4*>(out + nh * (int64_t)D + cb + 4 * cg) = o;
     }
 #pragma unroll
     for (int r = 0; r < RPT; ++r) {
@@ -135,15 +140,24 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* _
     }
 }
 
+template <int D, int SPLIT, typename TIn>
+hipError_t launch_decode_split(const Call& c)
+{
+    const int64_t blocks = c.n * c.h_v * SPLIT;
+    hipLaunchKernelGGL((decode_kernel<D, SPLIT, TIn>), dim3((unsigned)blocks),
+                       dim3(DecodeCfg<D, SPLIT>::NT), 0, c.stream, static_cast<const TIn*>(c.q),
+                       static_cast<const TIn*>(c.k), static_cast<const TIn*>(c.v), c.g, c.beta,
+                       c.state_in, c.out, c.state_out, c.h_qk, c.h_v, c.eps);
+    return hipGetLastError();
+}
+
+// Channel blocks of 32 when (sequence, V head) pairs alone would leave most CUs idle.
 template <int D, typename TIn>
 hipError_t launch_decode_t(const Call& c)
 {
-    const int64_t blocks = c.n * c.h_v;
-    hipLaunchKernelGGL((decode_kernel<D, TIn>), dim3((unsigned)blocks), dim3(DecodeCfg<D>::NT), 0,
-                       c.stream, static_cast<const TIn*>(c.q), static_cast<const TIn*>(c.k),
-                       static_cast<const TIn*>(c.v), c.g, c.beta, c.state_in, c.out,
-                       c.state_out, c.h_qk, c.h_v, c.eps);
-    return hipGetLastError();
+    constexpr int SPLIT = D >= 64 ? D / 32 : 1;
+    if (SPLIT > 1 && c.n * c.h_v < 256) return launch_decode_split<D, SPLIT, TIn>(c);
+    return launch_decode_split<D, 1, TIn>(c);
 }
 
 template <typename TIn>

@@ -43,11 +43,13 @@
  * n counts independent sequences; for the stacked decode step it counts layers.
  *
  * Pointers and ownership. Every data pointer is a DEVICE pointer on the current HIP
- * device. The caller allocates and owns every buffer, including the workspace. The
- * library never allocates, frees or synchronises, keeps no mutable global state, and is
- * safe to call from several host threads. Every compute call only enqueues work on
+ * device. The caller allocates and owns every buffer, including the workspace. Apart from
+ * the decode graph handle (gdn_decode_graph_create, which owns the HIP graph it records),
+ * the library never allocates, frees or synchronises, keeps no mutable global state, and
+ * is safe to call from several host threads. Every compute call only enqueues kernels on
  * `stream` (a hipStream_t; NULL is the default stream) and returns; results are ready
- * when the stream reaches that point.
+ * when the stream reaches that point. The compute calls make no memset or copy calls, so
+ * they may be recorded under HIP stream capture.
  *
  * Alignment. q, k, v, state_in, state_out, out and workspace must be 16-byte aligned;
  * g and beta 4-byte aligned.
@@ -148,6 +150,35 @@ gdn_status gdn_decode_step(const gdn_dims* dims, const void* q, const void* k,
                            const void* v, const float* g, const float* beta,
                            const float* state_in, float* out, float* state_out,
                            void* stream);
+
+/*
+ * Decode graph: one decode token through `layers` stacked GDN layers as dependent
+ * per-layer steps, recorded once as a HIP graph and replayed per token ("Decode: minimise
+ * bytes moved per token": keep each decode step on the GPU with as little host work per
+ * token as possible). Layer i runs gdn_decode_step(dims, q[i], k[i], v[i], g[i], beta[i],
+ * state[i], out[i], state[i]) -- its state updated in place -- after layer i - 1, in one
+ * stream. dims (t == 1, the same for every layer) and the pointer arrays (host arrays of
+ * `layers` device pointers) are validated per layer as for gdn_decode_step before anything
+ * is recorded; the device pointers are fixed in the graph, so the caller writes each
+ * token's inputs into the same buffers and keeps them alive until gdn_graph_destroy.
+ * `stream` must be a non-NULL stream (the legacy default stream cannot be captured); it is
+ * used only while recording. *graph receives the handle (NULL on error). Errors:
+ * GDN_ERR_NULL (a NULL pointer or stream), the gdn_decode_step errors of any layer
+ * (checked before recording), GDN_ERR_HIP if recording or instantiation fails.
+ *
+ * gdn_graph_launch enqueues one replay (all layers) on `stream` (NULL allowed);
+ * gdn_graph_destroy releases the handle (NULL is a no-op). Replays of one handle that
+ * overlap in time race on its buffers, as any two calls on the same buffers would.
+ */
+typedef struct gdn_graph_rec* gdn_graph;
+
+gdn_status gdn_decode_graph_create(const gdn_dims* dims, int32_t layers,
+                                   const void* const* q, const void* const* k,
+                                   const void* const* v, const float* const* g,
+                                   const float* const* beta, float* const* state,
+                                   float* const* out, void* stream, gdn_graph* graph);
+gdn_status gdn_graph_launch(gdn_graph graph, void* stream);
+gdn_status gdn_graph_destroy(gdn_graph graph);
 
 /*
  * Prefill method for these dims, from the measured scan-versus-chunk crossover on

@@ -239,3 +239,46 @@ def test_python_wrappers_reject_cpu_tensors():
     c = gdn_inputs.make_case(gdn_inputs.TINY, seed=1)
     with pytest.raises(ValueError):
         gdn.gdn_prefill_scan(c["q"], c["k"], c["v"], c["g"], c["beta"])
+
+
+# ------------------------------------------------------------------ decode graph (no GPU)
+def graph_args(layers, bufs, **over):
+    """Host arrays of per-layer fake device pointers for gdn_decode_graph_create."""
+    keys = ("q", "k", "v", "g", "beta", "state_in", "out")
+    arrays = []
+    for key in keys:
+        vals = [bufs[i].addr[key] for i in range(layers)]
+        if key in over:
+            vals = over[key](vals)
+        arrays.append((ctypes.c_void_p * max(1, layers))(*vals))
+    return [ctypes.cast(a, ctypes.POINTER(ctypes.c_void_p)) for a in arrays]
+
+
+def create_graph(lib, layers, bufs, dims, stream=ctypes.c_void_p(0x1000), handle=None, **over):
+    h = handle if handle is not None else ctypes.c_void_p(0xDEAD)
+    st = lib.gdn_decode_graph_create(ctypes.byref(dims), layers, *graph_args(layers, bufs, **over),
+                                     stream, ctypes.byref(h))
+    return st, h
+
+
+def test_decode_graph_validation(lib):
+    """Every layer is validated before anything is recorded (so no HIP call happens here);
+    the handle is cleared on error."""
+    bufs = [Bufs(t=1) for _ in range(3)]
+    dims = bufs[0].dims
+    st, h = create_graph(lib, 3, bufs, dims, stream=None)
+    assert st == NULL and not h.value                           # no stream to record on
+    st, h = create_graph(lib, 3, bufs, with_dims(bufs[0], t=2))
+    assert st == SHAPE and not h.value                          # decode is one token
+    st, h = create_graph(lib, 3, bufs, dims, q=lambda xs: xs[:2] + [None])
+    assert st == NULL and not h.value                           # layer 2 has no q
+    st, h = create_graph(lib, 3, bufs, dims, out=lambda xs: [xs[0], xs[1] + 4, xs[2]])
+    assert st == ALIGN and not h.value                          # layer 1 misaligned out
+    st, h = create_graph(lib, 3, bufs, dims, out=lambda xs: [xs[0], xs[1], bufs[2].addr["state_in"]])
+    assert st == ALIAS and not h.value                          # layer 2 out overlaps its state
+    st, h = create_graph(lib, -1, bufs, dims)
+    assert st == SHAPE and not h.value
+    assert lib.gdn_decode_graph_create(ctypes.byref(dims), 1, *graph_args(1, bufs),
+                                       ctypes.c_void_p(0x1000), None) == NULL
+    assert lib.gdn_graph_launch(None, None) == NULL
+    assert lib.gdn_graph_destroy(None) == OK
