@@ -94,7 +94,10 @@ size_t workspace_for(const gdn_dims* d, int32_t chunk)
                                                 d->qkv_dtype);
 }
 
-// Validate one call; `mode` 0 = scan, >0 = chunk size, -1 = decode (no workspace).
+// Validate one call. mode: a chunk size (chunked), 0 (direct scan), -1 (decode, t == 1,
+// no workspace) or -2 (no workspace
+// and no method-specific limit: the whole of a segmented call, whose segments are
+// validated again as they are issued).
 gdn_status validate(const gdn_dims* d, int32_t mode, const void* q, const void* k,
                     const void* v, const float* g, const float* beta, const float* state_in,
                     float* out, float* state_out, void* ws, size_t ws_bytes, Call* call)
@@ -264,6 +267,75 @@ gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, cons
     c.stream = static_cast<hipStream_t>(stream);
     (void)hipGetLastError();
     return finish(launch_decode(c));
+}
+
+size_t gdn_prefill_segmented_workspace_bytes(const gdn_dims* d, int64_t seg_t)
+{
+    Sizes s;
+    if (seg_t <= 0 || check_dims(d, &s) != GDN_OK || d->n == 0 || d->t == 0) return 0;
+    // the largest of a full segment's and the last segment's workspace, for one sequence
+    gdn_dims one = *d;
+    one.n = 1;
+    one.t = d->t < seg_t ? d->t : seg_t;
+    size_t need = gdn_prefill_workspace_bytes(&one);
+    if (d->t % seg_t != 0 && d->t > seg_t) {
+        one.t = d->t % seg_t;
+        const size_t last = gdn_prefill_workspace_bytes(&one);
+        need = last > need ? last : need;
+    }
+    return need;
+}
+
+gdn_status gdn_prefill_segmented(const gdn_dims* d, int64_t seg_t, const void* q, const void* k,
+                                 const void* v, const float* g, const float* beta,
+                                 const float* state_in, float* out, float* state_out, void* ws,
+                                 size_t ws_bytes, void* stream)
+{
+    if (!d) return GDN_ERR_NULL;
+    if (seg_t <= 0) return GDN_ERR_SHAPE;
+    // The whole call is validated as one (shapes, pointers, alignment, aliasing), with the
+    // segment workspace; every segment call below is a sub-range of it.
+    Call c;
+    gdn_status st = validate(d, -2, q, k, v, g, beta, state_in, out, state_out, nullptr, 0, &c);
+    if (st != GDN_OK) return st;
+    if (c.n == 0) return GDN_OK;
+    if (d->t == 0) return gdn_prefill(d, q, k, v, g, beta, state_in, out, state_out, ws, ws_bytes, stream);
+    const size_t need = gdn_prefill_segmented_workspace_bytes(d, seg_t);
+    if (need > 0 && (!ws || ws_bytes < need)) return GDN_ERR_WORKSPACE;
+    if (ws && need > 0) {
+        // the workspace must not overlap any buffer of the call
+        Sizes s;
+        check_dims(d, &s);
+        const Range r_w = range_of(ws, (int64_t)need, 1);
+        const Range others[] = {range_of(q, s.qk, s.esize), range_of(k, s.qk, s.esize),
+                                range_of(v, s.v, s.esize), range_of(g, s.gb, 4),
+                                range_of(beta, s.gb, 4), range_of(out, s.v, 4),
+                                range_of(state_out, s.state, 4),
+                                range_of(state_in, state_in ? s.state : 0, 4)};
+        for (const Range& r : others)
+            if (overlap(r_w, r)) return GDN_ERR_ALIAS;
+        if (!aligned(ws, 16)) return GDN_ERR_ALIGN;
+    }
+    const int64_t esz = d->qkv_dtype == GDN_BF16 ? 2 : 4;
+    const int64_t row_qk = (int64_t)d->h_qk * d->d_k, row_v = (int64_t)d->h_v * d->d_v;
+    const int64_t state_elems = (int64_t)d->h_v * d->d_k * d->d_v;
+    for (int64_t n = 0; n < d->n; ++n) {
+        for (int64_t t0 = 0; t0 < d->t; t0 += seg_t) {
+            gdn_dims one = *d;
+            one.n = 1;
+            one.t = d->t - t0 < seg_t ? d->t - t0 : seg_t;
+            const int64_t tok = n * d->t + t0;
+            const char* qb = static_cast<const char*>(q) + tok * row_qk * esz;
+            const char* kb = static_cast<const char*>(k) + tok * row_qk * esz;
+            const char* vb = static_cast<const char*>(v) + tok * row_v * esz;
+            const float* si = t0 == 0 ? (state_in ? state_in + n * state_elems : nullptr)
+                                      : state_out + n * state_elems;
+            st = gdn_prefill(&one, qb, kb, vb, g + tok * d->h_v, beta + tok * d->h_v, si,
+                             out + tok * row_v, state_out + n * state_elems, ws, ws_bytes, stream);
+            if (st != GDN_OK) return st;
+        }
+    }
+    return GDN_OK;
 }
 
 gdn_status gdn_decode_graph_create(const gdn_dims* d, int32_t layers, const void* const* q,

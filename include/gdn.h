@@ -197,6 +197,26 @@ gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const
                        float* out, float* state_out, void* workspace,
                        size_t workspace_bytes, void* stream);
 
+/*
+ * Segmented prefill ("Bound temporary memory with prompt chunking": a long prompt runs as
+ * bounded segments whose recurrent state carries the context forward, without changing
+ * the result). Each sequence's tokens are taken in consecutive segments of seg_t tokens
+ * (the last may be shorter); each segment runs the method gdn_prefill_choose picks for
+ * its length, on one sequence, with the state carried from segment to segment through
+ * state_out (updated in place after the first segment, which reads state_in). The one
+ * workspace is reused by every segment, so its size depends on seg_t, not on t:
+ * gdn_prefill_segmented_workspace_bytes(dims, seg_t). seg_t must be positive; the
+ * results agree with gdn_prefill to within rounding (the chunk boundaries restart at each
+ * segment). Errors as for gdn_prefill on the whole call, checked before anything is
+ * enqueued; GDN_ERR_SHAPE for seg_t <= 0.
+ */
+size_t gdn_prefill_segmented_workspace_bytes(const gdn_dims* dims, int64_t seg_t);
+gdn_status gdn_prefill_segmented(const gdn_dims* dims, int64_t seg_t, const void* q,
+                                 const void* k, const void* v, const float* g,
+                                 const float* beta, const float* state_in, float* out,
+                                 float* state_out, void* workspace, size_t workspace_bytes,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -282,3 +282,41 @@ def test_decode_graph_validation(lib):
                                        ctypes.c_void_p(0x1000), None) == NULL
     assert lib.gdn_graph_launch(None, None) == NULL
     assert lib.gdn_graph_destroy(None) == OK
+
+
+# ------------------------------------------------------------------ segmented prefill (no GPU)
+def call_segmented(lib, b, seg_t=16, dims=None, ws_bytes=64 * MB, **over):
+    a = {key: b.p(key) for key in ("q", "k", "v", "g", "beta", "state_in", "out",
+                                    "state_out", "ws")}
+    a.update(over)
+    d = ctypes.byref(dims if dims is not None else b.dims)
+    return lib.gdn_prefill_segmented(d, seg_t, a["q"], a["k"], a["v"], a["g"], a["beta"],
+                                     a["state_in"], a["out"], a["state_out"], a["ws"],
+                                     ws_bytes, None)
+
+
+def test_segmented_validation(lib):
+    """The whole call is validated before any segment is issued (no HIP call here)."""
+    b = Bufs(t=64)
+    assert lib.gdn_prefill_segmented(None, 16, *[None] * 9, 0, None) == NULL
+    assert call_segmented(lib, b, seg_t=0) == SHAPE
+    assert call_segmented(lib, b, seg_t=-5) == SHAPE
+    assert call_segmented(lib, b, q=None) == NULL
+    assert call_segmented(lib, b, out=b.p("out", 4)) == ALIGN
+    assert call_segmented(lib, b, out=b.p("q")) == ALIAS
+    assert call_segmented(lib, b, ws=None) == WS
+    assert call_segmented(lib, b, ws_bytes=16) == WS
+    assert call_segmented(lib, b, ws=b.p("state_out")) == ALIAS
+    assert call_segmented(lib, b, dims=with_dims(b, d_k=40, d_v=40)) == UNSUP
+
+
+def test_segmented_workspace_bytes(lib):
+    """The segmented workspace depends on the segment length, not on t."""
+    long = gdn.make_dims(2, 131072, 16, 32, 128)
+    seg = lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(long), 4096)
+    one = lib.gdn_prefill_workspace_bytes(ctypes.byref(gdn.make_dims(1, 4096, 16, 32, 128)))
+    assert seg == one > 0
+    assert lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(long), 0) == 0
+    ragged = gdn.make_dims(1, 4096 + 100, 16, 32, 128)
+    last = lib.gdn_prefill_workspace_bytes(ctypes.byref(gdn.make_dims(1, 100, 16, 32, 128)))
+    assert lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(ragged), 4096) == max(one, last)
