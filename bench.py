@@ -14,7 +14,10 @@ One step is the whole hot path once:
 The JSON line also carries decode_cold_us_per_token (the decode step with its states out of
 the MALL), decode_per_layer_{eager,graph}_us_per_token (the same token as 30 dependent
 per-layer steps of one sequence each, called one by one or replayed as one recorded HIP
-graph) and hbm_copy_GBps (what a 1 GiB device copy reaches; the achievable HBM rate next to
+graph), prefill_segmented_1024[_overlapped]_us_per_layer (one layer's prompt as four
+1024-token segments with the smaller workspace they need, in order or with each segment's
+per-chunk preparation on a side stream during the previous segment's sequential pass) and
+hbm_copy_GBps (what a 1 GiB device copy reaches; the achievable HBM rate next to
 the 8 TB/s peak), all measured after the timed region, and
   roofline:     the prefill call (its two kernels) against HBM: algorithmic bytes per call
                 (q, k, v, g, beta read once, out and state_out written once) divided by the
@@ -24,7 +27,9 @@ the 8 TB/s peak), all measured after the timed region, and
   cpu_baseline: the fp64 oracle timed on this host's cores on one layer of the same prefill.
 
 Modes for counter collection (no JSON line): --mode pmc-prefill runs the prefill calls of
-three layers; --mode pmc-copy runs a device copy of known size for counter calibration.
+three layers; --mode pmc-copy runs a device copy of known size for counter calibration;
+--mode segmented runs six segmented prefill calls (1024-token segments) in order, then six
+overlapped, for a kernel trace.
 """
 import argparse
 import json
@@ -47,7 +52,11 @@ def parse():
     ap.add_argument("--steps", type=int, default=10)
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--mode", choices=["bench", "pmc-prefill", "pmc-copy"], default="bench")
+    ap.add_argument("--core-only", action="store_true",
+                    help="skip the measurements after the timed region (their fields are null), "
+                         "so that a kernel trace holds only the timed step's kernels")
+    ap.add_argument("--mode", choices=["bench", "pmc-prefill", "pmc-copy", "segmented"],
+                    default="bench")
     return ap.parse_args()
 
 
@@ -91,11 +100,12 @@ def measured_traffic():
     return int(fields["bytes_per_call"])
 
 
-def reference_rates(gdn, dec, dec_out, dev):
+def reference_rates(gdn, dec, dec_out, pre, dev):
     """Outside the timed region: the decode step with its state out of the 256 MB MALL
     (six independent 30-layer state stacks used in turn, 360 MiB), and the HBM rate a plain
     1 GiB device copy reaches (read + write bytes per second), the achievable counterpart
-    of the 8 TB/s peak."""
+    of the 8 TB/s peak. Also one prefill layer run as 1024-token segments with the bounded
+    workspace that needs (gdn_prefill_segmented, in order and overlapped)."""
     import torch
     stacks = [torch.zeros(LAYERS, H_V, D, D, device=dev) for _ in range(6)]
     calls = [gdn.bind_decode_step(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], st,
@@ -138,6 +148,20 @@ def reference_rates(gdn, dec, dec_out, dev):
     layers_graph_us = timed(graph.launch)
     graph.close()
     del st, eager
+
+    seg_t = 1024
+    seg_out = torch.empty(1, T_PROMPT, H_V, D, device=dev)
+    seg_st = torch.empty(1, H_V, D, D, device=dev)
+    seg = {}
+    for ov in (False, True):
+        seg_ws = torch.empty(gdn.gdn_prefill_segmented_workspace_bytes(
+            1, T_PROMPT, H_QK, H_V, D, seg_t, overlapped=ov), device=dev, dtype=torch.uint8)
+        us = timed(lambda: gdn.gdn_prefill_segmented(
+            pre["q"], pre["k"], pre["v"], pre["g"], pre["beta"], None, seg_t=seg_t,
+            overlapped=ov, out=seg_out, state_out=seg_st, workspace=seg_ws))
+        seg[ov] = (us, seg_ws.numel())
+        del seg_ws
+    del seg_out, seg_st
     a = torch.empty(1 << 28, device=dev)
     b = torch.empty_like(a)
     b.copy_(a)
@@ -149,7 +173,26 @@ def reference_rates(gdn, dec, dec_out, dev):
     torch.cuda.synchronize()
     copy_gbs = 2 * a.numel() * 4 * 5 / (s.elapsed_time(e) * 1e-3) / 1e9
     return {"decode_cold_us": cold_us, "copy_GBps": copy_gbs,
-            "layers_eager_us": layers_eager_us, "layers_graph_us": layers_graph_us}
+            "layers_eager_us": layers_eager_us, "layers_graph_us": layers_graph_us,
+            "seg": seg}
+
+
+def extra_fields(extra):
+    """The JSON fields of reference_rates (null when it was skipped)."""
+    e = extra or {}
+    seg = e.get("seg", {})
+    cold = e.get("decode_cold_us")
+    return {
+        "decode_cold_us_per_token": cold,
+        "decode_cold_GBps": decode_bytes() / (cold * 1e-6) / 1e9 if cold else None,
+        "decode_per_layer_eager_us_per_token": e.get("layers_eager_us"),
+        "decode_per_layer_graph_us_per_token": e.get("layers_graph_us"),
+        "prefill_segmented_1024_us_per_layer": seg.get(False, (None, None))[0],
+        "prefill_segmented_1024_workspace_bytes": seg.get(False, (None, None))[1],
+        "prefill_segmented_1024_overlapped_us_per_layer": seg.get(True, (None, None))[0],
+        "prefill_segmented_1024_overlapped_workspace_bytes": seg.get(True, (None, None))[1],
+        "hbm_copy_GBps": e.get("copy_GBps"),
+    }
 
 
 def cpu_baseline():
@@ -225,6 +268,18 @@ def main():
         torch.cuda.synchronize()
         print("prefill calls done", flush=True)
         return
+    if args.mode == "segmented":
+        c = layers[0]
+        for ov in (False, True):
+            seg_ws = torch.empty(gdn.gdn_prefill_segmented_workspace_bytes(
+                1, T_PROMPT, H_QK, H_V, D, 1024, overlapped=ov), device=dev, dtype=torch.uint8)
+            for _ in range(6):
+                gdn.gdn_prefill_segmented(c["q"], c["k"], c["v"], c["g"], c["beta"], None,
+                                          seg_t=1024, overlapped=ov, out=outs[0],
+                                          state_out=states[0:1], workspace=seg_ws)
+            torch.cuda.synchronize()
+            print(f"segmented prefill calls done (overlapped={ov})", flush=True)
+        return
 
     def step(evs=None):
         if evs is None:
@@ -258,7 +313,7 @@ def main():
     achieved = prefill_bytes() / mean_call_s / 1e9
 
     traffic = measured_traffic()
-    extra = reference_rates(gdn, dec, dec_out, dev)
+    extra = None if args.core_only else reference_rates(gdn, dec, dec_out, layers[0], dev)
 
     res = {
         "metric": METRIC,
@@ -281,11 +336,8 @@ def main():
         "decode_us_per_token": sum(decode_ms) / len(decode_ms) * 1e3,
         "decode_GBps": decode_bytes() / (sum(decode_ms) / len(decode_ms) / 1e3) / 1e9,
         "prefill_us_per_layer": mean_call_s * 1e6,
-        "decode_cold_us_per_token": extra["decode_cold_us"],
-        "decode_cold_GBps": decode_bytes() / (extra["decode_cold_us"] * 1e-6) / 1e9,
-        "decode_per_layer_eager_us_per_token": extra["layers_eager_us"],
-        "decode_per_layer_graph_us_per_token": extra["layers_graph_us"],
-        "hbm_copy_GBps": extra["copy_GBps"],
+        **extra_fields(extra),
+        "prefill_workspace_bytes": ws.numel(),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gdn_prefill_chunked call (chunk_prep_kernel + chunk_scan_kernel)",

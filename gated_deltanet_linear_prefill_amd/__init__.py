@@ -68,8 +68,9 @@ def _load():
         "gdn_decode_graph_create": (ctypes.c_int, [D, i32] + [ctypes.POINTER(P)] * 7 + [P, ctypes.POINTER(P)]),
         "gdn_graph_launch": (ctypes.c_int, [P, P]),
         "gdn_graph_destroy": (ctypes.c_int, [P]),
-        "gdn_prefill_segmented_workspace_bytes": (sz, [D, ctypes.c_int64]),
-        "gdn_prefill_segmented": (ctypes.c_int, [D, ctypes.c_int64] + [P] * 9 + [sz, P]),
+        "gdn_prefill_segmented_workspace_bytes": (sz, [D, ctypes.c_int64, ctypes.c_int32]),
+        "gdn_prefill_segmented": (ctypes.c_int, [D, ctypes.c_int64, ctypes.c_int32] + [P] * 9
+                                  + [sz, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -259,25 +260,29 @@ def bind_decode_step(q, k, v, g, beta, state_in, out, state_out, *, l2_eps=1e-6,
                      (dims, q, k, v, g, beta, state_in, out, state_out))
 
 
-
-def gdn_prefill_segmented_workspace_bytes(n, t, h_qk, h_v, d, seg_t, dtype=torch.bfloat16) -> int:
+def gdn_prefill_segmented_workspace_bytes(n, t, h_qk, h_v, d, seg_t, overlapped=False,
+                                          dtype=torch.bfloat16) -> int:
     return _load().gdn_prefill_segmented_workspace_bytes(
-        ctypes.byref(make_dims(n, t, h_qk, h_v, d, dtype)), int(seg_t))
+        ctypes.byref(make_dims(n, t, h_qk, h_v, d, dtype)), int(seg_t), int(bool(overlapped)))
 
 
-def gdn_prefill_segmented(q, k, v, g, beta, state_in=None, *, seg_t, l2_eps=1e-6, out=None,
-                          state_out=None, workspace=None, stream=None):
+def gdn_prefill_segmented(q, k, v, g, beta, state_in=None, *, seg_t, overlapped=False,
+                          l2_eps=1e-6, out=None, state_out=None, workspace=None, stream=None):
     """Prefill as consecutive segments of seg_t tokens per sequence with one reused
-    workspace (sized by seg_t). Returns (out, state_out)."""
+    workspace (sized by seg_t; two segment slots when overlapped, so that a segment's
+    per-chunk preparation runs on a side stream during the previous segment's sequential
+    pass). Returns (out, state_out)."""
     dims, out, state_out = _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps)
+    ov = int(bool(overlapped))
     if workspace is None:
-        need = _load().gdn_prefill_segmented_workspace_bytes(ctypes.byref(dims), int(seg_t))
+        need = _load().gdn_prefill_segmented_workspace_bytes(ctypes.byref(dims), int(seg_t), ov)
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
     _check(_load().gdn_prefill_segmented(
-        ctypes.byref(dims), int(seg_t), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        ctypes.byref(dims), int(seg_t), ov, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
         _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace), workspace.numel(),
         _stream(q.device, stream)), "gdn_prefill_segmented")
     return out, state_out
+
 
 class DecodeGraph:
     """gdn_decode_graph_create / gdn_graph_launch / gdn_graph_destroy: one decode token

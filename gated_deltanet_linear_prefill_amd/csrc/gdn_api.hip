@@ -3,6 +3,7 @@
 //
 // Every check runs on the host before the first HIP call, so each error path is testable
 // without a GPU, and on error nothing is enqueued.
+#include <mutex>
 #include <vector>
 #include <math.h>
 #include <string.h>
@@ -179,6 +180,108 @@ int32_t choose_chunk(const gdn_dims* d)
     return pick;
 }
 
+// ---------------------------------------------------------------- segmented prefill
+
+// One segment of one sequence: a gdn_prefill call on sub-ranges of the whole call's buffers.
+struct Piece {
+    gdn_dims dims;
+    const void *q, *k, *v;
+    const float *g, *beta, *state_in;
+    float *out, *state_out;
+};
+
+// Segment p of a call (sequence-major): tokens [t0, t0 + len) of sequence p / per_seq. The
+// first segment of a sequence reads state_in; later ones continue from state_out in place.
+struct SegmentPlan {
+    const gdn_dims* d;
+    int64_t seg_t, per_seq, pieces;
+    const char *q, *k, *v;
+    const float *g, *beta, *state_in;
+    float *out, *state_out;
+
+    SegmentPlan(const gdn_dims* d_, int64_t seg, const void* q_, const void* k_, const void* v_,
+                const float* g_, const float* b_, const float* si, float* o, float* so)
+        : d(d_), seg_t(seg), per_seq((d_->t + seg - 1) / seg), pieces(d_->n * per_seq),
+          q(static_cast<const char*>(q_)), k(static_cast<const char*>(k_)),
+          v(static_cast<const char*>(v_)), g(g_), beta(b_), state_in(si), out(o), state_out(so)
+    {
+    }
+
+    Piece piece(int64_t p) const
+    {
+        const int64_t n = p / per_seq, t0 = (p % per_seq) * seg_t;
+        const int64_t esz = d->qkv_dtype == GDN_BF16 ? 2 : 4;
+        const int64_t row_qk = (int64_t)d->h_qk * d->d_k, row_v = (int64_t)d->h_v * d->d_v;
+        const int64_t state_elems = (int64_t)d->h_v * d->d_k * d->d_v;
+        const int64_t tok = n * d->t + t0;
+        Piece x;
+        x.dims = *d;
+        x.dims.n = 1;
+        x.dims.t = d->t - t0 < seg_t ? d->t - t0 : seg_t;
+        x.q = q + tok * row_qk * esz;
+        x.k = k + tok * row_qk * esz;
+        x.v = v + tok * row_v * esz;
+        x.g = g + tok * d->h_v;
+        x.beta = beta + tok * d->h_v;
+        x.state_in = t0 == 0 ? (state_in ? state_in + n * state_elems : nullptr)
+                             : state_out + n * state_elems;
+        x.out = out + tok * row_v;
+        x.state_out = state_out + n * state_elems;
+        return x;
+    }
+};
+
+// The largest of a full segment's and the last segment's workspace, for one sequence.
+size_t segment_workspace_bytes(const gdn_dims* d, int64_t seg_t)
+{
+    gdn_dims one = *d;
+    one.n = 1;
+    one.t = d->t < seg_t ? d->t : seg_t;
+    size_t need = workspace_for(&one, choose_chunk(&one));
+    if (d->t % seg_t != 0 && d->t > seg_t) {
+        one.t = d->t % seg_t;
+        const size_t last = workspace_for(&one, choose_chunk(&one));
+        need = last > need ? last : need;
+    }
+    return need;
+}
+
+size_t slot_bytes(size_t b)
+{
+    return (b + 255) / 256 * 256;
+}
+
+// The side stream and events of the overlapped schedule: one set per device, created on
+// first use and kept until the process ends. The stream has the default priority and does
+// not synchronise with the null stream; every dependency is an explicit event wait.
+struct SideStream {
+    hipStream_t stream = nullptr;
+    hipEvent_t start = nullptr, join = nullptr, prep[2] = {}, scan[2] = {};
+};
+constexpr int kMaxDevices = 64;
+SideStream g_side[kMaxDevices];
+std::mutex g_side_mu;  // held while a call records into its device's events
+
+gdn_status side_stream(SideStream** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GDN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return GDN_ERR_UNSUPPORTED;
+    SideStream& s = g_side[dev];
+    if (!s.stream) {
+        hipEvent_t* evs[] = {&s.start, &s.join, &s.prep[0], &s.prep[1], &s.scan[0], &s.scan[1]};
+        for (hipEvent_t* e : evs)
+            if (!*e && hipEventCreateWithFlags(e, hipEventDisableTiming) != hipSuccess)
+                return GDN_ERR_HIP;
+        if (hipStreamCreateWithFlags(&s.stream, hipStreamNonBlocking) != hipSuccess) {
+            s.stream = nullptr;
+            return GDN_ERR_HIP;
+        }
+    }
+    *out = &s;
+    return GDN_OK;
+}
+
 }  // namespace
 
 hipError_t launch_state_passthrough(const Call& c)
@@ -269,30 +372,23 @@ gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, cons
     return finish(launch_decode(c));
 }
 
-size_t gdn_prefill_segmented_workspace_bytes(const gdn_dims* d, int64_t seg_t)
+size_t gdn_prefill_segmented_workspace_bytes(const gdn_dims* d, int64_t seg_t, int32_t overlapped)
 {
     Sizes s;
-    if (seg_t <= 0 || check_dims(d, &s) != GDN_OK || d->n == 0 || d->t == 0) return 0;
-    // the largest of a full segment's and the last segment's workspace, for one sequence
-    gdn_dims one = *d;
-    one.n = 1;
-    one.t = d->t < seg_t ? d->t : seg_t;
-    size_t need = gdn_prefill_workspace_bytes(&one);
-    if (d->t % seg_t != 0 && d->t > seg_t) {
-        one.t = d->t % seg_t;
-        const size_t last = gdn_prefill_workspace_bytes(&one);
-        need = last > need ? last : need;
-    }
-    return need;
+    if (seg_t <= 0 || (overlapped != 0 && overlapped != 1) || check_dims(d, &s) != GDN_OK ||
+        d->n == 0 || d->t == 0)
+        return 0;
+    const size_t one = segment_workspace_bytes(d, seg_t);
+    return overlapped ? 2 * slot_bytes(one) : one;
 }
 
-gdn_status gdn_prefill_segmented(const gdn_dims* d, int64_t seg_t, const void* q, const void* k,
-                                 const void* v, const float* g, const float* beta,
-                                 const float* state_in, float* out, float* state_out, void* ws,
-                                 size_t ws_bytes, void* stream)
+gdn_status gdn_prefill_segmented(const gdn_dims* d, int64_t seg_t, int32_t overlapped,
+                                 const void* q, const void* k, const void* v, const float* g,
+                                 const float* beta, const float* state_in, float* out,
+                                 float* state_out, void* ws, size_t ws_bytes, void* stream)
 {
     if (!d) return GDN_ERR_NULL;
-    if (seg_t <= 0) return GDN_ERR_SHAPE;
+    if (seg_t <= 0 || (overlapped != 0 && overlapped != 1)) return GDN_ERR_SHAPE;
     // The whole call is validated as one (shapes, pointers, alignment, aliasing), with the
     // segment workspace; every segment call below is a sub-range of it.
     Call c;
@@ -300,7 +396,7 @@ gdn_status gdn_prefill_segmented(const gdn_dims* d, int64_t seg_t, const void* q
     if (st != GDN_OK) return st;
     if (c.n == 0) return GDN_OK;
     if (d->t == 0) return gdn_prefill(d, q, k, v, g, beta, state_in, out, state_out, ws, ws_bytes, stream);
-    const size_t need = gdn_prefill_segmented_workspace_bytes(d, seg_t);
+    const size_t need = gdn_prefill_segmented_workspace_bytes(d, seg_t, overlapped);
     if (need > 0 && (!ws || ws_bytes < need)) return GDN_ERR_WORKSPACE;
     if (ws && need > 0) {
         // the workspace must not overlap any buffer of the call
@@ -316,26 +412,72 @@ gdn_status gdn_prefill_segmented(const gdn_dims* d, int64_t seg_t, const void* q
             if (overlap(r_w, r)) return GDN_ERR_ALIAS;
         if (!aligned(ws, 16)) return GDN_ERR_ALIGN;
     }
-    const int64_t esz = d->qkv_dtype == GDN_BF16 ? 2 : 4;
-    const int64_t row_qk = (int64_t)d->h_qk * d->d_k, row_v = (int64_t)d->h_v * d->d_v;
-    const int64_t state_elems = (int64_t)d->h_v * d->d_k * d->d_v;
-    for (int64_t n = 0; n < d->n; ++n) {
-        for (int64_t t0 = 0; t0 < d->t; t0 += seg_t) {
-            gdn_dims one = *d;
-            one.n = 1;
-            one.t = d->t - t0 < seg_t ? d->t - t0 : seg_t;
-            const int64_t tok = n * d->t + t0;
-            const char* qb = static_cast<const char*>(q) + tok * row_qk * esz;
-            const char* kb = static_cast<const char*>(k) + tok * row_qk * esz;
-            const char* vb = static_cast<const char*>(v) + tok * row_v * esz;
-            const float* si = t0 == 0 ? (state_in ? state_in + n * state_elems : nullptr)
-                                      : state_out + n * state_elems;
-            st = gdn_prefill(&one, qb, kb, vb, g + tok * d->h_v, beta + tok * d->h_v, si,
-                             out + tok * row_v, state_out + n * state_elems, ws, ws_bytes, stream);
+    // Only two segment lengths occur (seg_t and the remainder): check the method-specific
+    // limits of both before anything is enqueued.
+    for (int64_t len : {d->t < seg_t ? d->t : seg_t, d->t % seg_t}) {
+        if (len == 0) continue;
+        gdn_dims one = *d;
+        one.n = 1;
+        one.t = len;
+        st = validate(&one, choose_chunk(&one), q, k, v, g, beta, state_in, out, state_out,
+                      nullptr, 0, &c);
+        if (st != GDN_OK && st != GDN_ERR_WORKSPACE) return st;
+    }
+    const SegmentPlan plan(d, seg_t, q, k, v, g, beta, state_in, out, state_out);
+    if (!overlapped) {
+        for (int64_t p = 0; p < plan.pieces; ++p) {
+            const Piece x = plan.piece(p);
+            st = gdn_prefill(&x.dims, x.q, x.k, x.v, x.g, x.beta, x.state_in, x.out,
+                             x.state_out, ws, ws_bytes, stream);
             if (st != GDN_OK) return st;
         }
+        return GDN_OK;
     }
-    return GDN_OK;
+
+    // Overlapped: the per-chunk preparation of segment p + 1 runs on the side stream while
+    // the sequential pass of segment p runs on the caller's stream, with the workspace split
+    // into two slots used by alternate segments.
+    hipStream_t main_s = static_cast<hipStream_t>(stream);
+    hipStreamCaptureStatus cap = hipStreamCaptureStatusNone;
+    if (hipStreamIsCapturing(main_s, &cap) != hipSuccess) return GDN_ERR_HIP;
+    if (cap != hipStreamCaptureStatusNone) return GDN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_side_mu);
+    SideStream* side = nullptr;
+    st = side_stream(&side);
+    if (st != GDN_OK) return st;
+    const size_t slot = slot_bytes(segment_workspace_bytes(d, seg_t));
+    (void)hipGetLastError();
+    hipError_t e = hipEventRecord(side->start, main_s);
+    if (e == hipSuccess) e = hipStreamWaitEvent(side->stream, side->start, 0);
+    for (int64_t p = 0; p < plan.pieces && e == hipSuccess; ++p) {
+        const Piece x = plan.piece(p);
+        const int sl = (int)(p & 1);
+        void* wsp = static_cast<char*>(ws) + sl * slot;
+        const int32_t chunk = choose_chunk(&x.dims);
+        st = validate(&x.dims, chunk, x.q, x.k, x.v, x.g, x.beta, x.state_in, x.out,
+                      x.state_out, wsp, slot, &c);
+        if (st != GDN_OK) break;
+        if (chunk > 0) {
+            // the slot's previous user (segment p - 2) has finished its sequential pass
+            if (p >= 2) e = hipStreamWaitEvent(side->stream, side->scan[sl], 0);
+            c.stream = side->stream;
+            if (e == hipSuccess) e = launch_chunked(c, chunk, kChunkPrep);
+            if (e == hipSuccess) e = hipEventRecord(side->prep[sl], side->stream);
+            if (e == hipSuccess) e = hipStreamWaitEvent(main_s, side->prep[sl], 0);
+            c.stream = main_s;
+            if (e == hipSuccess) e = launch_chunked(c, chunk, kChunkScan);
+        } else {
+            c.stream = main_s;
+            e = launch_scan(c);
+        }
+        if (e == hipSuccess) e = hipEventRecord(side->scan[sl], main_s);
+    }
+    // The caller's stream orders after everything enqueued on the side stream, also when
+    // the loop stopped early.
+    hipError_t j = hipEventRecord(side->join, side->stream);
+    if (j == hipSuccess) j = hipStreamWaitEvent(main_s, side->join, 0);
+    if (st != GDN_OK) return st;
+    return finish(e != hipSuccess ? e : j);
 }
 
 gdn_status gdn_decode_graph_create(const gdn_dims* d, int32_t layers, const void* const* q,

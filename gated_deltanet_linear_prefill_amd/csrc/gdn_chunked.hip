@@ -920,8 +920,7 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
     constexpr bool F32IN = std::is_same<TIn, float>::value;
     using G = Geo<D, C, F32IN>;
     using SG = ScanGeo<D, C, TIn>;
-    using Raw = typename RawFrag<TIn>::type;
-    constexpr int CP = G::CP, RT = G::RT, KTC = G::KTC, KTD = G::KTD, NS = G::NS;
+    constexpr int CP = G::CP, RT = G::RT, KTC = G::KTC, NS = G::NS;
     constexpr int NTRI = G::NTRI, NHF = G::NHF;
     constexpr int NSW = SG::NSW, KPS = SG::KPS, NHW = SG::NHW, NOH = SG::NOH, NSH = SG::NSH;
     constexpr int NR = SG::NR, ROWB = SG::ROWB, RPB = SG::RPB, NG = SG::NG;
@@ -1542,7 +1541,10 @@ chunk_scan_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TI
         dispatch_index<0, NHW>(hw, [&](auto ic) {
             constexpr int i = decltype(ic)::value;
             if constexpr (i == 0) output_helper(std::integral_constant<int, 0>{});
-            else if constexpr (NOH == 2 && i == NHW - 1) output_helper(std::integral_constant<int, 1>{});
+            // (the row tile is written as a function of i, 1 here, so that the call is only
+            // instantiated where the branch is taken)
+            else if constexpr (NOH == 2 && i == NHW - 1)
+                output_helper(std::integral_constant<int, i + 2 - NHW>{});
             else staging_helper(std::integral_constant<int, i - 1>{});
         });
     }
@@ -2046,7 +2048,7 @@ chunk_scan_wide_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, con
 }
 
 template <int D, int C, typename TIn>
-hipError_t launch_chunked_t(const Call& cl)
+hipError_t launch_chunked_t(const Call& cl, int parts)
 {
     constexpr bool F32IN = std::is_same<TIn, float>::value;
     const ChunkWs L = chunk_ws(cl.n, cl.t, cl.h_qk, cl.h_v, D, C, F32IN);
@@ -2055,10 +2057,13 @@ hipError_t launch_chunked_t(const Call& cl)
     const TIn* k = static_cast<const TIn*>(cl.k);
     const TIn* v = static_cast<const TIn*>(cl.v);
     const int64_t prep_blocks = cl.n * L.nch * cl.h_qk;
-    hipLaunchKernelGGL((chunk_prep_kernel<D, C, TIn>), dim3((unsigned)prep_blocks), dim3(256), 0,
-                       cl.stream, q, k, cl.g, cl.beta, ws, L, cl.t, cl.h_qk, cl.h_v, cl.eps);
-    hipError_t e = hipGetLastError();
-    if (e != hipSuccess) return e;
+    if (parts & kChunkPrep) {
+        hipLaunchKernelGGL((chunk_prep_kernel<D, C, TIn>), dim3((unsigned)prep_blocks), dim3(256), 0,
+                           cl.stream, q, k, cl.g, cl.beta, ws, L, cl.t, cl.h_qk, cl.h_v, cl.eps);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    if (!(parts & kChunkScan)) return hipSuccess;
     const int64_t scan_blocks = cl.n * cl.h_v * (D / 16);
     if constexpr (C <= 32) {
         hipLaunchKernelGGL((chunk_scan_kernel<D, C, TIn>), dim3((unsigned)scan_blocks),
@@ -2073,25 +2078,25 @@ hipError_t launch_chunked_t(const Call& cl)
 }
 
 template <int D, typename TIn>
-hipError_t dispatch_c(const Call& cl, int chunk)
+hipError_t dispatch_c(const Call& cl, int chunk, int parts)
 {
     switch (chunk) {
-        case 16: return launch_chunked_t<D, 16, TIn>(cl);
-        case 32: return launch_chunked_t<D, 32, TIn>(cl);
-        case 64: return launch_chunked_t<D, 64, TIn>(cl);
-        case 128: return launch_chunked_t<D, 128, TIn>(cl);
+        case 16: return launch_chunked_t<D, 16, TIn>(cl, parts);
+        case 32: return launch_chunked_t<D, 32, TIn>(cl, parts);
+        case 64: return launch_chunked_t<D, 64, TIn>(cl, parts);
+        case 128: return launch_chunked_t<D, 128, TIn>(cl, parts);
         default: return hipErrorInvalidValue;
     }
 }
 
 template <typename TIn>
-hipError_t dispatch_d(const Call& cl, int chunk)
+hipError_t dispatch_d(const Call& cl, int chunk, int parts)
 {
     switch (cl.d) {
-        case 16: return dispatch_c<16, TIn>(cl, chunk);
-        case 32: return dispatch_c<32, TIn>(cl, chunk);
-        case 64: return dispatch_c<64, TIn>(cl, chunk);
-        case 128: return dispatch_c<128, TIn>(cl, chunk);
+        case 16: return dispatch_c<16, TIn>(cl, chunk, parts);
+        case 32: return dispatch_c<32, TIn>(cl, chunk, parts);
+        case 64: return dispatch_c<64, TIn>(cl, chunk, parts);
+        case 128: return dispatch_c<128, TIn>(cl, chunk, parts);
         default: return hipErrorInvalidValue;
     }
 }
@@ -2104,9 +2109,10 @@ size_t chunked_workspace_bytes(int64_t n, int64_t t, int32_t h_qk, int32_t h_v, 
     return chunk_ws(n, t, h_qk, h_v, d, chunk, dtype != GDN_BF16).total;
 }
 
-hipError_t launch_chunked(const Call& c, int chunk)
+hipError_t launch_chunked(const Call& c, int chunk, int parts)
 {
-    return c.dtype == GDN_BF16 ? dispatch_d<uint16_t>(c, chunk) : dispatch_d<float>(c, chunk);
+    return c.dtype == GDN_BF16 ? dispatch_d<uint16_t>(c, chunk, parts)
+                               : dispatch_d<float>(c, chunk, parts);
 }
 
 }  // namespace gdn

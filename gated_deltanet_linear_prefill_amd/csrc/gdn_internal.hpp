@@ -27,7 +27,10 @@ struct Call {
 // launches. The caller has validated everything the kernels assume.
 hipError_t launch_decode(const Call& c);
 hipError_t launch_scan(const Call& c);
-hipError_t launch_chunked(const Call& c, int chunk);
+// parts: kChunkPrep (the per-chunk preparation into the workspace), kChunkScan (the
+// sequential pass that reads it), or both; the scan must follow a prep of the same call.
+constexpr int kChunkPrep = 1, kChunkScan = 2;
+hipError_t launch_chunked(const Call& c, int chunk, int parts = kChunkPrep | kChunkScan);
 hipError_t launch_state_passthrough(const Call& c);  // t == 0: state_out = state_in or 0
 
 size_t scan_workspace_bytes(int64_t n, int64_t t, int32_t h_qk, int32_t h_v, int32_t d);

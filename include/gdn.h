@@ -203,16 +203,32 @@ gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const
  * the result). Each sequence's tokens are taken in consecutive segments of seg_t tokens
  * (the last may be shorter); each segment runs the method gdn_prefill_choose picks for
  * its length, on one sequence, with the state carried from segment to segment through
- * state_out (updated in place after the first segment, which reads state_in). The one
+ * state_out (updated in place after the first segment, which reads state_in). The
  * workspace is reused by every segment, so its size depends on seg_t, not on t:
- * gdn_prefill_segmented_workspace_bytes(dims, seg_t). seg_t must be positive; the
- * results agree with gdn_prefill to within rounding (the chunk boundaries restart at each
- * segment). Errors as for gdn_prefill on the whole call, checked before anything is
- * enqueued; GDN_ERR_SHAPE for seg_t <= 0.
+ * gdn_prefill_segmented_workspace_bytes(dims, seg_t, overlapped). seg_t must be
+ * positive; the results agree with gdn_prefill to within rounding (the chunk boundaries
+ * restart at each segment), and are the same bits with overlapped 0 or 1.
+ *
+ * overlapped = 0: the segments run one after another on `stream`.
+ * overlapped = 1: the workspace holds two segment slots (twice the bytes, each slot
+ *   rounded up to 256). The per-chunk preparation of a chunked segment runs on a second
+ *   stream that the library creates on first use (one per device, default priority, kept
+ *   until the process ends) while the previous segment's sequential pass runs on
+ *   `stream`; events order the two, and `stream` waits for all of the call's work before
+ *   anything enqueued after it. The current device must be the device of `stream`. Calls
+ *   on one device are serialised on the host while they enqueue. Not for graph capture:
+ *   GDN_ERR_UNSUPPORTED when `stream` is capturing.
+ *
+ * Errors as for gdn_prefill on the whole call, checked before anything is enqueued
+ * (including the method limits of both segment lengths); GDN_ERR_SHAPE for seg_t <= 0 or
+ * overlapped not 0 or 1; GDN_ERR_HIP if the runtime fails to create or record the side
+ * stream's events. gdn_prefill_segmented_workspace_bytes returns 0 for an empty call or
+ * invalid arguments.
  */
-size_t gdn_prefill_segmented_workspace_bytes(const gdn_dims* dims, int64_t seg_t);
-gdn_status gdn_prefill_segmented(const gdn_dims* dims, int64_t seg_t, const void* q,
-                                 const void* k, const void* v, const float* g,
+size_t gdn_prefill_segmented_workspace_bytes(const gdn_dims* dims, int64_t seg_t,
+                                             int32_t overlapped);
+gdn_status gdn_prefill_segmented(const gdn_dims* dims, int64_t seg_t, int32_t overlapped,
+                                 const void* q, const void* k, const void* v, const float* g,
                                  const float* beta, const float* state_in, float* out,
                                  float* state_out, void* workspace, size_t workspace_bytes,
                                  void* stream);

@@ -285,12 +285,12 @@ def test_decode_graph_validation(lib):
 
 
 # ------------------------------------------------------------------ segmented prefill (no GPU)
-def call_segmented(lib, b, seg_t=16, dims=None, ws_bytes=64 * MB, **over):
+def call_segmented(lib, b, seg_t=16, dims=None, ws_bytes=64 * MB, overlapped=0, **over):
     a = {key: b.p(key) for key in ("q", "k", "v", "g", "beta", "state_in", "out",
                                     "state_out", "ws")}
     a.update(over)
     d = ctypes.byref(dims if dims is not None else b.dims)
-    return lib.gdn_prefill_segmented(d, seg_t, a["q"], a["k"], a["v"], a["g"], a["beta"],
+    return lib.gdn_prefill_segmented(d, seg_t, overlapped, a["q"], a["k"], a["v"], a["g"], a["beta"],
                                      a["state_in"], a["out"], a["state_out"], a["ws"],
                                      ws_bytes, None)
 
@@ -298,9 +298,14 @@ def call_segmented(lib, b, seg_t=16, dims=None, ws_bytes=64 * MB, **over):
 def test_segmented_validation(lib):
     """The whole call is validated before any segment is issued (no HIP call here)."""
     b = Bufs(t=64)
-    assert lib.gdn_prefill_segmented(None, 16, *[None] * 9, 0, None) == NULL
+    assert lib.gdn_prefill_segmented(None, 16, 0, *[None] * 9, 0, None) == NULL
     assert call_segmented(lib, b, seg_t=0) == SHAPE
     assert call_segmented(lib, b, seg_t=-5) == SHAPE
+    assert call_segmented(lib, b, overlapped=2) == SHAPE
+    assert call_segmented(lib, b, overlapped=-1) == SHAPE
+    need = lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(b.dims), 16, 1)
+    assert call_segmented(lib, b, overlapped=1, ws_bytes=need - 1) == WS
+    assert call_segmented(lib, b, overlapped=1, ws=b.p("ws", 8)) == ALIGN
     assert call_segmented(lib, b, q=None) == NULL
     assert call_segmented(lib, b, out=b.p("out", 4)) == ALIGN
     assert call_segmented(lib, b, out=b.p("q")) == ALIAS
@@ -313,10 +318,14 @@ def test_segmented_validation(lib):
 def test_segmented_workspace_bytes(lib):
     """The segmented workspace depends on the segment length, not on t."""
     long = gdn.make_dims(2, 131072, 16, 32, 128)
-    seg = lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(long), 4096)
+    seg = lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(long), 4096, 0)
     one = lib.gdn_prefill_workspace_bytes(ctypes.byref(gdn.make_dims(1, 4096, 16, 32, 128)))
     assert seg == one > 0
-    assert lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(long), 0) == 0
+    assert lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(long), 0, 0) == 0
     ragged = gdn.make_dims(1, 4096 + 100, 16, 32, 128)
     last = lib.gdn_prefill_workspace_bytes(ctypes.byref(gdn.make_dims(1, 100, 16, 32, 128)))
-    assert lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(ragged), 4096) == max(one, last)
+    assert lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(ragged), 4096, 0) == max(one, last)
+    # overlapped: two slots, each rounded up to 256 bytes
+    slot = (max(one, last) + 255) // 256 * 256
+    assert lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(ragged), 4096, 1) == 2 * slot
+    assert lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(ragged), 4096, 2) == 0

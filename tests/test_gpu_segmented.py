@@ -19,16 +19,19 @@ def run_oracle(c):
 
 
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
-@pytest.mark.parametrize("seg_t", [1, 7, 64, 100, 1000])
+@pytest.mark.parametrize("seg_t", [1, 7, 64, 100, 290, 1000])
 def test_segmented_small(dtype, seg_t):
-    """Two sequences, ragged segments (including one token at a time and one segment longer
-    than the prompt), non-zero initial state: every output and state against the oracle."""
+    """Two sequences, ragged segments (one token at a time, a chunked segment followed by a
+    direct-scan remainder, one segment longer than the prompt), non-zero initial state: every
+    output and state against the oracle; the overlapped schedule gives the same bits."""
     shape = Shape(n=2, t=300, h_qk=2, h_v=4, d=64, dtype=dtype)
     c = gdn_inputs.make_case(shape, seed=700 + seg_t, device=DEV, s0_std=0.1)
     out, st = gdn.gdn_prefill_segmented(**c, seg_t=seg_t)
+    o2, s2 = gdn.gdn_prefill_segmented(**c, seg_t=seg_t, overlapped=True)
     torch.cuda.synchronize()
     o_ref, s_ref = run_oracle(c)
     assert_parity(out, st, o_ref, s_ref, f"segmented seg_t={seg_t} {dtype}")
+    assert torch.equal(out, o2) and torch.equal(st, s2)
 
 
 def test_segmented_in_place_and_empty():
@@ -46,14 +49,30 @@ def test_segmented_in_place_and_empty():
     assert torch.equal(s0, c["state_in"])
 
 
+@pytest.mark.parametrize("overlapped", [False, True], ids=["in_order", "overlapped"])
 @pytest.mark.parametrize("seg_t", [1000, 1024, 8192])
-def test_segmented_prefill_4k(seg_t):
+def test_segmented_prefill_4k(seg_t, overlapped):
     """The 4096-token workload in segments (the chosen method per segment length): sampled
-    V heads against the oracle, every head against one whole-prompt gdn_prefill call."""
+    V heads against the oracle, every head against one whole-prompt gdn_prefill call.
+    q and k are written on the caller's stream right before the call, behind a long matrix
+    product, after being filled with NaN: a segment that read them before the caller's
+    earlier work had finished would produce NaN."""
     c = gdn_inputs.make_case(gdn_inputs.PREFILL_4K, seed=2, device=DEV)
-    ws = torch.empty(gdn.gdn_prefill_segmented_workspace_bytes(1, 4096, 16, 32, 128, seg_t),
+    src = {key: c[key] for key in ("q", "k")}
+    seg_in = dict(c)
+    for key in ("q", "k"):
+        seg_in[key] = torch.full_like(src[key], float("nan"))
+    torch.cuda.synchronize()
+    a = torch.randn(8192, 8192, device=DEV)
+    busy = a @ a  # several milliseconds on the caller's stream
+    for key in ("q", "k"):
+        seg_in[key].copy_(src[key])
+    ws = torch.empty(gdn.gdn_prefill_segmented_workspace_bytes(1, 4096, 16, 32, 128, seg_t,
+                                                               overlapped),
                      device=DEV, dtype=torch.uint8)
-    out, st = gdn.gdn_prefill_segmented(**c, seg_t=seg_t, workspace=ws)
+    ws.fill_(0xFF)  # stale slot contents must not leak into any segment
+    out, st = gdn.gdn_prefill_segmented(**seg_in, seg_t=seg_t, workspace=ws, overlapped=overlapped)
+    del busy
     whole_out, whole_st = gdn.gdn_prefill(**c)
     torch.cuda.synchronize()
     assert_parity(out, st, whole_out, whole_st, f"segmented {seg_t} vs whole call")
