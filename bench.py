@@ -29,7 +29,10 @@ the 8 TB/s peak), all measured after the timed region, and
 Modes for counter collection (no JSON line): --mode pmc-prefill runs the prefill calls of
 three layers; --mode pmc-copy runs a device copy of known size for counter calibration;
 --mode segmented runs six segmented prefill calls (1024-token segments) in order, then six
-overlapped, for a kernel trace.
+overlapped, for a kernel trace; --mode ablation times the state-residency ablation at 2048
+tokens (resident direct scan, the same scan with the state through device memory every 32
+tokens, and the chunked call) and prints one JSON line of its own; --mode pmc-ablation makes
+one call of each scan form for counter collection.
 """
 import argparse
 import json
@@ -55,8 +58,8 @@ def parse():
     ap.add_argument("--core-only", action="store_true",
                     help="skip the measurements after the timed region (their fields are null), "
                          "so that a kernel trace holds only the timed step's kernels")
-    ap.add_argument("--mode", choices=["bench", "pmc-prefill", "pmc-copy", "segmented"],
-                    default="bench")
+    ap.add_argument("--mode", choices=["bench", "pmc-prefill", "pmc-copy", "segmented",
+                                       "ablation", "pmc-ablation"], default="bench")
     return ap.parse_args()
 
 
@@ -177,6 +180,58 @@ def reference_rates(gdn, dec, dec_out, pre, dev):
             "seg": seg}
 
 
+def ablation(gdn, gdn_inputs, dev, counters):
+    """The state-residency ablation at 2048 tokens (16 QK / 32 V heads, d = 128, bf16): the
+    direct scan with the state resident for the whole prompt, against the same scan with
+    the state sent through device memory every 32 tokens. counters: one call of each (for
+    rocprofv3 --pmc) and no JSON line; else mean call times (HIP events, 10 calls after 2
+    warm-up) as one JSON line."""
+    import torch
+    c = gdn_inputs.make_case(gdn_inputs.ABLATION_2K, seed=300, device=dev)
+    shp = gdn_inputs.ABLATION_2K
+    block_t = 32
+    out = torch.empty(1, shp.t, shp.h_v, shp.d, device=dev)
+    st = torch.empty(1, shp.h_v, shp.d, shp.d, device=dev)
+    ws = torch.empty(gdn.gdn_workspace_bytes(1, shp.t, shp.h_qk, shp.h_v, shp.d, chunk=0),
+                     device=dev, dtype=torch.uint8)
+    chunk = gdn.gdn_prefill_choose(shp.t, shp.h_qk, shp.h_v, shp.d)
+    ws_c = torch.empty(gdn.gdn_workspace_bytes(1, shp.t, shp.h_qk, shp.h_v, shp.d, chunk=chunk),
+                       device=dev, dtype=torch.uint8)
+    runs = {
+        "resident": lambda: gdn.gdn_prefill_scan(**c, out=out, state_out=st, workspace=ws),
+        "blockwise": lambda: gdn.gdn_prefill_scan_blockwise(**c, block_t=block_t, out=out,
+                                                            state_out=st, workspace=ws),
+        "chunked": lambda: gdn.gdn_prefill_chunked(**c, chunk=chunk, out=out, state_out=st,
+                                                   workspace=ws_c),
+    }
+    if counters:
+        for name in ("resident", "blockwise"):
+            runs[name]()
+            torch.cuda.synchronize()
+            print(f"{name} call done", flush=True)
+        return
+    res = {}
+    for name, fn in runs.items():
+        for _ in range(2):
+            fn()
+        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        torch.cuda.synchronize()
+        s.record()
+        for _ in range(10):
+            fn()
+        e.record()
+        torch.cuda.synchronize()
+        res[name + "_us"] = s.elapsed_time(e) / 10 * 1e3
+    # fp32 state of one layer; with S0 = 0 the first block reads none, so the blockwise
+    # form moves (2 blocks - 1) states and the resident one a single write
+    state_bytes = shp.h_v * shp.d * shp.d * 4
+    blocks = -(-shp.t // block_t)
+    print(json.dumps({"workload": "GDN prefill, T=2048, 16 QK + 32 V heads, d=128, bf16, S0=0",
+                      "block_t": block_t, "blocks": blocks,
+                      "state_bytes_blockwise": state_bytes * (2 * blocks - 1),
+                      "state_bytes_resident": state_bytes, "chunk": chunk, **res}), flush=True)
+
+
 def extra_fields(extra):
     """The JSON fields of reference_rates (null when it was skipped)."""
     e = extra or {}
@@ -240,6 +295,10 @@ def main():
             b.copy_(a)
         torch.cuda.synchronize()
         print(f"copied {COPY_BYTES} bytes x3", flush=True)
+        return
+
+    if args.mode in ("ablation", "pmc-ablation"):
+        ablation(gdn, gdn_inputs, dev, counters=args.mode == "pmc-ablation")
         return
 
     # ---- inputs, all resident before timing

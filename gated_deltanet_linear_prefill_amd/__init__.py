@@ -19,7 +19,7 @@ __all__ = [
     "gdn_prefill_chunked", "gdn_prefill_scan", "gdn_decode_step", "gdn_prefill_choose",
     "gdn_prefill", "gdn_prefill_workspace_bytes", "library_path", "Dims", "BoundCall",
     "bind_prefill_chunked", "bind_prefill_scan", "bind_decode_step", "DecodeGraph",
-    "gdn_prefill_segmented", "gdn_prefill_segmented_workspace_bytes",
+    "gdn_prefill_segmented", "gdn_prefill_segmented_workspace_bytes", "gdn_prefill_scan_blockwise",
 ]
 
 GDN_F32, GDN_BF16 = 0, 1
@@ -68,6 +68,7 @@ def _load():
         "gdn_decode_graph_create": (ctypes.c_int, [D, i32] + [ctypes.POINTER(P)] * 7 + [P, ctypes.POINTER(P)]),
         "gdn_graph_launch": (ctypes.c_int, [P, P]),
         "gdn_graph_destroy": (ctypes.c_int, [P]),
+        "gdn_prefill_scan_blockwise": (ctypes.c_int, [D, ctypes.c_int64] + [P] * 9 + [sz, P]),
         "gdn_prefill_segmented_workspace_bytes": (sz, [D, ctypes.c_int64, ctypes.c_int32]),
         "gdn_prefill_segmented": (ctypes.c_int, [D, ctypes.c_int64, ctypes.c_int32] + [P] * 9
                                   + [sz, P]),
@@ -174,6 +175,20 @@ def gdn_prefill_scan(q, k, v, g, beta, state_in=None, *, l2_eps=1e-6, out=None,
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
         _ptr(out), _ptr(state_out), _ptr(workspace), wbytes, _stream(q.device, stream)),
         "gdn_prefill_scan")
+    return out, state_out
+
+
+def gdn_prefill_scan_blockwise(q, k, v, g, beta, state_in=None, *, block_t, l2_eps=1e-6,
+                               out=None, state_out=None, workspace=None, stream=None):
+    """The residency ablation of gdn_prefill_scan: one scan launch per block of block_t
+    tokens, the state written to and read back from state_out between blocks. Returns
+    (out, state_out)."""
+    dims, out, state_out = _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps)
+    workspace, wbytes = _workspace(dims, 0, workspace, q.device)
+    _check(_load().gdn_prefill_scan_blockwise(
+        ctypes.byref(dims), int(block_t), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace), wbytes,
+        _stream(q.device, stream)), "gdn_prefill_scan_blockwise")
     return out, state_out
 
 

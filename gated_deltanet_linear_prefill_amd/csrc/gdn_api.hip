@@ -359,6 +359,21 @@ gdn_status gdn_prefill_scan(const gdn_dims* d, const void* q, const void* k, con
     return finish(c.t == 0 ? launch_state_passthrough(c) : launch_scan(c));
 }
 
+gdn_status gdn_prefill_scan_blockwise(const gdn_dims* d, int64_t block_t, const void* q,
+                                      const void* k, const void* v, const float* g,
+                                      const float* beta, const float* state_in, float* out,
+                                      float* state_out, void* ws, size_t ws_bytes, void* stream)
+{
+    if (d && block_t <= 0) return GDN_ERR_SHAPE;
+    Call c;
+    gdn_status st = validate(d, 0, q, k, v, g, beta, state_in, out, state_out, ws, ws_bytes, &c);
+    if (st != GDN_OK) return st;
+    if (c.n == 0) return GDN_OK;
+    c.stream = static_cast<hipStream_t>(stream);
+    (void)hipGetLastError();
+    return finish(c.t == 0 ? launch_state_passthrough(c) : launch_scan_blockwise(c, block_t));
+}
+
 gdn_status gdn_decode_step(const gdn_dims* d, const void* q, const void* k, const void* v,
                            const float* g, const float* beta, const float* state_in,
                            float* out, float* state_out, void* stream)

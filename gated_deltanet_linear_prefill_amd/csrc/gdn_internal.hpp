@@ -27,6 +27,7 @@ struct Call {
 // launches. The caller has validated everything the kernels assume.
 hipError_t launch_decode(const Call& c);
 hipError_t launch_scan(const Call& c);
+hipError_t launch_scan_blockwise(const Call& c, int64_t block_t);  // block_t > 0
 // parts: kChunkPrep (the per-chunk preparation into the workspace), kChunkScan (the
 // sequential pass that reads it), or both; the scan must follow a prep of the same call.
 constexpr int kChunkPrep = 1, kChunkScan = 2;

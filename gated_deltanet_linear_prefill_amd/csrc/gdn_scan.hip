@@ -191,6 +191,42 @@ hipError_t launch_scan_t(const Call& c)
     return hipGetLastError();
 }
 
+// The ablation of state residency: the same normalisation and scan kernels, but the scan is
+// launched once per block of block_t tokens of each sequence, so the state leaves the chip
+// after every block (written to state_out, read back by the next block's launch).
+template <int D, typename TIn>
+hipError_t launch_scan_blockwise_t(const Call& c, int64_t block_t)
+{
+    const ScanWs w = scan_ws_layout(c.n, c.t, c.h_qk, D);
+    char* ws = static_cast<char*>(c.ws);
+    const float* qhat = reinterpret_cast<const float*>(ws + w.qhat);
+    const float* khat = reinterpret_cast<const float*>(ws + w.khat);
+    const float* qk = reinterpret_cast<const float*>(ws + w.qk);
+    const int64_t rows = c.n * c.t * c.h_qk;
+    hipLaunchKernelGGL((qk_normalise_kernel<D, TIn>), dim3((unsigned)((rows + 15) / 16)), dim3(256),
+                       0, c.stream, static_cast<const TIn*>(c.q), static_cast<const TIn*>(c.k),
+                       rows, c.eps, reinterpret_cast<float*>(ws + w.qhat),
+                       reinterpret_cast<float*>(ws + w.khat), reinterpret_cast<float*>(ws + w.qk));
+    hipError_t e = hipGetLastError();
+    const TIn* v = static_cast<const TIn*>(c.v);
+    const int64_t state_elems = (int64_t)c.h_v * D * D;
+    for (int64_t s = 0; s < c.n && e == hipSuccess; ++s) {
+        for (int64_t t0 = 0; t0 < c.t && e == hipSuccess; t0 += block_t) {
+            const int64_t len = c.t - t0 < block_t ? c.t - t0 : block_t;
+            const int64_t tok = s * c.t + t0;
+            const float* si = t0 == 0 ? (c.state_in ? c.state_in + s * state_elems : nullptr)
+                                      : c.state_out + s * state_elems;
+            hipLaunchKernelGGL((scan_kernel<D, TIn>), dim3((unsigned)(c.h_v * (D / 16))), dim3(256), 0,
+                               c.stream, qhat + tok * c.h_qk * D, khat + tok * c.h_qk * D,
+                               qk + tok * c.h_qk, v + tok * c.h_v * D, c.g + tok * c.h_v,
+                               c.beta + tok * c.h_v, si, c.out + tok * c.h_v * D,
+                               c.state_out + s * state_elems, len, c.h_qk, c.h_v);
+            e = hipGetLastError();
+        }
+    }
+    return e;
+}
+
 template <typename TIn>
 hipError_t dispatch_d(const Call& c)
 {
@@ -199,6 +235,18 @@ hipError_t dispatch_d(const Call& c)
         case 32: return launch_scan_t<32, TIn>(c);
         case 64: return launch_scan_t<64, TIn>(c);
         case 128: return launch_scan_t<128, TIn>(c);
+        default: return hipErrorInvalidValue;
+    }
+}
+
+template <typename TIn>
+hipError_t dispatch_blockwise(const Call& c, int64_t block_t)
+{
+    switch (c.d) {
+        case 16: return launch_scan_blockwise_t<16, TIn>(c, block_t);
+        case 32: return launch_scan_blockwise_t<32, TIn>(c, block_t);
+        case 64: return launch_scan_blockwise_t<64, TIn>(c, block_t);
+        case 128: return launch_scan_blockwise_t<128, TIn>(c, block_t);
         default: return hipErrorInvalidValue;
     }
 }
@@ -214,6 +262,12 @@ size_t scan_workspace_bytes(int64_t n, int64_t t, int32_t h_qk, int32_t h_v, int
 hipError_t launch_scan(const Call& c)
 {
     return c.dtype == GDN_BF16 ? dispatch_d<uint16_t>(c) : dispatch_d<float>(c);
+}
+
+hipError_t launch_scan_blockwise(const Call& c, int64_t block_t)
+{
+    return c.dtype == GDN_BF16 ? dispatch_blockwise<uint16_t>(c, block_t)
+                               : dispatch_blockwise<float>(c, block_t);
 }
 
 }  // namespace gdn

@@ -36,6 +36,7 @@ TINY = Shape(n=1, t=64, h_qk=1, h_v=2, d=16, dtype=torch.float32)
 PREFILL_4K = Shape(n=1, t=4096, h_qk=16, h_v=32, d=128)
 DECODE_30L = Shape(n=30, t=1, h_qk=16, h_v=32, d=128)
 LONG_SEGMENT = Shape(n=1, t=4096, h_qk=16, h_v=32, d=128)  # 32 segments = 131072 tokens
+ABLATION_2K = Shape(n=1, t=2048, h_qk=16, h_v=32, d=128)   # the state-residency ablation prompt
 LONG_SEGMENTS = 32
 SWEEP_T = (256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072)
 SWEEP_CHUNKS = (32, 64, 128)

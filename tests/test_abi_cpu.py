@@ -329,3 +329,26 @@ def test_segmented_workspace_bytes(lib):
     slot = (max(one, last) + 255) // 256 * 256
     assert lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(ragged), 4096, 1) == 2 * slot
     assert lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(ragged), 4096, 2) == 0
+
+
+# ------------------------------------------------------------------ blockwise scan ablation (no GPU)
+def test_scan_blockwise_validation(lib):
+    """Validated like gdn_prefill_scan before any launch; block_t must be positive."""
+    b = Bufs(t=64)
+    a = {key: b.p(key) for key in ("q", "k", "v", "g", "beta", "state_in", "out", "state_out",
+                                    "ws")}
+
+    def call(block_t=16, ws_bytes=64 * MB, **over):
+        x = dict(a, **over)
+        return lib.gdn_prefill_scan_blockwise(ctypes.byref(b.dims), block_t, x["q"], x["k"],
+                                              x["v"], x["g"], x["beta"], x["state_in"],
+                                              x["out"], x["state_out"], x["ws"], ws_bytes, None)
+
+    assert lib.gdn_prefill_scan_blockwise(None, 16, *[None] * 9, 0, None) == NULL
+    assert call(block_t=0) == SHAPE
+    assert call(block_t=-1) == SHAPE
+    assert call(q=None) == NULL
+    assert call(ws=None) == WS
+    assert call(ws_bytes=16) == WS
+    assert call(out=b.p("q")) == ALIAS
+    assert call(out=b.p("out", 4)) == ALIGN
