@@ -80,8 +80,13 @@ scan_kernel(const float* __restrict__ qhat, const float* __restrict__ khat,
     constexpr int NCB = D / 16;  // 16-column blocks per head
     constexpr int ST = 4;        // tokens per pipeline stage
 
-    const int64_t nh = blockIdx.x / NCB;  // sequence * h_v + V head
-    const int cb = blockIdx.x % NCB;
+    // Workgroups that share a QK head's normalised rows (its V heads' column blocks, which
+    // are consecutive in `lin`) run on one XCD (blockIdx % 8 picks the XCD), so those rows
+    // are fetched into one L2 rather than into all eight.
+    int64_t lin = blockIdx.x;
+    if (gridDim.x % 8 == 0) lin = (int64_t)(blockIdx.x % 8) * (gridDim.x / 8) + blockIdx.x / 8;
+    const int64_t nh = lin / NCB;  // sequence * h_v + V head
+    const int cb = (int)(lin % NCB);
     const int64_t seq = nh / h_v;
     const int h = (int)(nh - seq * h_v);
     const int hq = h / (h_v / h_qk);
