@@ -32,7 +32,8 @@ three layers; --mode pmc-copy runs a device copy of known size for counter calib
 overlapped, for a kernel trace; --mode ablation times the state-residency ablation at 2048
 tokens (resident direct scan, the same scan with the state through device memory every 32
 tokens, and the chunked call) and prints one JSON line of its own; --mode pmc-ablation makes
-one call of each scan form for counter collection.
+one call of each scan form for counter collection; --mode pmc-mfma runs one MFMA loop of
+known flops (calibration of the MFMA counters).
 """
 import argparse
 import json
@@ -45,6 +46,7 @@ sys.path.insert(0, ROOT)
 
 T_PROMPT, LAYERS, H_QK, H_V, D = 4096, 30, 16, 32, 128
 HBM_PEAK_GBS = 8000.0
+BF16_PEAK_TFLOPS = 2500.0  # dense bf16 MFMA, published
 COPY_BYTES = 256 << 20
 METRIC = "GDN prefill tokens/s at T=4096 x30 layers; decode step us/token; % roofline"
 
@@ -59,7 +61,7 @@ def parse():
                     help="skip the measurements after the timed region (their fields are null), "
                          "so that a kernel trace holds only the timed step's kernels")
     ap.add_argument("--mode", choices=["bench", "pmc-prefill", "pmc-copy", "segmented",
-                                       "ablation", "pmc-ablation"], default="bench")
+                                       "ablation", "pmc-ablation", "pmc-mfma"], default="bench")
     return ap.parse_args()
 
 
@@ -71,6 +73,12 @@ def prefill_bytes():
     out = T_PROMPT * H_V * D * 4
     st = H_V * D * D * 4
     return 2 * qk + v + 2 * gb + out + st
+
+
+def prefill_flops(chunk):
+    """Algorithmic flops of one chunked prefill call: (6 d^2 + 4 C d) per token and V head
+    (the state products, the Gram terms once per QK head, triangles counted as half)."""
+    return (6 * D * D + 4 * chunk * D) * T_PROMPT * H_V
 
 
 def decode_bytes():
@@ -165,6 +173,20 @@ def reference_rates(gdn, dec, dec_out, pre, dev):
         seg[ov] = (us, seg_ws.numel())
         del seg_ws
     del seg_out, seg_st
+    # The achievable dense bf16 MFMA rate: a loop of independent MFMAs over the whole chip.
+    sink = torch.empty(1024 * 256, device=dev)
+    gdn.calib_mfma_bf16(100, 1024, sink)
+    torch.cuda.synchronize()
+    best = float("inf")
+    for _ in range(3):
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        flops = gdn.calib_mfma_bf16(4000, 1024, sink)
+        e0.record()
+        torch.cuda.synchronize()
+        best = min(best, s0.elapsed_time(e0) * 1e-3)
+    mfma_tflops = flops / best / 1e12
+    del sink
     a = torch.empty(1 << 28, device=dev)
     b = torch.empty_like(a)
     b.copy_(a)
@@ -177,7 +199,7 @@ def reference_rates(gdn, dec, dec_out, pre, dev):
     copy_gbs = 2 * a.numel() * 4 * 5 / (s.elapsed_time(e) * 1e-3) / 1e9
     return {"decode_cold_us": cold_us, "copy_GBps": copy_gbs,
             "layers_eager_us": layers_eager_us, "layers_graph_us": layers_graph_us,
-            "seg": seg}
+            "seg": seg, "mfma_tflops": mfma_tflops}
 
 
 def ablation(gdn, gdn_inputs, dev, counters):
@@ -232,6 +254,19 @@ def ablation(gdn, gdn_inputs, dev, counters):
                       "state_bytes_resident": state_bytes, "chunk": chunk, **res}), flush=True)
 
 
+def matrix_fields(chunk, call_s, extra):
+    """The chunked call's algorithmic MFMA rate against the published dense bf16 peak and
+    against the MFMA loop's achievable rate (null when that was skipped)."""
+    if not chunk:
+        return None
+    flops = prefill_flops(chunk)
+    tf = flops / call_s / 1e12
+    loop = (extra or {}).get("mfma_tflops")
+    return {"algorithmic_flops_per_call": flops, "achieved_TFLOPs": tf,
+            "peak_TFLOPs": BF16_PEAK_TFLOPS, "frac_peak": tf / BF16_PEAK_TFLOPS,
+            "loop_TFLOPs": loop, "frac_loop": tf / loop if loop else None}
+
+
 def extra_fields(extra):
     """The JSON fields of reference_rates (null when it was skipped)."""
     e = extra or {}
@@ -247,6 +282,7 @@ def extra_fields(extra):
         "prefill_segmented_1024_overlapped_us_per_layer": seg.get(True, (None, None))[0],
         "prefill_segmented_1024_overlapped_workspace_bytes": seg.get(True, (None, None))[1],
         "hbm_copy_GBps": e.get("copy_GBps"),
+        "mfma_bf16_loop_TFLOPs": e.get("mfma_tflops"),
     }
 
 
@@ -264,11 +300,18 @@ def cpu_baseline():
         spent += time.perf_counter() - t0
         layers += 1
     per_layer = spent / layers
+    # the same oracle on one thread, one layer, for the scaling of the host figure
+    c = gdn_inputs.make_case(gdn_inputs.PREFILL_4K, seed=100)
+    t0 = time.perf_counter()
+    oracle.run(c["q"], c["k"], c["v"], c["g"], c["beta"], None, threads=1)
+    one = time.perf_counter() - t0
     return {"value": T_PROMPT / (LAYERS * per_layer), "unit": "tokens/s", "cores": threads,
             "kind": "oracle",
             "sample": f"{layers} layer(s) of the prefill workload (T=4096, 32 V heads, d=128, "
                       f"each its own inputs), {spent:.1f} s of oracle time; value = 4096 / "
-                      f"(30 x mean layer time)"}
+                      f"(30 x mean layer time)",
+            "one_thread_layer_s": one,
+            "one_thread_value": T_PROMPT / (LAYERS * one)}
 
 
 def main():
@@ -297,6 +340,12 @@ def main():
         print(f"copied {COPY_BYTES} bytes x3", flush=True)
         return
 
+    if args.mode == "pmc-mfma":
+        sink = torch.empty(1024 * 256, device=dev)
+        flops = gdn.calib_mfma_bf16(200, 1024, sink)
+        torch.cuda.synchronize()
+        print(f"MFMA loop done: {flops} flops", flush=True)
+        return
     if args.mode in ("ablation", "pmc-ablation"):
         ablation(gdn, gdn_inputs, dev, counters=args.mode == "pmc-ablation")
         return
@@ -401,6 +450,7 @@ def main():
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
                      "kernel": "gdn_prefill_chunked call (chunk_prep_kernel + chunk_scan_kernel)",
                      "algorithmic_bytes_per_call": prefill_bytes()},
+        "matrix": matrix_fields(chunk, mean_call_s, extra),
     }
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline()

@@ -20,6 +20,7 @@ __all__ = [
     "gdn_prefill", "gdn_prefill_workspace_bytes", "library_path", "Dims", "BoundCall",
     "bind_prefill_chunked", "bind_prefill_scan", "bind_decode_step", "DecodeGraph",
     "gdn_prefill_segmented", "gdn_prefill_segmented_workspace_bytes", "gdn_prefill_scan_blockwise",
+    "calib_mfma_bf16",
 ]
 
 GDN_F32, GDN_BF16 = 0, 1
@@ -68,6 +69,8 @@ def _load():
         "gdn_decode_graph_create": (ctypes.c_int, [D, i32] + [ctypes.POINTER(P)] * 7 + [P, ctypes.POINTER(P)]),
         "gdn_graph_launch": (ctypes.c_int, [P, P]),
         "gdn_graph_destroy": (ctypes.c_int, [P]),
+        "gdn_calib_mfma_bf16_flops": (ctypes.c_int64, [ctypes.c_int64, ctypes.c_int32]),
+        "gdn_calib_mfma_bf16": (ctypes.c_int, [ctypes.c_int64, ctypes.c_int32, P, P]),
         "gdn_prefill_scan_blockwise": (ctypes.c_int, [D, ctypes.c_int64] + [P] * 9 + [sz, P]),
         "gdn_prefill_segmented_workspace_bytes": (sz, [D, ctypes.c_int64, ctypes.c_int32]),
         "gdn_prefill_segmented": (ctypes.c_int, [D, ctypes.c_int64, ctypes.c_int32] + [P] * 9
@@ -190,6 +193,15 @@ def gdn_prefill_scan_blockwise(q, k, v, g, beta, state_in=None, *, block_t, l2_e
         _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace), wbytes,
         _stream(q.device, stream)), "gdn_prefill_scan_blockwise")
     return out, state_out
+
+
+def calib_mfma_bf16(iters, blocks, sink, stream=None) -> int:
+    """Launch the bf16 MFMA loop (measurement only) into `sink` (a float32 device tensor of
+    at least blocks * 256 elements); returns the flops the launch performs."""
+    assert sink.dtype == torch.float32 and sink.is_cuda and sink.numel() >= blocks * 256
+    _check(_load().gdn_calib_mfma_bf16(int(iters), int(blocks), _ptr(sink),
+                                       _stream(sink.device, stream)), "gdn_calib_mfma_bf16")
+    return int(_load().gdn_calib_mfma_bf16_flops(int(iters), int(blocks)))
 
 
 def gdn_decode_step(q, k, v, g, beta, state_in=None, *, l2_eps=1e-6, out=None,

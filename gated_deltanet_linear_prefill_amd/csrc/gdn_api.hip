@@ -172,6 +172,8 @@ __global__ void state_passthrough_kernel(const float4* __restrict__ src, float4*
         dst[i] = src ? src[i] : make_float4(0.f, 0.f, 0.f, 0.f);
 }
 
+constexpr int32_t kMaxCalibBlocks = 1 << 20;
+
 int32_t choose_chunk(const gdn_dims* d)
 {
     int32_t pick = kCrossover[0].chunk;
@@ -580,6 +582,22 @@ gdn_status gdn_prefill(const gdn_dims* d, const void* q, const void* k, const vo
                                          ws_bytes, stream)
                       : gdn_prefill_chunked(d, chunk, q, k, v, g, beta, state_in, out,
                                             state_out, ws, ws_bytes, stream);
+}
+
+int64_t gdn_calib_mfma_bf16_flops(int64_t iters, int32_t blocks)
+{
+    if (iters <= 0 || blocks <= 0 || blocks > kMaxCalibBlocks) return 0;
+    // 4 waves per workgroup, 4 MFMAs per iteration, 32 x 32 x 16 multiply-adds each
+    return (int64_t)blocks * 4 * iters * 4 * (32 * 32 * 16 * 2);
+}
+
+gdn_status gdn_calib_mfma_bf16(int64_t iters, int32_t blocks, float* sink, void* stream)
+{
+    if (!sink) return GDN_ERR_NULL;
+    if (iters <= 0 || blocks <= 0 || blocks > kMaxCalibBlocks) return GDN_ERR_SHAPE;
+    if (!aligned(sink, 4)) return GDN_ERR_ALIGN;
+    (void)hipGetLastError();
+    return finish(launch_mfma_loop(iters, blocks, sink, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

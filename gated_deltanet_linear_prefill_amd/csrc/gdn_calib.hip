@@ -1,0 +1,51 @@
+// gdn_calib.hip -- a loop of dense bf16 MFMAs, for the achievable matrix rate that the
+// chunked kernels' MFMA use is reported against (measurement only; the prefill and decode
+// paths never call it).
+//
+// Each wave keeps four independent 32x32x16 accumulators, so consecutive MFMAs never wait
+// for each other, and writes one sum per lane at the end so that nothing is optimised away.
+// (On gfx950 the 32x32x16 bf16 form sustains about 2.0 PFLOP/s in such a loop, the 16x16x32
+// form about 1.2-1.4: measured, the former is the achievable figure.)
+#include "gdn_internal.hpp"
+
+namespace gdn {
+namespace {
+
+typedef __bf16 calib_bf16x8 __attribute__((ext_vector_type(8)));
+typedef float calib_floatx16 __attribute__((ext_vector_type(16)));
+
+__global__ void __launch_bounds__(256) mfma_loop_kernel(int64_t iters, float* __restrict__ sink)
+{
+    const int l = threadIdx.x & 63;
+    calib_bf16x8 a, b;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        a[i] = (__bf16)(0.001f * (float)(l + i));
+        b[i] = (__bf16)(0.002f * (float)(l - i));
+    }
+    calib_floatx16 acc[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) acc[j][e] = 0.f;
+    for (int64_t it = 0; it < iters; ++it) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, acc[j], 0, 0, 0);
+    }
+    float s = 0.f;
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+#pragma unroll
+        for (int e = 0; e < 16; ++e) s += acc[j][e];
+    sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
+}
+
+}  // namespace
+
+hipError_t launch_mfma_loop(int64_t iters, int32_t blocks, float* sink, hipStream_t stream)
+{
+    hipLaunchKernelGGL(mfma_loop_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, iters, sink);
+    return hipGetLastError();
+}
+
+}  // namespace gdn

@@ -250,6 +250,19 @@ gdn_status gdn_prefill_segmented(const gdn_dims* dims, int64_t seg_t, int32_t ov
                                  float* state_out, void* workspace, size_t workspace_bytes,
                                  void* stream);
 
+/*
+ * Calibration (measurement only): `blocks` workgroups of four waves each issue `iters`
+ * rounds of four independent 32x32x16 bf16 MFMAs on `stream`, then write one float per
+ * lane to `sink` (device memory of blocks x 256 floats, contents meaningless). The
+ * achievable dense bf16 rate is gdn_calib_mfma_bf16_flops(iters, blocks) divided by the
+ * launch time; the chunked kernels' MFMA rate is reported against it and against the
+ * published peak. GDN_ERR_NULL for a NULL sink, GDN_ERR_SHAPE unless iters > 0 and
+ * 0 < blocks <= 2^20, GDN_ERR_ALIGN for a sink not 4-byte aligned. The flop count is 0
+ * for invalid arguments.
+ */
+int64_t gdn_calib_mfma_bf16_flops(int64_t iters, int32_t blocks);
+gdn_status gdn_calib_mfma_bf16(int64_t iters, int32_t blocks, float* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

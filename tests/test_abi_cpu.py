@@ -352,3 +352,17 @@ def test_scan_blockwise_validation(lib):
     assert call(ws_bytes=16) == WS
     assert call(out=b.p("q")) == ALIAS
     assert call(out=b.p("out", 4)) == ALIGN
+
+
+# ------------------------------------------------------------------ MFMA calibration loop (no GPU)
+def test_calib_validation(lib):
+    """Arguments are checked before any launch; the flop count follows the loop's shape."""
+    sink = ctypes.c_void_p(0x100000)
+    assert lib.gdn_calib_mfma_bf16(10, 4, None, None) == NULL
+    assert lib.gdn_calib_mfma_bf16(0, 4, sink, None) == SHAPE
+    assert lib.gdn_calib_mfma_bf16(10, 0, sink, None) == SHAPE
+    assert lib.gdn_calib_mfma_bf16(10, (1 << 20) + 1, sink, None) == SHAPE
+    assert lib.gdn_calib_mfma_bf16(10, 4, ctypes.c_void_p(0x100002), None) == ALIGN
+    assert lib.gdn_calib_mfma_bf16_flops(10, 4) == 4 * 4 * 10 * 4 * 32 * 32 * 16 * 2
+    assert lib.gdn_calib_mfma_bf16_flops(0, 4) == 0
+    assert lib.gdn_calib_mfma_bf16_flops(10, -1) == 0
