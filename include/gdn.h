@@ -43,13 +43,17 @@
  * n counts independent sequences; for the stacked decode step it counts layers.
  *
  * Pointers and ownership. Every data pointer is a DEVICE pointer on the current HIP
- * device. The caller allocates and owns every buffer, including the workspace. Apart from
- * the decode graph handle (gdn_decode_graph_create, which owns the HIP graph it records),
- * the library never allocates, frees or synchronises, keeps no mutable global state, and
- * is safe to call from several host threads. Every compute call only enqueues kernels on
- * `stream` (a hipStream_t; NULL is the default stream) and returns; results are ready
- * when the stream reaches that point. The compute calls make no memset or copy calls, so
- * they may be recorded under HIP stream capture.
+ * device. The caller allocates and owns every buffer, including the workspace. The
+ * library never allocates device memory, frees or synchronises, and is safe to call from
+ * several host threads, with two exceptions that hold runtime objects: the decode graph
+ * handle (gdn_decode_graph_create owns the HIP graph it records until
+ * gdn_graph_destroy), and the overlapped schedule of gdn_prefill_segmented, which creates
+ * one side stream and a few events per device on first use, keeps them until the process
+ * ends, and serialises the calls that enqueue on them. Every compute call only enqueues
+ * kernels on `stream` (a hipStream_t; NULL is the default stream) and returns; results are
+ * ready when the stream reaches that point. The compute calls make no memset or copy
+ * calls, so they may be recorded under HIP stream capture (except the overlapped
+ * segmented schedule, which refuses a capturing stream).
  *
  * Alignment. q, k, v, state_in, state_out, out and workspace must be 16-byte aligned;
  * g and beta 4-byte aligned.
@@ -77,7 +81,7 @@
 extern "C" {
 #endif
 
-#define GDN_ABI_VERSION 1
+#define GDN_ABI_VERSION 2
 
 typedef enum {
     GDN_OK = 0,
