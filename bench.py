@@ -33,7 +33,8 @@ overlapped, for a kernel trace; --mode ablation times the state-residency ablati
 tokens (resident direct scan, the same scan with the state through device memory every 32
 tokens, and the chunked call) and prints one JSON line of its own; --mode pmc-ablation makes
 one call of each scan form for counter collection; --mode pmc-mfma runs one MFMA loop of
-known flops (calibration of the MFMA counters).
+known flops (calibration of the MFMA counters); --mode pmc-decode runs three stacked decode
+steps (30 layers).
 """
 import argparse
 import json
@@ -61,7 +62,8 @@ def parse():
                     help="skip the measurements after the timed region (their fields are null), "
                          "so that a kernel trace holds only the timed step's kernels")
     ap.add_argument("--mode", choices=["bench", "pmc-prefill", "pmc-copy", "segmented",
-                                       "ablation", "pmc-ablation", "pmc-mfma"], default="bench")
+                                       "ablation", "pmc-ablation", "pmc-mfma", "pmc-decode"],
+                    default="bench")
     return ap.parse_args()
 
 
@@ -375,6 +377,12 @@ def main():
             calls[l]()
         torch.cuda.synchronize()
         print("prefill calls done", flush=True)
+        return
+    if args.mode == "pmc-decode":
+        for _ in range(3):
+            decode()
+        torch.cuda.synchronize()
+        print("decode steps done", flush=True)
         return
     if args.mode == "segmented":
         c = layers[0]

@@ -29,6 +29,6 @@ def test_help_lists_the_modes():
     r = run_bench("--help")
     assert r.returncode == 0
     for mode in ("bench", "pmc-prefill", "pmc-copy", "segmented", "ablation", "pmc-ablation",
-                 "pmc-mfma"):
+                 "pmc-mfma", "pmc-decode"):
         assert mode in r.stdout
     assert "--core-only" in r.stdout
