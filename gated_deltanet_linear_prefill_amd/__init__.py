@@ -58,7 +58,7 @@ def _load():
     i32, sz = ctypes.c_int32, ctypes.c_size_t
     sig = {
         "gdn_abi_version": (i32, []),
-        "gdn_status_str": (ctypes.c_char_p, [ctypes.c_int]),
+        "gdn_status_str": (ctypes.c_char_p, [ctypes.c_int32]),
         "gdn_workspace_bytes": (sz, [D, i32]),
         "gdn_prefill_chunked": (ctypes.c_int, [D, i32] + [P] * 9 + [sz, P]),
         "gdn_prefill_scan": (ctypes.c_int, [D] + [P] * 9 + [sz, P]),

@@ -309,7 +309,7 @@ int32_t gdn_abi_version(void)
     return GDN_ABI_VERSION;
 }
 
-const char* gdn_status_str(gdn_status s)
+const char* gdn_status_str(int32_t s)
 {
     switch (s) {
         case GDN_OK: return "GDN_OK: success";

@@ -110,8 +110,9 @@ typedef struct {
 /* Version of this header the library was built from (GDN_ABI_VERSION). */
 int32_t gdn_abi_version(void);
 
-/* Static string for a status code; never NULL. */
-const char* gdn_status_str(gdn_status status);
+/* Static string for a status code (any int32_t: a value that is no gdn_status gives an
+ * "unknown status" string); never NULL. */
+const char* gdn_status_str(int32_t status);
 
 /*
  * Workspace bytes a call needs: chunk in {16,32,64,128} for gdn_prefill_chunked, chunk 0
