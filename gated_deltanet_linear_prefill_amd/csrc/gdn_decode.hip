@@ -28,7 +28,9 @@ struct DecodeCfg {
     static constexpr int CG = DC / 4;                                  // float4 per row segment
     static constexpr int RG = NT / CG;                                 // row groups
     static constexpr int RPT = D / RG;                                 // rows per thread
+    static constexpr int NW = NT / 64;                                 // waves
     static_assert(RG * RPT == D && CG * RG == NT, "decode tiling");
+    static_assert(NT % 64 == 0 && 64 % CG == 0, "a wave holds whole row groups");
 };
 
 template <int D, int SPLIT, typename TIn>
@@ -39,9 +41,9 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* _
               int h_v, float eps)
 {
     using Cfg = DecodeCfg<D, SPLIT>;
-    constexpr int CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT;
+    constexpr int CG = Cfg::CG, RG = Cfg::RG, RPT = Cfg::RPT, NW = Cfg::NW;
     __shared__ float s_q[D], s_k[D], s_norm[3];
-    __shared__ float4 s_part[RG][CG][2];
+    __shared__ float4 s_part[NW][CG][2];
 
     const int64_t nh = blockIdx.x / SPLIT;  // sequence * h_v + V head
     const int cb = (int)(blockIdx.x % SPLIT) * Cfg::DC;  // first channel of this workgroup
@@ -101,14 +103,25 @@ decode_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const TIn* _
         pk.x += ki * m[r].x; pk.y += ki * m[r].y; pk.z += ki * m[r].z; pk.w += ki * m[r].w;
         pq.x += qi * m[r].x; pq.y += qi * m[r].y; pq.z += qi * m[r].z; pq.w += qi * m[r].w;
     }
-    s_part[rg][cg][0] = pk;
-    s_part[rg][cg][1] = pq;
+    // 5. Column sums in a fixed order (so the result is deterministic): first over the row
+    // groups of a wave (lanes CG apart hold the same columns) by cross-lane exchanges, then
+    // over the waves through LDS.
+#pragma unroll
+    for (int off = CG; off < 64; off *= 2) {
+        pk.x += __shfl_xor(pk.x, off); pk.y += __shfl_xor(pk.y, off);
+        pk.z += __shfl_xor(pk.z, off); pk.w += __shfl_xor(pk.w, off);
+        pq.x += __shfl_xor(pq.x, off); pq.y += __shfl_xor(pq.y, off);
+        pq.z += __shfl_xor(pq.z, off); pq.w += __shfl_xor(pq.w, off);
+    }
+    const int wave = tid / 64;
+    if ((tid & 63) < CG) {
+        s_part[wave][cg][0] = pk;
+        s_part[wave][cg][1] = pq;
+    }
     __syncthreads();
-
-    // 5. Column sums (fixed order, so the result is deterministic), output, update.
     float4 tk = make_float4(0.f, 0.f, 0.f, 0.f), tq = tk;
 #pragma unroll
-    for (int j = 0; j < RG; ++j) {
+    for (int j = 0; j < NW; ++j) {
         const float4 a = s_part[j][cg][0], c = s_part[j][cg][1];
         tk.x += a.x; tk.y += a.y; tk.z += a.z; tk.w += a.w;
         tq.x += c.x; tq.y += c.y; tq.z += c.z; tq.w += c.w;
