@@ -25,7 +25,7 @@ import torch
 PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 TABLE = os.path.join(PKG, "csrc", "gdn_crossover.inc")
-LENGTHS = (16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072)
+LENGTHS = (1, 4, 8, 16, 32, 64, 128, 256, 512, 1024, 2048, 4096, 8192, 16384, 32768, 65536, 131072)
 CHUNKS = (16, 32, 64, 128)
 H_QK, H_V, D = 16, 32, 128
 
