@@ -96,9 +96,8 @@ size_t workspace_for(const gdn_dims* d, int32_t chunk)
 }
 
 // Validate one call. mode: a chunk size (chunked), 0 (direct scan), -1 (decode, t == 1,
-// no workspace) or -2 (no workspace
-// and no method-specific limit: the whole of a segmented call, whose segments are
-// validated again as they are issued).
+// no workspace) or -2 (no workspace and no method-specific limit: the whole of a segmented
+// call, whose segments are validated again as they are issued).
 gdn_status validate(const gdn_dims* d, int32_t mode, const void* q, const void* k,
                     const void* v, const float* g, const float* beta, const float* state_in,
                     float* out, float* state_out, void* ws, size_t ws_bytes, Call* call)
@@ -182,6 +181,19 @@ int32_t choose_chunk(const gdn_dims* d)
     return pick;
 }
 
+// What gdn_prefill runs: kDecodeMethod for a single token (the decode step does the same
+// arithmetic in one launch, with no workspace), else the table's choice (0 = direct scan).
+constexpr int32_t kDecodeMethod = -1;
+int32_t prefill_method(const gdn_dims* d)
+{
+    return d->t == 1 ? kDecodeMethod : choose_chunk(d);
+}
+
+size_t method_workspace(const gdn_dims* d, int32_t method)
+{
+    return method == kDecodeMethod ? 0 : workspace_for(d, method);
+}
+
 // ---------------------------------------------------------------- segmented prefill
 
 // One segment of one sequence: a gdn_prefill call on sub-ranges of the whole call's buffers.
@@ -239,10 +251,10 @@ size_t segment_workspace_bytes(const gdn_dims* d, int64_t seg_t)
     gdn_dims one = *d;
     one.n = 1;
     one.t = d->t < seg_t ? d->t : seg_t;
-    size_t need = workspace_for(&one, choose_chunk(&one));
+    size_t need = method_workspace(&one, prefill_method(&one));
     if (d->t % seg_t != 0 && d->t > seg_t) {
         one.t = d->t % seg_t;
-        const size_t last = workspace_for(&one, choose_chunk(&one));
+        const size_t last = method_workspace(&one, prefill_method(&one));
         need = last > need ? last : need;
     }
     return need;
@@ -436,7 +448,7 @@ gdn_status gdn_prefill_segmented(const gdn_dims* d, int64_t seg_t, int32_t overl
         gdn_dims one = *d;
         one.n = 1;
         one.t = len;
-        st = validate(&one, choose_chunk(&one), q, k, v, g, beta, state_in, out, state_out,
+        st = validate(&one, prefill_method(&one), q, k, v, g, beta, state_in, out, state_out,
                       nullptr, 0, &c);
         if (st != GDN_OK && st != GDN_ERR_WORKSPACE) return st;
     }
@@ -470,11 +482,14 @@ gdn_status gdn_prefill_segmented(const gdn_dims* d, int64_t seg_t, int32_t overl
         const Piece x = plan.piece(p);
         const int sl = (int)(p & 1);
         void* wsp = static_cast<char*>(ws) + sl * slot;
-        const int32_t chunk = choose_chunk(&x.dims);
+        const int32_t chunk = prefill_method(&x.dims);
         st = validate(&x.dims, chunk, x.q, x.k, x.v, x.g, x.beta, x.state_in, x.out,
                       x.state_out, wsp, slot, &c);
         if (st != GDN_OK) break;
-        if (chunk > 0) {
+        if (chunk == kDecodeMethod) {
+            c.stream = main_s;
+            e = launch_decode(c);
+        } else if (chunk > 0) {
             // the slot's previous user (segment p - 2) has finished its sequential pass
             if (p >= 2) e = hipStreamWaitEvent(side->stream, side->scan[sl], 0);
             c.stream = side->stream;
@@ -568,7 +583,7 @@ size_t gdn_prefill_workspace_bytes(const gdn_dims* d)
 {
     Sizes s;
     if (check_dims(d, &s) != GDN_OK) return 0;
-    return workspace_for(d, choose_chunk(d));
+    return method_workspace(d, prefill_method(d));
 }
 
 gdn_status gdn_prefill(const gdn_dims* d, const void* q, const void* k, const void* v,
@@ -578,6 +593,7 @@ gdn_status gdn_prefill(const gdn_dims* d, const void* q, const void* k, const vo
     int32_t chunk = 0;
     gdn_status st = gdn_prefill_choose(d, &chunk);
     if (st != GDN_OK) return st;
+    if (d->t == 1) return gdn_decode_step(d, q, k, v, g, beta, state_in, out, state_out, stream);
     return chunk == 0 ? gdn_prefill_scan(d, q, k, v, g, beta, state_in, out, state_out, ws,
                                          ws_bytes, stream)
                       : gdn_prefill_chunked(d, chunk, q, k, v, g, beta, state_in, out,

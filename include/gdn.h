@@ -210,8 +210,10 @@ gdn_status gdn_graph_destroy(gdn_graph graph);
 gdn_status gdn_prefill_choose(const gdn_dims* dims, int32_t* chunk_or_zero);
 
 /*
- * Prefill with the method gdn_prefill_choose picks. The workspace must be at least
- * gdn_workspace_bytes(dims, chosen chunk); gdn_prefill_workspace_bytes gives that size.
+ * Prefill with the method gdn_prefill_choose picks, except that a single token (t == 1)
+ * runs as gdn_decode_step (the same arithmetic in one launch, no workspace). The workspace
+ * must be at least gdn_prefill_workspace_bytes(dims): gdn_workspace_bytes(dims, chosen
+ * chunk), or 0 when t == 1.
  */
 size_t gdn_prefill_workspace_bytes(const gdn_dims* dims);
 gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const void* v,
@@ -223,8 +225,8 @@ gdn_status gdn_prefill(const gdn_dims* dims, const void* q, const void* k, const
  * Segmented prefill ("Bound temporary memory with prompt chunking": a long prompt runs as
  * bounded segments whose recurrent state carries the context forward, without changing
  * the result). Each sequence's tokens are taken in consecutive segments of seg_t tokens
- * (the last may be shorter); each segment runs the method gdn_prefill_choose picks for
- * its length, on one sequence, with the state carried from segment to segment through
+ * (the last may be shorter); each segment runs the method gdn_prefill runs for its
+ * length, on one sequence, with the state carried from segment to segment through
  * state_out (updated in place after the first segment, which reads state_in). The
  * workspace is reused by every segment, so its size depends on seg_t, not on t:
  * gdn_prefill_segmented_workspace_bytes(dims, seg_t, overlapped). seg_t must be

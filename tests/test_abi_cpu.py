@@ -366,3 +366,14 @@ def test_calib_validation(lib):
     assert lib.gdn_calib_mfma_bf16_flops(10, 4) == 4 * 4 * 10 * 4 * 32 * 32 * 16 * 2
     assert lib.gdn_calib_mfma_bf16_flops(0, 4) == 0
     assert lib.gdn_calib_mfma_bf16_flops(10, -1) == 0
+
+
+def test_single_token_prefill_needs_no_workspace(lib):
+    """gdn_prefill runs one token as the decode step, which needs no workspace; the
+    segmented workspace for one-token segments is therefore 0 as well."""
+    one = gdn.make_dims(2, 1, 16, 32, 128)
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(one)) == 0
+    two = gdn.make_dims(2, 2, 16, 32, 128)
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(two)) > 0
+    seq = gdn.make_dims(1, 100, 16, 32, 128)
+    assert lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(seq), 1, 0) == 0

@@ -84,3 +84,15 @@ def test_segmented_prefill_4k(seg_t, overlapped):
                                   h["v"][:, :, hv:hv + 1].contiguous(), h["g"][:, :, hv:hv + 1].contiguous(),
                                   h["beta"][:, :, hv:hv + 1].contiguous())
         assert_parity(out[:, :, hv], st[:, hv], o_ref[:, :, 0], s_ref[:, 0], f"segmented {seg_t} head {hv}")
+
+
+def test_single_token_prefill_is_the_decode_step():
+    """gdn_prefill with t == 1 gives the decode step's bits (it runs that kernel)."""
+    c = gdn_inputs.make_case(Shape(n=3, t=1, h_qk=16, h_v=32, d=128), seed=730, device=DEV,
+                             s0_std=0.05)
+    o1, s1 = gdn.gdn_prefill(**c)
+    o2, s2 = gdn.gdn_decode_step(**c)
+    torch.cuda.synchronize()
+    assert torch.equal(o1, o2) and torch.equal(s1, s2)
+    o_ref, s_ref = run_oracle(c)
+    assert_parity(o1, s1, o_ref, s_ref, "prefill t=1")
