@@ -10,6 +10,8 @@ One step is the whole hot path once:
     continuing from the states the prefill produced, updated in place.
 `value` is prefill tokens per second for the 30 layers (4096 / prefill seconds per step);
 `decode_us_per_token` is the decode part. Inputs are resident in HBM before timing starts.
+prefill_us_per_layer is the mean prefill call (HIP events around every timed call), with its
+median, minimum and 90th percentile beside it.
 
 The JSON line also carries decode_cold_us_per_token (the decode step with its states out of
 the MALL), decode_per_layer_{eager,graph}_us_per_token (the same token as 30 dependent
@@ -39,6 +41,7 @@ steps (30 layers).
 import argparse
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -452,6 +455,9 @@ def main():
         "decode_us_per_token": sum(decode_ms) / len(decode_ms) * 1e3,
         "decode_GBps": decode_bytes() / (sum(decode_ms) / len(decode_ms) / 1e3) / 1e9,
         "prefill_us_per_layer": mean_call_s * 1e6,
+        "prefill_us_per_layer_median": float(statistics.median(call_ms)) * 1e3,
+        "prefill_us_per_layer_min": min(call_ms) * 1e3,
+        "prefill_us_per_layer_p90": sorted(call_ms)[int(0.9 * (len(call_ms) - 1))] * 1e3,
         **extra_fields(extra),
         "prefill_workspace_bytes": ws.numel(),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
