@@ -26,7 +26,8 @@ the 8 TB/s peak), all measured after the timed region, and
                 mean call duration from HIP events around every timed call, on the stream
                 the kernels run on; traffic = HBM bytes per call from the committed
                 rocprofv3 counter summary (null once the kernel source has changed);
-  cpu_baseline: the fp64 oracle timed on this host's cores on one layer of the same prefill.
+  cpu_baseline: the fp64 oracle timed on this host's cores over the prefill step's layers
+                (up to 30, or 20 s of oracle time), plus one layer on one thread.
 
 Modes for counter collection (no JSON line): --mode pmc-prefill runs the prefill calls of
 three layers; --mode pmc-copy runs a device copy of known size for counter calibration;

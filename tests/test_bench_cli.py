@@ -1,5 +1,5 @@
 """bench.py's command-line contract that needs no GPU: more than one GPU is refused with a
-message (this build measures one GPU), and the argument parser knows every mode."""
+message (the benchmark measures one GPU), and the argument parser knows every mode."""
 import os
 import subprocess
 import sys
