@@ -68,3 +68,13 @@ def test_calls_replay_from_a_graph():
         torch.cuda.synchronize()
         for name, (o, s) in outs.items():
             assert torch.equal(o, eager[name][0]) and torch.equal(s, eager[name][1]), (replay, name)
+
+
+def test_mfma_calibration_loop_runs():
+    """gdn_calib_mfma_bf16 (measurement only): the launch completes, the reported flops follow
+    its shape, and every lane writes a finite sum."""
+    sink = torch.full((16 * 256,), float("nan"), device=DEV)
+    flops = gdn.calib_mfma_bf16(5, 16, sink)
+    torch.cuda.synchronize()
+    assert flops == 16 * 4 * 5 * 4 * 32 * 32 * 16 * 2
+    assert torch.isfinite(sink).all()
