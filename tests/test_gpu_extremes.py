@@ -1,0 +1,64 @@
+"""GPU parity under extreme gates and write strengths, against the fp64 oracle: decays strong
+enough that exp(gamma) underflows fp32 inside a chunk (g down to -60 per token), no decay,
+a mix of both, and write strengths of exactly 0 and 1. The chunked form applies decays as
+pairwise exp(gamma_r - gamma_s) <= 1, so none of these may overflow or produce NaN."""
+import pytest
+import torch
+
+import gated_deltanet_linear_prefill_amd as gdn
+import gdn_inputs
+import oracle
+from gdn_inputs import Shape
+from parity import assert_parity
+
+pytestmark = pytest.mark.gpu
+DEV = "cuda"
+
+
+def case(kind, seed):
+    c = gdn_inputs.make_case(Shape(n=2, t=150, h_qk=2, h_v=4, d=128), seed=seed, device=DEV,
+                             s0_std=0.05)
+    gen = torch.Generator(device="cpu").manual_seed(seed)
+    shape = c["g"].shape
+    if kind == "strong_decay":
+        g = -torch.rand(shape, generator=gen, dtype=torch.float64) * 60.0
+    elif kind == "no_decay":
+        g = torch.zeros(shape, dtype=torch.float64)
+    else:  # mixed: mostly mild, with occasional resets
+        g = -torch.rand(shape, generator=gen, dtype=torch.float64) * 0.1
+        g[torch.rand(shape, generator=gen) < 0.05] = -50.0
+    beta = torch.rand(shape, generator=gen, dtype=torch.float64)
+    beta[torch.rand(shape, generator=gen) < 0.2] = 0.0
+    beta[torch.rand(shape, generator=gen) < 0.2] = 1.0
+    c["g"] = g.to(torch.float32).to(DEV)
+    c["beta"] = beta.to(torch.float32).to(DEV)
+    return c
+
+
+def ref(c):
+    h = {key: (None if val is None else val.cpu()) for key, val in c.items()}
+    return oracle.run(h["q"], h["k"], h["v"], h["g"], h["beta"], h["state_in"])
+
+
+@pytest.mark.parametrize("kind", ["strong_decay", "no_decay", "mixed"])
+@pytest.mark.parametrize("method", ["C16", "C32", "C64", "C128", "scan"])
+def test_extreme_gates(kind, method):
+    c = case(kind, seed=1300 + len(kind) + len(method))
+    if method == "scan":
+        out, st = gdn.gdn_prefill_scan(**c)
+    else:
+        out, st = gdn.gdn_prefill_chunked(**c, chunk=int(method[1:]))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(st).all()
+    o_ref, s_ref = ref(c)
+    assert_parity(out, st, o_ref, s_ref, f"{method} {kind}")
+
+
+@pytest.mark.parametrize("kind", ["strong_decay", "no_decay", "mixed"])
+def test_extreme_gates_decode(kind):
+    c = case(kind, seed=1400 + len(kind))
+    d1 = {key: (val[:, :1].contiguous() if key != "state_in" else val) for key, val in c.items()}
+    out, st = gdn.gdn_decode_step(**d1)
+    torch.cuda.synchronize()
+    o_ref, s_ref = ref(d1)
+    assert_parity(out, st, o_ref, s_ref, f"decode {kind}")
