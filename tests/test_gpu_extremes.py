@@ -62,3 +62,35 @@ def test_extreme_gates_decode(kind):
     torch.cuda.synchronize()
     o_ref, s_ref = ref(d1)
     assert_parity(out, st, o_ref, s_ref, f"decode {kind}")
+
+
+@pytest.mark.parametrize("method", ["C16", "C32", "C64", "C128", "scan", "decode"])
+def test_extreme_input_scales(method):
+    """q rows scaled by 1000, k rows exactly zero (they normalise to zero with l2_eps > 0,
+    so their token writes nothing) and k rows of norm 1e-3 (where l2_eps matters): the
+    normalisation inside every method matches the oracle's."""
+    c = gdn_inputs.make_case(Shape(n=1, t=130, h_qk=2, h_v=4, d=128), seed=1500, device=DEV,
+                             s0_std=0.05)
+    gen = torch.Generator(device="cpu").manual_seed(1501)
+    t = c["q"].shape[1]
+    big = torch.rand(t, generator=gen) < 0.2
+    zero = torch.rand(t, generator=gen) < 0.1
+    tiny = (torch.rand(t, generator=gen) < 0.1) & ~zero
+    q = c["q"].float().cpu()
+    k = c["k"].float().cpu()
+    q[:, big] *= 1000.0
+    k[:, zero] = 0.0
+    k[:, tiny] *= 1e-3
+    c["q"] = q.to(c["v"].dtype).to(DEV)
+    c["k"] = k.to(c["v"].dtype).to(DEV)
+    if method == "decode":
+        c = {key: (val[:, :1].contiguous() if key != "state_in" else val) for key, val in c.items()}
+        out, st = gdn.gdn_decode_step(**c)
+    elif method == "scan":
+        out, st = gdn.gdn_prefill_scan(**c)
+    else:
+        out, st = gdn.gdn_prefill_chunked(**c, chunk=int(method[1:]))
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(st).all()
+    o_ref, s_ref = ref(c)
+    assert_parity(out, st, o_ref, s_ref, f"{method} input scales")
