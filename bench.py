@@ -10,8 +10,9 @@ One step is the whole hot path once:
     continuing from the states the prefill produced, updated in place.
 `value` is prefill tokens per second for the 30 layers (4096 / prefill seconds per step);
 `decode_us_per_token` is the decode part. Inputs are resident in HBM before timing starts.
-prefill_us_per_layer is the mean prefill call (HIP events around every timed call), with its
-median, minimum and 90th percentile beside it.
+prefill_us_per_layer is the timed steps' prefill time over 30 (the mean duration of one of
+the back-to-back calls); prefill_us_per_call_{median,min,p90} come from a separate pass with an
+event around every call.
 
 The JSON line also carries decode_cold_us_per_token (the decode step with its states out of
 the MALL), decode_per_layer_{eager,graph}_us_per_token (the same token as 30 dependent
@@ -23,9 +24,10 @@ hbm_copy_GBps (what a 1 GiB device copy reaches; the achievable HBM rate next to
 the 8 TB/s peak), all measured after the timed region, and
   roofline:     the prefill call (its two kernels) against HBM: algorithmic bytes per call
                 (q, k, v, g, beta read once, out and state_out written once) divided by the
-                mean call duration from HIP events around every timed call, on the stream
-                the kernels run on; traffic = HBM bytes per call from the committed
-                rocprofv3 counter summary (null once the kernel source has changed);
+                mean call duration (HIP events around the 30 back-to-back calls of every
+                timed step, on the stream the kernels run on, divided by 30); traffic =
+                HBM bytes per call from the committed rocprofv3 counter summary (null once
+                the kernel source has changed);
   cpu_baseline: the fp64 oracle timed on this host's cores over the prefill step's layers
                 (up to 30, or 20 s of oracle time), plus one layer on one thread.
 
@@ -401,22 +403,23 @@ def main():
             print(f"segmented prefill calls done (overlapped={ov})", flush=True)
         return
 
+    # A timed step records events only at its boundaries (an event between two calls
+    # costs about 2 us on this stack); the per-call durations come from a separate pass
+    # after the timed region.
     def step(evs=None):
-        if evs is None:
-            for c in calls:
-                c()
-            decode()
-            return
-        for l, c in enumerate(calls):
-            evs[l].record()
+        if evs is not None:
+            evs[0].record()
+        for c in calls:
             c()
-        evs[LAYERS].record()
+        if evs is not None:
+            evs[1].record()
         decode()
-        evs[LAYERS + 1].record()
+        if evs is not None:
+            evs[2].record()
 
     for _ in range(args.warmup):
         step()
-    all_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(LAYERS + 2)]
+    all_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)]
                for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
@@ -425,12 +428,23 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
 
-    call_ms = [evs[l].elapsed_time(evs[l + 1]) for evs in all_evs for l in range(LAYERS)]
-    prefill_ms = [evs[0].elapsed_time(evs[LAYERS]) for evs in all_evs]
-    decode_ms = [evs[LAYERS].elapsed_time(evs[LAYERS + 1]) for evs in all_evs]
+    prefill_ms = [evs[0].elapsed_time(evs[1]) for evs in all_evs]
+    decode_ms = [evs[1].elapsed_time(evs[2]) for evs in all_evs]
     prefill_s = sum(prefill_ms) / len(prefill_ms) / 1e3
-    mean_call_s = sum(call_ms) / len(call_ms) / 1e3
+    mean_call_s = prefill_s / LAYERS  # average duration of one of the back-to-back calls
     achieved = prefill_bytes() / mean_call_s / 1e9
+
+    # per-call distribution (not part of the timed steps): an event around every call
+    cev = [torch.cuda.Event(enable_timing=True) for _ in range(LAYERS + 1)]
+    call_ms = []
+    for _ in range(3):
+        torch.cuda.synchronize()
+        for l, c in enumerate(calls):
+            cev[l].record()
+            c()
+        cev[LAYERS].record()
+        torch.cuda.synchronize()
+        call_ms += [cev[l].elapsed_time(cev[l + 1]) for l in range(LAYERS)]
 
     traffic = measured_traffic()
     extra = None if args.core_only else reference_rates(gdn, dec, dec_out, layers[0], dev)
@@ -456,9 +470,9 @@ def main():
         "decode_us_per_token": sum(decode_ms) / len(decode_ms) * 1e3,
         "decode_GBps": decode_bytes() / (sum(decode_ms) / len(decode_ms) / 1e3) / 1e9,
         "prefill_us_per_layer": mean_call_s * 1e6,
-        "prefill_us_per_layer_median": float(statistics.median(call_ms)) * 1e3,
-        "prefill_us_per_layer_min": min(call_ms) * 1e3,
-        "prefill_us_per_layer_p90": sorted(call_ms)[int(0.9 * (len(call_ms) - 1))] * 1e3,
+        "prefill_us_per_call_median": float(statistics.median(call_ms)) * 1e3,
+        "prefill_us_per_call_min": min(call_ms) * 1e3,
+        "prefill_us_per_call_p90": sorted(call_ms)[int(0.9 * (len(call_ms) - 1))] * 1e3,
         **extra_fields(extra),
         "prefill_workspace_bytes": ws.numel(),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
