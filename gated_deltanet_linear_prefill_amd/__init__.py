@@ -118,37 +118,73 @@ def _stream(device, stream):
     return ctypes.c_void_p(s.cuda_stream)
 
 
+def _check_tensor(name, x, shape, dtype, dev):
+    """x must be a contiguous CUDA (HIP) tensor on dev with exactly this shape and dtype."""
+    if not isinstance(x, torch.Tensor):
+        raise ValueError(f"{name} must be a torch.Tensor")
+    if not x.is_cuda or x.device != dev:
+        raise ValueError(f"{name} must be a CUDA (HIP) tensor on {dev}")
+    if x.dtype != dtype:
+        raise ValueError(f"{name} must be {dtype}, got {x.dtype}")
+    if tuple(x.shape) != tuple(shape):
+        raise ValueError(f"{name} must have shape {tuple(shape)}, got {tuple(x.shape)}")
+    if not x.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
 def _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps):
-    tensors = [("q", q), ("k", k), ("v", v), ("g", g), ("beta", beta)]
-    if state_in is not None:
-        tensors.append(("state_in", state_in))
-    dev = q.device
-    for name, x in tensors:
-        if not x.is_cuda or x.device != dev:
-            raise ValueError(f"{name} must be a CUDA (HIP) tensor on {dev}")
-        if not x.is_contiguous():
-            raise ValueError(f"{name} must be contiguous")
-    if k.dtype != q.dtype or v.dtype != q.dtype or q.dtype not in _DTYPES:
+    """Check every tensor of a call against the sizes q and v define (all before any
+    launch: a wrong shape, dtype, device or layout would otherwise reach the kernels as a
+    raw pointer) and allocate out / state_out when they are not given."""
+    if not isinstance(q, torch.Tensor) or not isinstance(v, torch.Tensor):
+        raise ValueError("q and v must be torch tensors")
+    if q.dim() != 4 or v.dim() != 4:
+        raise ValueError("q must be [n, t, h_qk, d] and v [n, t, h_v, d]")
+    if q.dtype not in _DTYPES:
         raise ValueError("q, k, v must share one dtype, bfloat16 or float32")
-    for name, x in (("g", g), ("beta", beta), ("state_in", state_in)):
-        if x is not None and x.dtype != torch.float32:
-            raise ValueError(f"{name} must be float32")
-    dims = _dims_of(q, v, l2_eps)
-    n, t, _, d = q.shape
+    dev = q.device
+    n, t, h_qk, d = q.shape
     h_v = v.shape[2]
+    f32 = torch.float32
+    _check_tensor("q", q, (n, t, h_qk, d), q.dtype, dev)
+    _check_tensor("k", k, (n, t, h_qk, d), q.dtype, dev)
+    _check_tensor("v", v, (n, t, h_v, v.shape[3]), q.dtype, dev)
+    if v.shape[3] != d:
+        raise ValueError(f"v must have shape {(n, t, h_v, d)}, got {tuple(v.shape)}")
+    _check_tensor("g", g, (n, t, h_v), f32, dev)
+    _check_tensor("beta", beta, (n, t, h_v), f32, dev)
+    if state_in is not None:
+        _check_tensor("state_in", state_in, (n, h_v, d, d), f32, dev)
+    dims = _dims_of(q, v, l2_eps)
     if out is None:
-        out = torch.empty((n, t, h_v, d), device=dev, dtype=torch.float32)
+        out = torch.empty((n, t, h_v, d), device=dev, dtype=f32)
+    else:
+        _check_tensor("out", out, (n, t, h_v, d), f32, dev)
     if state_out is None:
-        state_out = torch.empty((n, h_v, d, d), device=dev, dtype=torch.float32)
+        state_out = torch.empty((n, h_v, d, d), device=dev, dtype=f32)
+    else:
+        _check_tensor("state_out", state_out, (n, h_v, d, d), f32, dev)
     return dims, out, state_out
+
+
+def _check_workspace(workspace, dev):
+    """A caller-supplied workspace: a contiguous uint8 tensor on the call's device."""
+    if workspace is None:
+        return 0
+    if not isinstance(workspace, torch.Tensor) or workspace.dtype != torch.uint8:
+        raise ValueError("workspace must be a uint8 torch tensor")
+    if not workspace.is_cuda or workspace.device != dev:
+        raise ValueError(f"workspace must be a CUDA (HIP) tensor on {dev}")
+    if not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    return workspace.numel()
 
 
 def _workspace(dims, chunk, workspace, dev):
     need = _load().gdn_workspace_bytes(ctypes.byref(dims), int(chunk))
     if workspace is None and need > 0:
         workspace = torch.empty(need, device=dev, dtype=torch.uint8)
-    nbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
-    return workspace, nbytes
+    return workspace, _check_workspace(workspace, dev)
 
 
 def gdn_workspace_bytes(n, t, h_qk, h_v, d, dtype=torch.bfloat16, chunk=64) -> int:
@@ -235,7 +271,7 @@ def gdn_prefill(q, k, v, g, beta, state_in=None, *, l2_eps=1e-6, out=None, state
         need = _load().gdn_prefill_workspace_bytes(ctypes.byref(dims))
         if need > 0:
             workspace = torch.empty(need, device=q.device, dtype=torch.uint8)
-    wbytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    wbytes = _check_workspace(workspace, q.device)
     _check(_load().gdn_prefill(
         ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
         _ptr(out), _ptr(state_out), _ptr(workspace), wbytes, _stream(q.device, stream)),
@@ -260,7 +296,7 @@ class BoundCall:
 def bind_prefill_chunked(q, k, v, g, beta, state_in, out, state_out, workspace, *, chunk=64,
                          l2_eps=1e-6, stream=None) -> BoundCall:
     dims, out, state_out = _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps)
-    nbytes = workspace.numel() * workspace.element_size()
+    nbytes = _check_workspace(workspace, q.device)
     args = (ctypes.byref(dims), int(chunk), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
             _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace), nbytes,
             _stream(q.device, stream))
@@ -271,7 +307,7 @@ def bind_prefill_chunked(q, k, v, g, beta, state_in, out, state_out, workspace, 
 def bind_prefill_scan(q, k, v, g, beta, state_in, out, state_out, workspace, *, l2_eps=1e-6,
                       stream=None) -> BoundCall:
     dims, out, state_out = _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps)
-    nbytes = workspace.numel() * workspace.element_size()
+    nbytes = _check_workspace(workspace, q.device)
     args = (ctypes.byref(dims), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta), _ptr(state_in),
             _ptr(out), _ptr(state_out), _ptr(workspace), nbytes, _stream(q.device, stream))
     return BoundCall(_load().gdn_prefill_scan, args, "gdn_prefill_scan",
@@ -304,9 +340,10 @@ def gdn_prefill_segmented(q, k, v, g, beta, state_in=None, *, seg_t, overlapped=
     if workspace is None:
         need = _load().gdn_prefill_segmented_workspace_bytes(ctypes.byref(dims), int(seg_t), ov)
         workspace = torch.empty(max(need, 1), device=q.device, dtype=torch.uint8)
+    wbytes = _check_workspace(workspace, q.device)
     _check(_load().gdn_prefill_segmented(
         ctypes.byref(dims), int(seg_t), ov, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
-        _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace), workspace.numel(),
+        _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace), wbytes,
         _stream(q.device, stream)), "gdn_prefill_segmented")
     return out, state_out
 
@@ -329,6 +366,10 @@ class DecodeGraph:
                    for i in range(layers)]
         for i in range(layers):
             _prepare(q[i], k[i], v[i], g[i], beta[i], state[i], out[i], state[i], l2_eps)
+            # one gdn_dims describes every layer: each layer must match layer 0 exactly
+            if (q[i].shape != q[0].shape or v[i].shape != v[0].shape
+                    or q[i].dtype != q[0].dtype or q[i].device != q[0].device):
+                raise ValueError(f"layer {i}: q/v shapes, dtype and device must equal layer 0's")
         self.tensors = (list(q), list(k), list(v), list(g), list(beta), list(state), list(out))
         self.out = self.tensors[6]
         dims = _dims_of(q[0], v[0], l2_eps) if layers else make_dims(0, 1, 1, 1, 16)

@@ -167,6 +167,10 @@ gdn_status gdn_prefill_scan_blockwise(const gdn_dims* dims, int64_t block_t, con
  * Batch-1 decode step (dims->t must be 1): one token per sequence; each (sequence, V
  * head) state streams from HBM through registers back to HBM once, with the q/k
  * normalisation fused in. No workspace.
+ * Source: "Decode: minimise bytes moved per token" -- at batch 1 a decode step is bound by
+ * the bytes it moves per token, and the fused-chain list there pairs the recurrent update
+ * with its normalisation; the per-token update itself is the one of "Qwen creates three
+ * distinct workload shapes" (every token depends on the state after the previous one).
  */
 gdn_status gdn_decode_step(const gdn_dims* dims, const void* q, const void* k,
                            const void* v, const float* g, const float* beta,
@@ -206,6 +210,14 @@ gdn_status gdn_graph_destroy(gdn_graph graph);
  * Prefill method for these dims, from the measured scan-versus-chunk crossover on
  * MI355X: *chunk_or_zero receives 0 for the direct scan or the chunk size to pass to
  * gdn_prefill_chunked.
+ * Source: "Qwen creates three distinct workload shapes" -- the direct scan and the chunked
+ * form compute the same result, and which one is faster depends on the model dimensions,
+ * the workload and the hardware, so the choice is measured rather than fixed ("Optimization
+ * strategy": decide from measurements on the target machine).
+ * Scope of the table: it was measured for one sequence (n = 1), 16 QK / 32 V heads,
+ * d = 128 and bf16 q/k/v, and is keyed on the token count only; other head counts, head
+ * dimensions, fp32 inputs and batched calls get the same pick by length, which is correct
+ * (every method computes the same result) but not tuned for them.
  */
 gdn_status gdn_prefill_choose(const gdn_dims* dims, int32_t* chunk_or_zero);
 
