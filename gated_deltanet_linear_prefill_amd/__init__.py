@@ -20,7 +20,7 @@ __all__ = [
     "gdn_prefill", "gdn_prefill_workspace_bytes", "library_path", "Dims", "BoundCall",
     "bind_prefill_chunked", "bind_prefill_scan", "bind_decode_step", "DecodeGraph",
     "gdn_prefill_segmented", "gdn_prefill_segmented_workspace_bytes", "gdn_prefill_scan_blockwise",
-    "calib_mfma_bf16",
+    "calib_mfma_bf16", "gdn_prefill_segmented_noalloc", "gdn_noalloc_scratch_bytes",
 ]
 
 GDN_F32, GDN_BF16 = 0, 1
@@ -75,6 +75,8 @@ def _load():
         "gdn_prefill_segmented_workspace_bytes": (sz, [D, ctypes.c_int64, ctypes.c_int32]),
         "gdn_prefill_segmented": (ctypes.c_int, [D, ctypes.c_int64, ctypes.c_int32] + [P] * 9
                                   + [sz, P]),
+        "gdn_noalloc_scratch_bytes": (sz, []),
+        "gdn_prefill_segmented_noalloc": (ctypes.c_int, [D, ctypes.c_int64] + [P] * 9),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -345,6 +347,24 @@ def gdn_prefill_segmented(q, k, v, g, beta, state_in=None, *, seg_t, overlapped=
         ctypes.byref(dims), int(seg_t), ov, _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
         _ptr(state_in), _ptr(out), _ptr(state_out), _ptr(workspace), wbytes,
         _stream(q.device, stream)), "gdn_prefill_segmented")
+    return out, state_out
+
+
+def gdn_noalloc_scratch_bytes() -> int:
+    """Size of the library's static per-GPU workspace used by gdn_prefill_segmented_noalloc."""
+    return int(_load().gdn_noalloc_scratch_bytes())
+
+
+def gdn_prefill_segmented_noalloc(q, k, v, g, beta, state_in=None, *, seg_t, l2_eps=1e-6,
+                                  out, state_out, stream=None):
+    """gdn_prefill_segmented (in order) with the library's static workspace instead of a
+    caller's: the library allocates nothing. The caller passes the outputs. Returns
+    (out, state_out)."""
+    dims, out, state_out = _prepare(q, k, v, g, beta, state_in, out, state_out, l2_eps)
+    _check(_load().gdn_prefill_segmented_noalloc(
+        ctypes.byref(dims), int(seg_t), _ptr(q), _ptr(k), _ptr(v), _ptr(g), _ptr(beta),
+        _ptr(state_in), _ptr(out), _ptr(state_out), _stream(q.device, stream)),
+        "gdn_prefill_segmented_noalloc")
     return out, state_out
 
 

@@ -296,6 +296,36 @@ gdn_status side_stream(SideStream** out)
     return GDN_OK;
 }
 
+// ---------------------------------------------------------------- allocation-free entry
+
+// The workspace of gdn_prefill_segmented_noalloc: a file-scope device array, one copy per
+// GPU, held until the process ends. Host code never passes the array's name to a kernel
+// (on the host it is only a stand-in symbol); it looks up each device's address once with
+// hipGetSymbolAddress and passes that.
+__device__ __align__(256) unsigned char scratch[GDN_NOALLOC_SCRATCH_BYTES];
+
+void* g_scratch_addr[kMaxDevices];
+std::mutex g_scratch_mu;
+
+// The current device's address of `scratch`, looked up on the first call on that device.
+gdn_status scratch_address(void** out)
+{
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess) return GDN_ERR_HIP;
+    if (dev < 0 || dev >= kMaxDevices) return GDN_ERR_UNSUPPORTED;
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_addr[dev]) {
+        void* p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return GDN_ERR_HIP;
+        }
+        g_scratch_addr[dev] = p;
+    }
+    *out = g_scratch_addr[dev];
+    return GDN_OK;
+}
+
 }  // namespace
 
 hipError_t launch_state_passthrough(const Call& c)
@@ -310,6 +340,53 @@ hipError_t launch_state_passthrough(const Call& c)
     return hipGetLastError();
 }
 
+}  // namespace gdn
+
+namespace gdn {
+namespace {
+
+// The checks gdn_prefill_segmented makes on the whole call, except those on the workspace:
+// shapes, pointers, alignment, aliasing, and the method-specific limits of both segment
+// lengths (seg_t and the remainder), all before anything is enqueued. *empty is set when
+// there is nothing to do beyond the t == 0 state copy.
+gdn_status check_segmented(const gdn_dims* d, int64_t seg_t, int32_t overlapped, const void* q,
+                           const void* k, const void* v, const float* g, const float* beta,
+                           const float* state_in, float* out, float* state_out)
+{
+    if (!d) return GDN_ERR_NULL;
+    if (seg_t <= 0 || (overlapped != 0 && overlapped != 1)) return GDN_ERR_SHAPE;
+    Call c;
+    gdn_status st = validate(d, -2, q, k, v, g, beta, state_in, out, state_out, nullptr, 0, &c);
+    if (st != GDN_OK || d->n == 0 || d->t == 0) return st;
+    for (int64_t len : {d->t < seg_t ? d->t : seg_t, d->t % seg_t}) {
+        if (len == 0) continue;
+        gdn_dims one = *d;
+        one.n = 1;
+        one.t = len;
+        st = validate(&one, prefill_method(&one), q, k, v, g, beta, state_in, out, state_out,
+                      nullptr, 0, &c);
+        if (st != GDN_OK && st != GDN_ERR_WORKSPACE) return st;
+    }
+    return GDN_OK;
+}
+
+// The in-order schedule: each segment as one gdn_prefill call on `stream`, all sharing ws.
+gdn_status run_segments_in_order(const gdn_dims* d, int64_t seg_t, const void* q, const void* k,
+                                 const void* v, const float* g, const float* beta,
+                                 const float* state_in, float* out, float* state_out, void* ws,
+                                 size_t ws_bytes, void* stream)
+{
+    const SegmentPlan plan(d, seg_t, q, k, v, g, beta, state_in, out, state_out);
+    for (int64_t p = 0; p < plan.pieces; ++p) {
+        const Piece x = plan.piece(p);
+        const gdn_status st = gdn_prefill(&x.dims, x.q, x.k, x.v, x.g, x.beta, x.state_in,
+                                          x.out, x.state_out, ws, ws_bytes, stream);
+        if (st != GDN_OK) return st;
+    }
+    return GDN_OK;
+}
+
+}  // namespace
 }  // namespace gdn
 
 using namespace gdn;
@@ -416,14 +493,12 @@ gdn_status gdn_prefill_segmented(const gdn_dims* d, int64_t seg_t, int32_t overl
                                  const float* beta, const float* state_in, float* out,
                                  float* state_out, void* ws, size_t ws_bytes, void* stream)
 {
-    if (!d) return GDN_ERR_NULL;
-    if (seg_t <= 0 || (overlapped != 0 && overlapped != 1)) return GDN_ERR_SHAPE;
-    // The whole call is validated as one (shapes, pointers, alignment, aliasing), with the
-    // segment workspace; every segment call below is a sub-range of it.
-    Call c;
-    gdn_status st = validate(d, -2, q, k, v, g, beta, state_in, out, state_out, nullptr, 0, &c);
+    // The whole call is validated as one (shapes, pointers, alignment, aliasing, both
+    // segment lengths' limits); every segment call below is a sub-range of it.
+    gdn_status st = check_segmented(d, seg_t, overlapped, q, k, v, g, beta, state_in, out,
+                                    state_out);
     if (st != GDN_OK) return st;
-    if (c.n == 0) return GDN_OK;
+    if (d->n == 0) return GDN_OK;
     if (d->t == 0) return gdn_prefill(d, q, k, v, g, beta, state_in, out, state_out, ws, ws_bytes, stream);
     const size_t need = gdn_prefill_segmented_workspace_bytes(d, seg_t, overlapped);
     if (need > 0 && (!ws || ws_bytes < need)) return GDN_ERR_WORKSPACE;
@@ -441,27 +516,12 @@ gdn_status gdn_prefill_segmented(const gdn_dims* d, int64_t seg_t, int32_t overl
             if (overlap(r_w, r)) return GDN_ERR_ALIAS;
         if (!aligned(ws, 16)) return GDN_ERR_ALIGN;
     }
-    // Only two segment lengths occur (seg_t and the remainder): check the method-specific
-    // limits of both before anything is enqueued.
-    for (int64_t len : {d->t < seg_t ? d->t : seg_t, d->t % seg_t}) {
-        if (len == 0) continue;
-        gdn_dims one = *d;
-        one.n = 1;
-        one.t = len;
-        st = validate(&one, prefill_method(&one), q, k, v, g, beta, state_in, out, state_out,
-                      nullptr, 0, &c);
-        if (st != GDN_OK && st != GDN_ERR_WORKSPACE) return st;
-    }
+    if (!overlapped)
+        return run_segments_in_order(d, seg_t, q, k, v, g, beta, state_in, out, state_out, ws,
+                                     ws_bytes, stream);
+
+    Call c;
     const SegmentPlan plan(d, seg_t, q, k, v, g, beta, state_in, out, state_out);
-    if (!overlapped) {
-        for (int64_t p = 0; p < plan.pieces; ++p) {
-            const Piece x = plan.piece(p);
-            st = gdn_prefill(&x.dims, x.q, x.k, x.v, x.g, x.beta, x.state_in, x.out,
-                             x.state_out, ws, ws_bytes, stream);
-            if (st != GDN_OK) return st;
-        }
-        return GDN_OK;
-    }
 
     // Overlapped: the per-chunk preparation of segment p + 1 runs on the side stream while
     // the sequential pass of segment p runs on the caller's stream, with the workspace split
@@ -510,6 +570,30 @@ gdn_status gdn_prefill_segmented(const gdn_dims* d, int64_t seg_t, int32_t overl
     if (j == hipSuccess) j = hipStreamWaitEvent(main_s, side->join, 0);
     if (st != GDN_OK) return st;
     return finish(e != hipSuccess ? e : j);
+}
+
+size_t gdn_noalloc_scratch_bytes(void)
+{
+    return GDN_NOALLOC_SCRATCH_BYTES;
+}
+
+gdn_status gdn_prefill_segmented_noalloc(const gdn_dims* d, int64_t seg_t, const void* q,
+                                         const void* k, const void* v, const float* g,
+                                         const float* beta, const float* state_in, float* out,
+                                         float* state_out, void* stream)
+{
+    gdn_status st = check_segmented(d, seg_t, 0, q, k, v, g, beta, state_in, out, state_out);
+    if (st != GDN_OK) return st;
+    if (d->n == 0) return GDN_OK;
+    const size_t need = d->t == 0 ? 0 : gdn_prefill_segmented_workspace_bytes(d, seg_t, 0);
+    if (need > GDN_NOALLOC_SCRATCH_BYTES) return GDN_ERR_WORKSPACE;
+    void* ws = nullptr;
+    if (need > 0) {
+        st = scratch_address(&ws);
+        if (st != GDN_OK) return st;
+    }
+    return run_segments_in_order(d, seg_t, q, k, v, g, beta, state_in, out, state_out, ws,
+                                 need > 0 ? (size_t)GDN_NOALLOC_SCRATCH_BYTES : 0, stream);
 }
 
 gdn_status gdn_decode_graph_create(const gdn_dims* d, int32_t layers, const void* const* q,

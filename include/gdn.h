@@ -270,6 +270,35 @@ gdn_status gdn_prefill_segmented(const gdn_dims* dims, int64_t seg_t, int32_t ov
                                  void* stream);
 
 /*
+ * Allocation-free segmented prefill, for callers that cannot allocate device memory: code
+ * recorded under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc.
+ * Computes exactly what gdn_prefill_segmented(dims, seg_t, 0, ...) computes (the in-order
+ * schedule, the same kernels, the same bits), but takes no workspace argument: the
+ * segments' workspace is a static device array inside the library of
+ * GDN_NOALLOC_SCRATCH_BYTES bytes per GPU, reserved when the library's code is loaded on
+ * that GPU and held until the process ends. The call allocates and frees nothing; its first
+ * call on a device looks up that device's address of the array (hipGetSymbolAddress).
+ *
+ * Limit: gdn_prefill_segmented_workspace_bytes(dims, seg_t, 0) must not exceed
+ * GDN_NOALLOC_SCRATCH_BYTES, else GDN_ERR_WORKSPACE and nothing is enqueued (at 32 V heads
+ * of d = 128 segments of up to 1024 tokens fit). The array keeps whatever the last call on
+ * the GPU left in it; every kernel that reads a workspace region writes it first within
+ * the same call, so no call depends on its contents. All calls on one GPU share the one
+ * array: two calls that overlap in time on the same GPU (different streams or host
+ * threads with no ordering between them) race on it and give undefined results; calls on
+ * one stream, or ordered by events, are safe. Other arguments and errors as for
+ * gdn_prefill_segmented with overlapped = 0; GDN_ERR_HIP if the array's address cannot be
+ * looked up.
+ */
+#define GDN_NOALLOC_SCRATCH_BYTES (16u << 20)
+
+size_t gdn_noalloc_scratch_bytes(void);
+gdn_status gdn_prefill_segmented_noalloc(const gdn_dims* dims, int64_t seg_t, const void* q,
+                                         const void* k, const void* v, const float* g,
+                                         const float* beta, const float* state_in, float* out,
+                                         float* state_out, void* stream);
+
+/*
  * Calibration (measurement only): `blocks` workgroups of four waves each issue `iters`
  * rounds of four independent 32x32x16 bf16 MFMAs on `stream`, then write one float per
  * lane to `sink` (device memory of blocks x 256 floats, contents meaningless). The

@@ -377,3 +377,36 @@ def test_single_token_prefill_needs_no_workspace(lib):
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(two)) > 0
     seq = gdn.make_dims(1, 100, 16, 32, 128)
     assert lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(seq), 1, 0) == 0
+
+
+# ------------------------------------------------------------- allocation-free entry (no GPU)
+def call_noalloc(lib, b, seg_t=16, dims=None, **over):
+    a = {key: b.p(key) for key in ("q", "k", "v", "g", "beta", "state_in", "out", "state_out")}
+    a.update(over)
+    d = ctypes.byref(dims if dims is not None else b.dims)
+    return lib.gdn_prefill_segmented_noalloc(d, seg_t, a["q"], a["k"], a["v"], a["g"],
+                                             a["beta"], a["state_in"], a["out"],
+                                             a["state_out"], None)
+
+
+def test_noalloc_validation(lib):
+    """Every error of the allocation-free entry is returned before its scratch lookup or any
+    launch (no HIP call here): the segmented checks, and a segment whose workspace exceeds
+    the static array."""
+    assert lib.gdn_noalloc_scratch_bytes() == 16 << 20
+    b = Bufs(t=64)
+    assert lib.gdn_prefill_segmented_noalloc(None, 16, *[None] * 8, None) == NULL
+    assert call_noalloc(lib, b, seg_t=0) == SHAPE
+    assert call_noalloc(lib, b, seg_t=-1) == SHAPE
+    assert call_noalloc(lib, b, q=None) == NULL
+    assert call_noalloc(lib, b, out=b.p("out", 4)) == ALIGN
+    assert call_noalloc(lib, b, out=b.p("q")) == ALIAS
+    assert call_noalloc(lib, b, state_out=b.p("out")) == ALIAS
+    assert call_noalloc(lib, b, dims=with_dims(b, d_k=40, d_v=40)) == UNSUP
+    # the 4K workload: 1024-token segments fit the 16 MiB array, 2048-token ones do not
+    big = Bufs(t=4096, h_qk=16, h_v=32, d=128)
+    fit = lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(big.dims), 1024, 0)
+    over = lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(big.dims), 2048, 0)
+    assert 0 < fit <= lib.gdn_noalloc_scratch_bytes() < over
+    assert call_noalloc(lib, big, seg_t=2048) == WS
+    assert call_noalloc(lib, big, seg_t=4096) == WS
