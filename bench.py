@@ -12,10 +12,18 @@ One step is the whole hot path once:
 `decode_us_per_token` is the decode part. Inputs are resident in HBM before timing starts.
 prefill_us_per_layer is the timed steps' prefill time over 30 (the mean duration of one of
 the back-to-back calls); prefill_us_per_call_{median,min,p90} come from a separate pass with an
-event around every call.
+event around every call. prefill_c64_us_per_layer is the same 30 calls with 64-token chunks
+(the chunk the 4096-token workload is specified with), timed the same way after the timed
+region, with its fraction of the HBM roofline (prefill_c64_hbm_frac).
 
-The JSON line also carries decode_cold_us_per_token (the decode step with its states out of
-the MALL), decode_per_layer_{eager,graph}_us_per_token (the same token as 30 dependent
+decode_us_per_token is the step's own decode token: its 60 MiB of state were last written by
+the prefill calls, whose outputs have since pushed them out of the 256 MB MALL, so it reads
+them from HBM. The JSON line also carries decode_steady_us_per_token (consecutive decode
+steps on one state stack, as in the 4096-step decode workload: the state stays in the MALL
+between steps), decode_cold_us_per_token (consecutive steps over six stacks used in turn,
+360 MiB), stream_copy_{warm,cold}_GBps (the library's streaming-copy calibration kernel over
+the same 60 MiB, one buffer pair or six in turn: the achievable read + write rate the decode
+fractions are taken against), decode_per_layer_{eager,graph}_us_per_token (the same token as 30 dependent
 per-layer steps of one sequence each, called one by one or replayed as one recorded HIP
 graph), prefill_segmented_1024[_overlapped]_us_per_layer (one layer's prompt as four
 1024-token segments with the smaller workspace they need, in order or with each segment's
@@ -39,7 +47,8 @@ tokens (resident direct scan, the same scan with the state through device memory
 tokens, and the chunked call) and prints one JSON line of its own; --mode pmc-ablation makes
 one call of each scan form for counter collection; --mode pmc-mfma runs one MFMA loop of
 known flops (calibration of the MFMA counters); --mode pmc-decode runs three stacked decode
-steps (30 layers).
+steps (30 layers); --mode decode-layers runs five decode tokens as 30 dependent per-layer
+steps launched one by one, then five as replays of the recorded decode graph.
 """
 import argparse
 import json
@@ -68,7 +77,8 @@ def parse():
                     help="skip the measurements after the timed region (their fields are null), "
                          "so that a kernel trace holds only the timed step's kernels")
     ap.add_argument("--mode", choices=["bench", "pmc-prefill", "pmc-copy", "segmented",
-                                       "ablation", "pmc-ablation", "pmc-mfma", "pmc-decode"],
+                                       "ablation", "pmc-ablation", "pmc-mfma", "pmc-decode",
+                                       "decode-layers"],
                     default="bench")
     return ap.parse_args()
 
@@ -129,17 +139,34 @@ def reference_rates(gdn, dec, dec_out, pre, dev):
     stacks = [torch.zeros(LAYERS, H_V, D, D, device=dev) for _ in range(6)]
     calls = [gdn.bind_decode_step(dec["q"], dec["k"], dec["v"], dec["g"], dec["beta"], st,
                                   dec_out, st) for st in stacks]
-    for c in calls:
-        c()
-    torch.cuda.synchronize()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(31)]
-    for i in range(30):
-        evs[i].record()
-        calls[i % 6]()
-    evs[30].record()
-    torch.cuda.synchronize()
-    cold_us = evs[0].elapsed_time(evs[30]) / 30 * 1e3
+
+    def span_us(fns, reps=30):
+        """Mean duration of fns[i % len(fns)] for i < reps, back to back between two events."""
+        for i in range(3):
+            fns[i % len(fns)]()
+        torch.cuda.synchronize()
+        s0, e0 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        s0.record()
+        for i in range(reps):
+            fns[i % len(fns)]()
+        e0.record()
+        torch.cuda.synchronize()
+        return s0.elapsed_time(e0) / reps * 1e3
+
+    # consecutive decode steps on one 30-layer state stack (the 4096-step decode workload:
+    # the 60 MiB of state stay in the 256 MB MALL from step to step), and the same steps
+    # with six stacks used in turn (360 MiB, so every step reads its state from HBM)
+    steady_us = span_us(calls[:1])
+    cold_us = span_us(calls)
     del stacks, calls
+    # the achievable read + write rate with the library's streaming copy over the decode
+    # step's state bytes (60 MiB), warm (one buffer pair) and cold (six pairs in turn)
+    nst = LAYERS * H_V * D * D
+    pairs = [(torch.ones(nst, device=dev), torch.empty(nst, device=dev)) for _ in range(6)]
+    cps = [(lambda a=a, b=b: gdn.calib_stream_copy(a, b, blocks=1024)) for a, b in pairs]
+    copy_warm_us = span_us(cps[:1])
+    copy_cold_us = span_us(cps)
+    del pairs, cps
 
     # The same decode token as 30 dependent per-layer steps (one sequence each, the layer
     # order of a real model): called one by one, and recorded once as a HIP graph.
@@ -205,7 +232,9 @@ def reference_rates(gdn, dec, dec_out, pre, dev):
     e.record()
     torch.cuda.synchronize()
     copy_gbs = 2 * a.numel() * 4 * 5 / (s.elapsed_time(e) * 1e-3) / 1e9
-    return {"decode_cold_us": cold_us, "copy_GBps": copy_gbs,
+    return {"decode_cold_us": cold_us, "decode_steady_us": steady_us, "copy_GBps": copy_gbs,
+            "stream_copy_warm_GBps": 2 * nst * 4 / (copy_warm_us * 1e-6) / 1e9,
+            "stream_copy_cold_GBps": 2 * nst * 4 / (copy_cold_us * 1e-6) / 1e9,
             "layers_eager_us": layers_eager_us, "layers_graph_us": layers_graph_us,
             "seg": seg, "mfma_tflops": mfma_tflops}
 
@@ -280,9 +309,18 @@ def extra_fields(extra):
     e = extra or {}
     seg = e.get("seg", {})
     cold = e.get("decode_cold_us")
+    steady = e.get("decode_steady_us")
+    rate = lambda us: decode_bytes() / (us * 1e-6) / 1e9 if us else None
+    ratio = lambda a, b: a / b if a and b else None
     return {
+        "decode_steady_us_per_token": steady,
+        "decode_steady_GBps": rate(steady),
         "decode_cold_us_per_token": cold,
-        "decode_cold_GBps": decode_bytes() / (cold * 1e-6) / 1e9 if cold else None,
+        "decode_cold_GBps": rate(cold),
+        "stream_copy_warm_GBps": e.get("stream_copy_warm_GBps"),
+        "stream_copy_cold_GBps": e.get("stream_copy_cold_GBps"),
+        "decode_steady_frac_of_stream_copy": ratio(rate(steady), e.get("stream_copy_warm_GBps")),
+        "decode_cold_frac_of_stream_copy": ratio(rate(cold), e.get("stream_copy_cold_GBps")),
         "decode_per_layer_eager_us_per_token": e.get("layers_eager_us"),
         "decode_per_layer_graph_us_per_token": e.get("layers_graph_us"),
         "prefill_segmented_1024_us_per_layer": seg.get(False, (None, None))[0],
@@ -292,6 +330,24 @@ def extra_fields(extra):
         "hbm_copy_GBps": e.get("copy_GBps"),
         "mfma_bf16_loop_TFLOPs": e.get("mfma_tflops"),
     }
+
+
+def _cpus_allowed():
+    try:
+        return len(os.sched_getaffinity(0))
+    except AttributeError:
+        return None
+
+
+def _cpu_model():
+    """The host CPU's model name (as lscpu prints it, read from /proc/cpuinfo)."""
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.lower().startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
 
 
 def cpu_baseline():
@@ -314,6 +370,8 @@ def cpu_baseline():
     oracle.run(c["q"], c["k"], c["v"], c["g"], c["beta"], None, threads=1)
     one = time.perf_counter() - t0
     return {"value": T_PROMPT / (LAYERS * per_layer), "unit": "tokens/s", "cores": threads,
+            "host_nproc": os.cpu_count(), "host_cpus_allowed": _cpus_allowed(),
+            "host_cpu_model": _cpu_model(),
             "kind": "oracle",
             "sample": f"{layers} layer(s) of the prefill workload (T=4096, 32 V heads, d=128, "
                       f"each its own inputs), {spent:.1f} s of oracle time; value = 4096 / "
@@ -390,6 +448,30 @@ def main():
         torch.cuda.synchronize()
         print("decode steps done", flush=True)
         return
+    if args.mode == "decode-layers":
+        # one decode token as 30 dependent per-layer steps: 5 tokens launched one step at a
+        # time, then 5 tokens as replays of the recorded graph (for a kernel trace)
+        st = torch.zeros(LAYERS, H_V, D, D, device=dev)
+        per = {key: [dec[key][l:l + 1] for l in range(LAYERS)]
+               for key in ("q", "k", "v", "g", "beta")}
+        outs1 = [dec_out[l:l + 1] for l in range(LAYERS)]
+        sts = [st[l:l + 1] for l in range(LAYERS)]
+        eager = [gdn.bind_decode_step(per["q"][l], per["k"][l], per["v"][l], per["g"][l],
+                                      per["beta"][l], sts[l], outs1[l], sts[l])
+                 for l in range(LAYERS)]
+        graph = gdn.DecodeGraph(per["q"], per["k"], per["v"], per["g"], per["beta"], sts,
+                                outs1, stream=torch.cuda.Stream())
+        for _ in range(5):
+            for c in eager:
+                c()
+        torch.cuda.synchronize()
+        print("eager per-layer tokens done", flush=True)
+        for _ in range(5):
+            graph.launch()
+        torch.cuda.synchronize()
+        graph.close()
+        print("graph per-layer tokens done", flush=True)
+        return
     if args.mode == "segmented":
         c = layers[0]
         for ov in (False, True):
@@ -446,6 +528,30 @@ def main():
         torch.cuda.synchronize()
         call_ms += [cev[l].elapsed_time(cev[l + 1]) for l in range(LAYERS)]
 
+    # The 4096-token workload's configured chunk (64 tokens), timed as the timed steps time
+    # the dispatched chunk: the 30 layers' calls back to back between two events, 3 rounds.
+    c64_us = None
+    if not args.core_only and chunk != 64:
+        ws64 = torch.empty(gdn.gdn_workspace_bytes(1, T_PROMPT, H_QK, H_V, D, chunk=64),
+                           device=dev, dtype=torch.uint8)
+        calls64 = [gdn.bind_prefill_chunked(c["q"], c["k"], c["v"], c["g"], c["beta"], None,
+                                            outs[l], states[l:l + 1], ws64, chunk=64)
+                   for l, c in enumerate(layers)]
+        for f in calls64[:3]:
+            f()
+        torch.cuda.synchronize()
+        e64 = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        e64[0].record()
+        for _ in range(3):
+            for f in calls64:
+                f()
+        e64[1].record()
+        torch.cuda.synchronize()
+        c64_us = e64[0].elapsed_time(e64[1]) / (3 * LAYERS) * 1e3
+        del calls64, ws64
+    elif chunk == 64:
+        c64_us = mean_call_s * 1e6
+
     traffic = measured_traffic()
     extra = None if args.core_only else reference_rates(gdn, dec, dec_out, layers[0], dev)
 
@@ -473,6 +579,9 @@ def main():
         "prefill_us_per_call_median": float(statistics.median(call_ms)) * 1e3,
         "prefill_us_per_call_min": min(call_ms) * 1e3,
         "prefill_us_per_call_p90": sorted(call_ms)[int(0.9 * (len(call_ms) - 1))] * 1e3,
+        "prefill_c64_us_per_layer": c64_us,
+        "prefill_c64_hbm_frac": (prefill_bytes() / (c64_us * 1e-6) / 1e9 / HBM_PEAK_GBS
+                                 if c64_us else None),
         **extra_fields(extra),
         "prefill_workspace_bytes": ws.numel(),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,

@@ -20,7 +20,7 @@ __all__ = [
     "gdn_prefill", "gdn_prefill_workspace_bytes", "library_path", "Dims", "BoundCall",
     "bind_prefill_chunked", "bind_prefill_scan", "bind_decode_step", "DecodeGraph",
     "gdn_prefill_segmented", "gdn_prefill_segmented_workspace_bytes", "gdn_prefill_scan_blockwise",
-    "calib_mfma_bf16", "gdn_prefill_segmented_noalloc", "gdn_noalloc_scratch_bytes",
+    "calib_mfma_bf16", "calib_stream_copy", "gdn_prefill_segmented_noalloc", "gdn_noalloc_scratch_bytes",
 ]
 
 GDN_F32, GDN_BF16 = 0, 1
@@ -76,6 +76,7 @@ def _load():
         "gdn_prefill_segmented": (ctypes.c_int, [D, ctypes.c_int64, ctypes.c_int32] + [P] * 9
                                   + [sz, P]),
         "gdn_noalloc_scratch_bytes": (sz, []),
+        "gdn_calib_stream_copy": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32, P]),
         "gdn_prefill_segmented_noalloc": (ctypes.c_int, [D, ctypes.c_int64] + [P] * 9),
     }
     for name, (res, args) in sig.items():
@@ -240,6 +241,17 @@ def calib_mfma_bf16(iters, blocks, sink, stream=None) -> int:
     _check(_load().gdn_calib_mfma_bf16(int(iters), int(blocks), _ptr(sink),
                                        _stream(sink.device, stream)), "gdn_calib_mfma_bf16")
     return int(_load().gdn_calib_mfma_bf16_flops(int(iters), int(blocks)))
+
+
+def calib_stream_copy(src, dst, blocks=1024, stream=None):
+    """Launch the streaming-copy calibration kernel (measurement only): dst <- src, two
+    contiguous device tensors of the same byte size (a multiple of 16)."""
+    nbytes = src.numel() * src.element_size()
+    if not (src.is_cuda and dst.is_cuda and src.is_contiguous() and dst.is_contiguous()
+            and dst.numel() * dst.element_size() == nbytes):
+        raise ValueError("src and dst must be contiguous device tensors of the same byte size")
+    _check(_load().gdn_calib_stream_copy(_ptr(src), _ptr(dst), nbytes, int(blocks),
+                                         _stream(src.device, stream)), "gdn_calib_stream_copy")
 
 
 def gdn_decode_step(q, k, v, g, beta, state_in=None, *, l2_eps=1e-6, out=None,

@@ -700,4 +700,17 @@ gdn_status gdn_calib_mfma_bf16(int64_t iters, int32_t blocks, float* sink, void*
     return finish(launch_mfma_loop(iters, blocks, sink, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_calib_stream_copy(const void* src, void* dst, int64_t bytes, int32_t blocks,
+                                 void* stream)
+{
+    if (!src || !dst) return GDN_ERR_NULL;
+    if (bytes <= 0 || bytes % 16 != 0 || blocks <= 0 || blocks > kMaxCalibBlocks)
+        return GDN_ERR_SHAPE;
+    if (!aligned(src, 16) || !aligned(dst, 16)) return GDN_ERR_ALIGN;
+    const Range a = range_of(src, bytes, 1), b = range_of(dst, bytes, 1);
+    if (overlap(a, b)) return GDN_ERR_ALIAS;
+    (void)hipGetLastError();
+    return finish(launch_stream_copy(src, dst, bytes / 16, blocks, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -1,6 +1,9 @@
-// gdn_calib.hip -- a loop of dense bf16 MFMAs, for the achievable matrix rate that the
-// chunked kernels' MFMA use is reported against (measurement only; the prefill and decode
-// paths never call it).
+// gdn_calib.hip -- calibration kernels (measurement only; the prefill and decode paths never
+// call them):
+//  * a loop of dense bf16 MFMAs, for the achievable matrix rate that the chunked kernels'
+//    MFMA use is reported against;
+//  * a streaming device copy, for the achievable HBM rate (read + write) that the decode
+//    step, which reads and writes every state element once, is reported against.
 //
 // Each wave keeps four independent 32x32x16 accumulators, so consecutive MFMAs never wait
 // for each other, and writes one sum per lane at the end so that nothing is optimised away.
@@ -40,7 +43,29 @@ __global__ void __launch_bounds__(256) mfma_loop_kernel(int64_t iters, float* __
     sink[(int64_t)blockIdx.x * blockDim.x + threadIdx.x] = s;
 }
 
+// Streaming copy: every thread moves one 16-byte element per iteration (load, then store)
+// over a grid-stride loop, so that at any time the whole grid works in one narrow address
+// window and loads and stores of different waves are in flight together. Of the forms
+// measured on MI355X (one to eight elements per thread per iteration, 256 to 8192
+// workgroups, and a tile-per-workgroup copy shaped like the decode step), this one with 1024
+// workgroups moved the most bytes per second, warm and with the buffers out of the MALL.
+__global__ void __launch_bounds__(256) stream_copy_kernel(const float4* __restrict__ src,
+                                                          float4* __restrict__ dst, int64_t n16)
+{
+    const int64_t stride = (int64_t)gridDim.x * blockDim.x;
+    for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n16; i += stride)
+        dst[i] = src[i];
+}
+
 }  // namespace
+
+hipError_t launch_stream_copy(const void* src, void* dst, int64_t n16, int32_t blocks,
+                              hipStream_t stream)
+{
+    hipLaunchKernelGGL(stream_copy_kernel, dim3((unsigned)blocks), dim3(256), 0, stream,
+                       static_cast<const float4*>(src), static_cast<float4*>(dst), n16);
+    return hipGetLastError();
+}
 
 hipError_t launch_mfma_loop(int64_t iters, int32_t blocks, float* sink, hipStream_t stream)
 {

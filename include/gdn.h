@@ -311,6 +311,18 @@ gdn_status gdn_prefill_segmented_noalloc(const gdn_dims* dims, int64_t seg_t, co
 int64_t gdn_calib_mfma_bf16_flops(int64_t iters, int32_t blocks);
 gdn_status gdn_calib_mfma_bf16(int64_t iters, int32_t blocks, float* sink, void* stream);
 
+/*
+ * Calibration (measurement only): copy `bytes` (a positive multiple of 16) from src to dst,
+ * both device pointers, 16-byte aligned and disjoint, with `blocks` workgroups of 256
+ * threads sweeping the buffers in a grid-stride loop of 16-byte elements, on `stream`. The
+ * achievable read + write rate of device memory is 2 * bytes divided by the launch time;
+ * the decode step, which reads and writes each state element once, is reported against it
+ * next to the published 8 TB/s. GDN_ERR_NULL, GDN_ERR_SHAPE (bytes or blocks out of range,
+ * blocks at most 2^20), GDN_ERR_ALIGN, GDN_ERR_ALIAS (the ranges overlap).
+ */
+gdn_status gdn_calib_stream_copy(const void* src, void* dst, int64_t bytes, int32_t blocks,
+                                 void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -410,3 +410,18 @@ def test_noalloc_validation(lib):
     assert 0 < fit <= lib.gdn_noalloc_scratch_bytes() < over
     assert call_noalloc(lib, big, seg_t=2048) == WS
     assert call_noalloc(lib, big, seg_t=4096) == WS
+
+
+def test_calib_stream_copy_validation(lib):
+    """Argument checks of the streaming-copy calibration (no launch on any error)."""
+    P = ctypes.c_void_p
+    a, b = P(0x7F0000000000), P(0x7F0000100000)
+    f = lib.gdn_calib_stream_copy
+    assert f(None, b, 1024, 16, None) == NULL
+    assert f(a, None, 1024, 16, None) == NULL
+    assert f(a, b, 0, 16, None) == SHAPE
+    assert f(a, b, 1000, 16, None) == SHAPE
+    assert f(a, b, 1024, 0, None) == SHAPE
+    assert f(a, b, 1024, (1 << 20) + 1, None) == SHAPE
+    assert f(P(0x7F0000000008), b, 1024, 16, None) == ALIGN
+    assert f(a, P(0x7F0000000200), 1024, 16, None) == ALIAS
