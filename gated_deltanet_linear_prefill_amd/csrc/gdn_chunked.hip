@@ -2047,6 +2047,464 @@ chunk_scan_wide_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, con
     }
 }
 
+// ================================================== scan, 64-token chunks, bf16, d_k = d_v = 128
+// The sequential pass for the workload this library is tuned for (bf16 q/k/v, 128-wide
+// heads, 64-token chunks). One workgroup of eight waves per (sequence, V head, 16 value
+// channels); wave w runs on SIMD w mod 4:
+//   chain waves 0, 1 (SIMDs 0, 1): each holds one d_k half of the state (64 features x 16
+//        channels) in MFMA accumulators and runs the whole recurrence of every chunk from
+//        operands in LDS or registers, with one exchange of partial products per chunk:
+//          P_c = K_c M_c (the halves' parts summed in a fixed order, so both waves form the
+//          same X and U), X = V - diag(a) P_c, U = T' X, W = diag(s) U,
+//          M_{c+1} = Gamma_C M_c + K_c^T W, then its part of P_{c+1} = K_{c+1} M_{c+1} and
+//          the K_{c+1}^T fragments of the next update, read from LDS while K_{c+1} is there;
+//   output waves 2, 3 (SIMDs 2, 3): one window behind, O^T = (Q M_c)^T diag(o) + U^T Ptil^T
+//        for two 16-token row tiles each (tiles 0 and 3, 1 and 2: equal triangular work),
+//        with the Ptil pieces loaded straight into registers a window ahead;
+//   staging waves 4..7 (one per SIMD): every other input straight into LDS one window ahead
+//        of use (loads that write LDS directly), into rings of two chunks.
+// Every ring and exchange slot is indexed by chunk parity, and the loops take two windows
+// per iteration, so every LDS address is fixed at compile time. The chain waves also touch,
+// every window, one cache line per lane of the inputs of the chunk eight ahead (shared out
+// over the workgroups that read them), so that the staging loads hit L2.
+// Windows are separated by workgroup barriers, one per chunk: window -1 forms the state's
+// first partial products; windows 0 .. nwin - 1 the chunks, where nwin is the chunk count
+// rounded up to even (the extra window, when there is one, has s = 0 and Gamma_C = 1 staged,
+// so that it leaves the state unchanged: M <- 1 * M + K^T 0); a last window the last outputs.
+// Staged data of chunks past the sequence is the last chunk's again (or zero scalars), in
+// slots whose products nobody reads. The rings start cleared, so rows past a short last
+// chunk (never written: their loads fall outside the buffer range) hold finite values, which
+// meet zero coefficients (a, s, T', Ptil are zero for tokens past the sequence).
+namespace c64 {
+constexpr int D = 128, C = 64;
+constexpr int RT = 4;        // 16-token row tiles of a chunk
+constexpr int KTC = 2;       // token k tiles (32) of a chunk
+constexpr int KTH = 2;       // feature k tiles (32) per chain wave
+constexpr int MTH = 4;       // 16-feature state tiles per chain wave
+constexpr int NTRI = 6;      // stored lower-triangular 16 x 32 tiles of T' and Ptil
+constexpr int ROWB = 256;    // bytes per staged bf16 row of 128 features
+constexpr int K_BYTES = C * ROWB;  // one chunk of staged K (or Q) rows
+constexpr int NSTG = 4;      // staging waves
+constexpr int NKI = C * ROWB / 1024;  // 1 KB row loads per chunk (4 rows each)
+constexpr int TOUCH_AHEAD = 8;
+}  // namespace c64
+
+template <int P>
+using parity_t = std::integral_constant<int, P>;
+
+__global__ void __launch_bounds__(512)
+chunk64_scan_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__ k,
+                    const uint16_t* __restrict__ v, const char* __restrict__ ws, ChunkWs L,
+                    const float* state_in, float* __restrict__ out, float* state_out, int64_t T,
+                    int h_qk, int h_v, int64_t nblocks)
+{
+    using namespace c64;
+    using G = Geo<D, C, false>;
+    static_assert(G::NTRI == NTRI && G::RT == RT && G::KTC == KTC && G::KTH == KTH &&
+                  G::MTH == MTH && G::H_BYTES == 0, "geometry of the prepared workspace");
+    constexpr int ES = 2;
+    constexpr int RPB = 256 / ROWB;  // staged rows per 64 LDS banks (1)
+    constexpr int NG = ROWB / 16;    // 16-byte granules per staged row
+    constexpr int RPI = 4;           // staged rows per 1 KB load
+
+    // LDS, every ring and exchange by chunk parity
+    __shared__ __align__(16) char s_k[2][K_BYTES];             // K rows (swizzled granules)
+    __shared__ __align__(16) char s_q[2][K_BYTES];             // Q rows (swizzled granules)
+    __shared__ __align__(16) bf16x8 s_tf[2][2 * NTRI][64];     // T' pieces (hi, lo)
+    __shared__ __align__(16) char s_v[2][C * 32];              // V block: 64 tokens x 16 bf16
+    __shared__ __align__(16) float s_sc[2][256];               // a, s, o, Gamma_C
+    __shared__ __align__(16) floatx4 s_pp[2][2][RT][64];       // each chain wave's part of K M
+    __shared__ __align__(16) bf16x8 s_mf[2][2 * KTH][2][64];   // the state as B fragments
+    __shared__ __align__(16) floatx4 s_uf[2][RT][64];          // U (accumulator layout)
+
+    int64_t lin = blockIdx.x;
+    if (nblocks % 8 == 0) lin = (int64_t)(blockIdx.x % 8) * (nblocks / 8) + blockIdx.x / 8;
+    const int cb = (int)(lin % (D / 16));
+    const int64_t nh = lin / (D / 16);
+    const int64_t seq = nh / h_v;
+    const int h = (int)(nh - seq * h_v);
+    const int hq = h / (h_v / h_qk);
+    const int tid = threadIdx.x, l = tid & 63, lr = l & 15, lg = l >> 4;
+    const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int64_t nch = L.nch;
+    const int64_t nwin = nch + (nch & 1);
+
+    const int64_t row_qk = (int64_t)h_qk * D * ES;
+    const int64_t row_v = (int64_t)h_v * D * ES;
+    const int64_t row_o = (int64_t)h_v * D * 4;
+    auto clampc = [&](int64_t c) { return c < 0 ? 0 : (c < nch ? c : nch - 1); };
+    auto tok0_of = [&](int64_t c) { return seq * T + c * C; };
+    auto rows_of = [&](int64_t c) { return (T - c * C) < C ? (T - c * C) : (int64_t)C; };
+    auto vh_of = [&](int64_t c) { return (size_t)((seq * nch + c) * h_v + h); };
+    auto srow = [&](int r, int j) { return r * ROWB + 16 * (j ^ swz<RPB>(r)); };
+
+    // Clear the staged rows and V blocks once (see above). 512 threads, 16 bytes each.
+    for (int o = 16 * tid; o < 2 * K_BYTES; o += 16 * 512) {
+        *reinterpret_cast<u32x4*>(&s_k[0][0] + o) = u32x4{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4*>(&s_q[0][0] + o) = u32x4{0u, 0u, 0u, 0u};
+    }
+    for (int o = 16 * tid; o < 2 * C * 32; o += 16 * 512)
+        *reinterpret_cast<u32x4*>(&s_v[0][0] + o) = u32x4{0u, 0u, 0u, 0u};
+    __syncthreads();
+
+    if (w < 2) {
+        // ======================================================= chain wave hh
+        const int hh = w;
+        const int64_t sbase = nh * (int64_t)D * D;
+        auto st_off = [&](int mt, int e) {
+            const int f = feat_of(mt, 4 * lg + e);
+            return (int)((f * D + cb * 16 + lr) * 4);
+        };
+        floatx4 macc[MTH];  // state tiles MTH hh + i
+        {
+            const auto r = make_rsrc(state_in + (state_in ? sbase : 0), state_in ? (int64_t)D * D * 4 : 0);
+#pragma unroll
+            for (int i = 0; i < MTH; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e) macc[i][e] = buf_elem<float>(r, st_off(MTH * hh + i, e));
+        }
+        bf16x8 mf[KTH][2];
+        auto split_state = [&]() {
+#pragma unroll
+            for (int kk = 0; kk < KTH; ++kk) pair_to_frag(macc[2 * kk], macc[2 * kk + 1], mf[kk][0], mf[kk][1]);
+        };
+        bf16x8 kts[MTH][KTC];  // K^T A fragments of the chunk the next update uses
+        bf16x8 ka[RT][KTH];    // K row A fragments (this wave's features) of the next chunk
+        // From K ring slot S (the chunk after the current one): its K rows and K^T fragments
+        // (two transposing reads each, token slots 0..3 and 4..7) into registers.
+        auto read_next_k = [&](auto slot_c, bf16x8 (*ktn)[KTC]) {
+            constexpr int S = decltype(slot_c)::value;
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+                for (int kk = 0; kk < KTH; ++kk)
+                    ka[rt][kk] = *reinterpret_cast<const bf16x8*>(s_k[S] + srow(16 * rt + lr, 4 * (KTH * hh + kk) + lg));
+#pragma unroll
+            for (int i = 0; i < MTH; ++i)
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt) {
+                    const int r = 32 * kt + 4 * lg + (lr >> 2);
+                    const int j = 4 * (KTH * hh + (i >> 1)) + (lr & 3);
+                    const char* base = s_k[S] + 8 * (i & 1);
+                    const bf16x4 x0 = lds_read_tr16(base + srow(r, j));
+                    const bf16x4 x1 = lds_read_tr16(base + srow(r + 16, j));
+                    ktn[i][kt] = bf16x8{x0[0], x0[1], x0[2], x0[3], x1[0], x1[1], x1[2], x1[3]};
+                }
+        };
+        floatx4 pp[RT];  // this wave's part of K M for the chunk about to be processed
+        // This wave's part of K M for the next chunk (K rows in ka), published with the state
+        // fragments in exchange slot S.
+        auto publish_next = [&](auto slot_c) {
+            constexpr int S = decltype(slot_c)::value;
+#pragma unroll
+            for (int kk = 0; kk < KTH; ++kk)
+#pragma unroll
+                for (int p = 0; p < 2; ++p) s_mf[S][KTH * hh + kk][p][l] = mf[kk][p];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kk = 0; kk < KTH; ++kk) acc = mfma_split<1, 2>(&ka[rt][kk], mf[kk], acc);
+                pp[rt] = acc;
+                s_pp[S][hh][rt][l] = acc;
+            }
+        };
+
+        // Cache-line touches: one 128-byte line per lane of a chunk's inputs. K and Q rows go
+        // round the workgroups of the QK head, workspace blocks and V rows round the
+        // workgroups of the V head; lanes past this workgroup's share touch lane 0's line.
+        // The lane's line in chunk j is touch_base + j * touch_step (full chunks; a partial
+        // last chunk is touched as the chunk before it).
+        uint64_t touch_base, touch_step;
+        {
+            constexpr int LPR128 = (D * ES + 127) / 128;
+            constexpr int NCB = D / 16;
+            constexpr int TL = (int)(G::TRI_BYTES / 128);
+            constexpr int SCL = (int)((G::SC_BYTES + 127) / 128) - 1;
+            constexpr int NWS = 2 * TL + SCL;
+            constexpr int HALF = C * LPR128;
+            auto pick = [](bool cond, uint64_t x, uint64_t y) {
+                const uint64_t m = 0 - (uint64_t)cond;
+                return (x & m) | (y & ~m);
+            };
+            const int grp = h_v / h_qk, nbq = grp * NCB, iq = (h % grp) * NCB + cb;
+            const int nq_mine = (2 * HALF - iq + nbq - 1) / nbq;
+            const int nv_mine = (NWS + HALF - cb + NCB - 1) / NCB;
+            // the second chain wave touches lane 0's line only (its loop issues the same
+            // loads as the first's, see below, but need not repeat its requests)
+            const int li = (l < nq_mine + nv_mine && hh == 0) ? l : 0;
+            const bool isq = li < nq_mine;
+            const int lq = iq + nbq * li, rq = lq < HALF ? lq : lq - HALF;
+            const uint64_t q0 = pick(lq < HALF, (uint64_t)k, (uint64_t)q) +
+                                (uint64_t)(((seq * T + rq / LPR128) * h_qk + hq) * (int64_t)D * ES + 128 * (rq % LPR128));
+            const uint64_t qs = (uint64_t)C * h_qk * D * ES;
+            const int lv = isq ? 0 : cb + NCB * (li - nq_mine);
+            const uint64_t vh0 = (uint64_t)(seq * nch * h_v + h), wsb = (uint64_t)ws;
+            const uint64_t w_tt = wsb + L.tt + vh0 * G::TRI_BYTES + 128 * lv;
+            const uint64_t w_pt = wsb + L.pt + vh0 * G::TRI_BYTES + 128 * (lv - TL);
+            const uint64_t w_sc = wsb + L.sc + vh0 * G::SC_BYTES + 128 * (lv - 2 * TL);
+            uint64_t w0 = pick(lv < 2 * TL, w_pt, w_sc);
+            uint64_t ws_step = pick(lv < 2 * TL, (uint64_t)h_v * G::TRI_BYTES, (uint64_t)h_v * G::SC_BYTES);
+            w0 = pick(lv < TL, w_tt, w0);
+            const int rv = lv - NWS;
+            const uint64_t v0 = (uint64_t)v + (uint64_t)(((seq * T + rv / LPR128) * h_v + h) * (int64_t)D * ES + 128 * (rv % LPR128));
+            const uint64_t vs = (uint64_t)C * h_v * D * ES;
+            touch_base = pick(isq, q0, pick(lv < NWS, w0, v0));
+            touch_step = pick(isq, qs, pick(lv < NWS, ws_step, vs));
+        }
+        // the last chunk touched: the last full one (the sequence's only, partial, chunk: none)
+        const int64_t tlast = rows_of(nch - 1) == C ? nch - 1 : nch - 2;
+        const uint64_t touch_first = tlast >= 0 ? touch_base : (uint64_t)ws;
+        uint64_t touch_at = touch_first + (uint64_t)(tlast < TOUCH_AHEAD ? (tlast > 0 ? tlast : 0) : TOUCH_AHEAD) * touch_step;
+
+        split_state();
+        barrier_lds_only();               // K rows of chunk 0 staged
+        read_next_k(parity_t<0>{}, kts);  // window -1: K_0 and K_0^T
+        publish_next(parity_t<0>{});      // this wave's part of K_0 M_0
+
+        // One chunk. Every LDS read of the window is issued right after its barrier: the
+        // partner's partial products, V and a (which X waits for) first, then T', s and the
+        // next chunk's K rows and K^T fragments (its ring slot is stable all window), so that
+        // one LDS round trip precedes X and the last products wait for no read. The work
+        // then runs by token k tile, so that the hi/lo splits of one tile overlap the
+        // products of the other.
+        auto window = [&](auto par_c, int64_t c, uint32_t& touched) {
+            constexpr int PAR = decltype(par_c)::value;  // c & 1
+            barrier_lds_only();
+            floatx4 po[RT], vv[RT], av[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) {
+                po[rt] = s_pp[PAR][hh ^ 1][rt][l];
+                const bf16x4 vr = lds_read_tr16(s_v[PAR] + (16 * rt + 4 * lg + (lr >> 2)) * 32 + 8 * (lr & 3));
+                vv[rt] = floatx4{(float)vr[0], (float)vr[1], (float)vr[2], (float)vr[3]};
+                av[rt] = *reinterpret_cast<const floatx4*>(&s_sc[PAR][16 * rt + 4 * lg]);
+            }
+            bf16x8 tf[2 * NTRI];
+#pragma unroll
+            for (int pi = 0; pi < 2 * NTRI; ++pi) tf[pi] = s_tf[PAR][pi][l];
+            floatx4 sv[RT];
+#pragma unroll
+            for (int rt = 0; rt < RT; ++rt) sv[rt] = *reinterpret_cast<const floatx4*>(&s_sc[PAR][C + 16 * rt + 4 * lg]);
+            const float gc = s_sc[PAR][3 * C];
+            bf16x8 ktn[MTH][KTC];
+            read_next_k(parity_t<PAR ^ 1>{}, ktn);  // chunk c + 1 (past the last: never used)
+            // X = V - diag(a) K M, the two parts added in the order chain 0 + chain 1, as B
+            // fragments by token k tile
+            bf16x8 xf[KTC][2];
+#pragma unroll
+            for (int kt = 0; kt < KTC; ++kt) {
+                floatx4 x2[2];
+#pragma unroll
+                for (int hf = 0; hf < 2; ++hf) {
+                    const int rt = 2 * kt + hf;
+                    const floatx4 z = hh == 0 ? pp[rt] + po[rt] : po[rt] + pp[rt];
+                    x2[hf] = vv[rt] - av[rt] * z;
+                }
+                pair_to_frag(x2[0], x2[1], xf[kt][0], xf[kt][1]);
+            }
+            // U = T' X (lower triangular: row tile rt uses token k tiles 0 .. rt / 2),
+            // W = diag(s) U, then M <- Gamma_C M + K^T W, token k tile by token k tile
+            floatx4 u[RT];
+            bf16x8 wf[KTC][2];
+            auto u_tile = [&](int rt) {
+                floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                for (int kt = 0; 2 * kt <= rt; ++kt) acc = mfma_split<2, 2>(&tf[2 * (tri_off(rt) + kt)], xf[kt], acc);
+                u[rt] = acc;
+            };
+            auto w_frag = [&](int kt) {
+                const floatx4 w0 = u[2 * kt] * sv[2 * kt], w1 = u[2 * kt + 1] * sv[2 * kt + 1];
+                pair_to_frag(w0, w1, wf[kt][0], wf[kt][1]);
+            };
+            u_tile(0);
+            u_tile(1);
+            w_frag(0);
+            u_tile(2);
+            u_tile(3);
+#pragma unroll
+            for (int i = 0; i < MTH; ++i) macc[i] = mfma_split<1, 2>(&kts[i][0], wf[0], gc * macc[i]);
+            w_frag(1);
+            if (hh == 0) {
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) s_uf[PAR][rt][l] = u[rt];
+            }
+#pragma unroll
+            for (int i = 0; i < MTH; ++i) macc[i] = mfma_split<1, 2>(&kts[i][1], wf[1], macc[i]);
+            split_state();
+            publish_next(parity_t<PAR ^ 1>{});  // chunk c + 1 (past the last: never read)
+#pragma unroll
+            for (int i = 0; i < MTH; ++i)
+#pragma unroll
+                for (int kt = 0; kt < KTC; ++kt) kts[i][kt] = ktn[i][kt];
+            // Touch the lines of chunk c + 8 after the touch of window c - 2 has landed. Both
+            // chain waves issue a touch (with no branch around it, the wait for the earlier
+            // touch is exact: this wave issues no other vector memory operations in the loop).
+            asm volatile("" ::"v"(touched));
+            touched = *(const __attribute__((address_space(1))) uint32_t*)touch_at;
+            if (c + TOUCH_AHEAD < tlast) touch_at += touch_step;  // wave-uniform
+        };
+        uint32_t ta = 0, tb = 0;
+#pragma unroll 1
+        for (int64_t c = 0; c < nwin; c += 2) {
+            window(parity_t<0>{}, c, ta);
+            window(parity_t<1>{}, c + 1, tb);
+        }
+        barrier_lds_only();  // the last window
+        asm volatile("" ::"v"(ta), "v"(tb));
+        {
+            const auto r = make_rsrc(state_out + sbase, (int64_t)D * D * 4);
+#pragma unroll
+            for (int i = 0; i < MTH; ++i)
+#pragma unroll
+                for (int e = 0; e < 4; ++e)
+                    __builtin_amdgcn_raw_buffer_store_b32(__float_as_uint(macc[i][e]), r, st_off(MTH * hh + i, e), 0, 0);
+        }
+    } else if (w < 4) {
+        // ======================================================= output wave
+        // Row tiles OW and 3 - OW (equal triangular work), fixed at compile time.
+        auto output_wave = [&](auto owc) {
+            constexpr int OW = decltype(owc)::value;
+            constexpr int RTS[2] = {OW, 3 - OW};
+            floatx4 qm[2];         // (Q M_c)^T of the chunk being finished
+            float ov[2];           // o of token lr of each row tile of that chunk
+            bf16x8 pf[2][KTC][2];  // its Ptil^T pieces: [row tile][token k tile][hi, lo]
+            auto start_chunk = [&](auto par_c, int64_t c) {
+                constexpr int PAR = decltype(par_c)::value;
+                const auto r = make_rsrc(ws + L.pt + vh_of(c) * G::TRI_BYTES, G::TRI_BYTES);
+#pragma unroll
+                for (int i = 0; i < 2; ++i)
+#pragma unroll
+                    for (int kt = 0; kt < KTC; ++kt) {
+                        if (2 * kt > RTS[i]) continue;
+                        const int o = (tri_off(RTS[i]) + kt) * 2048 + l * 16;
+                        pf[i][kt][0] = buf_bf16x8(r, o);
+                        pf[i][kt][1] = buf_bf16x8(r, o + 1024);
+                    }
+                bf16x8 mfr[2 * KTH][2];
+#pragma unroll
+                for (int kt = 0; kt < 2 * KTH; ++kt)
+#pragma unroll
+                    for (int p = 0; p < 2; ++p) mfr[kt][p] = s_mf[PAR][kt][p][l];
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    ov[i] = s_sc[PAR][2 * C + 16 * RTS[i] + lr];
+                    floatx4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+                    for (int kt = 0; kt < 2 * KTH; ++kt) {
+                        const bf16x8 qa = *reinterpret_cast<const bf16x8*>(s_q[PAR] + srow(16 * RTS[i] + lr, 4 * kt + lg));
+                        acc = mfma_split<2, 1>(mfr[kt], &qa, acc);
+                    }
+                    qm[i] = acc;
+                }
+            };
+            // O^T = U^T Ptil^T + (Q M)^T diag(o), 16 value channels x 16 tokens per row tile:
+            // each lane ends up with four consecutive channels of one token (one 16-byte store).
+            auto finish_chunk = [&](auto par_c, int64_t c) {
+                constexpr int PAR = decltype(par_c)::value;
+                floatx4 urow[RT];
+#pragma unroll
+                for (int rt = 0; rt < RT; ++rt) urow[rt] = s_uf[PAR][rt][l];
+                bf16x8 ufr[KTC][2];
+                rows_to_frags<RT, KTC>(urow, ufr);
+                const auto r_o = make_rsrc(out + (tok0_of(c) * h_v + h) * (int64_t)D + cb * 16,
+                                           (rows_of(c) - 1) * row_o + 64);
+#pragma unroll
+                for (int i = 0; i < 2; ++i) {
+                    floatx4 acc = ov[i] * qm[i];
+#pragma unroll
+                    for (int kt = 0; kt < KTC; ++kt)
+                        if (2 * kt <= RTS[i]) acc = mfma_split<2, 2>(ufr[kt], pf[i][kt], acc);
+                    __builtin_amdgcn_raw_buffer_store_b128(__builtin_bit_cast(u32x4, acc), r_o,
+                                                           (int)((16 * RTS[i] + lr) * row_o) + lg * 16, 0, 0);
+                }
+            };
+            // window c: finish chunk c - 1, start chunk c
+            auto window = [&](auto par_c, int64_t c) {
+                constexpr int PAR = decltype(par_c)::value;
+                barrier_lds_only();
+                if (c >= 1 && c <= nch) finish_chunk(parity_t<PAR ^ 1>{}, c - 1);
+                if (c < nch) start_chunk(par_c, c);
+            };
+            barrier_lds_only();  // window -1
+#pragma unroll 1
+            for (int64_t c = 0; c < nwin; c += 2) {
+                window(parity_t<0>{}, c);
+                window(parity_t<1>{}, c + 1);
+            }
+            window(parity_t<0>{}, nwin);  // the last window
+            __builtin_amdgcn_s_waitcnt(0);
+        };
+        if (w == 2) output_wave(std::integral_constant<int, 0>{});
+        else output_wave(std::integral_constant<int, 1>{});
+    } else {
+        // ======================================================= staging wave hs
+        const int hs = w - 4;
+        auto qk_rsrc = [&](const uint16_t* base, int64_t c) {
+            return make_rsrc(base + (tok0_of(c) * h_qk + hq) * (int64_t)D, (rows_of(c) - 1) * row_qk + D * ES);
+        };
+        // K or Q rows of chunk c straight into `dst`: load m covers staged rows 4 mi .. 4 mi + 3
+        // (mi = hs + NSTG m), 1 KB, lane l landing at byte 16 l of it.
+        auto dma_rows = [&](const uint16_t* base, int64_t c, char* dst) {
+            const auto r = qk_rsrc(base, clampc(c));
+#pragma unroll
+            for (int m = 0; m < NKI / NSTG; ++m) {
+                const int mi = hs + NSTG * m;
+                const int row = RPI * mi + l / NG, pos = l % NG;
+                const int g = pos ^ swz<RPB>(row);
+                load_to_lds(r, dst + mi * 1024, (int)((uint32_t)(row * row_qk) + (uint32_t)(16 * g)));
+            }
+        };
+        // window c stages what window c + 1 reads: K rows of chunk c + 2 (into the slot of
+        // chunk c, whose reads ended in window c - 1), and the Q rows, T' pieces, V block
+        // and scalars of chunk c + 1. Chunks past the sequence: the last chunk's rows and
+        // pieces again, and scalars s = 0, Gamma_C = 1 (an update that changes nothing).
+        auto stage = [&](auto par_c, int64_t c) {
+            constexpr int PAR = decltype(par_c)::value;  // c & 1
+            constexpr int NXT = PAR ^ 1;                 // (c + 1) & 1
+            const int64_t j = c + 1, jc = clampc(j);
+            dma_rows(k, c + 2, s_k[PAR]);
+            dma_rows(q, j, s_q[NXT]);
+            {
+                const auto r = make_rsrc(ws + L.tt + vh_of(jc) * G::TRI_BYTES, G::TRI_BYTES);
+#pragma unroll
+                for (int m = 0; hs + NSTG * m < 2 * NTRI; ++m)
+                    load_to_lds(r, s_tf[NXT][hs + NSTG * m], (hs + NSTG * m) * 1024 + l * 16);
+            }
+            if (hs == 0) {
+                const auto r_v = make_rsrc(v + (tok0_of(jc) * h_v + h) * (int64_t)D + cb * 16,
+                                           (rows_of(jc) - 1) * row_v + 32);
+#pragma unroll
+                for (int m = 0; m < 2; ++m) {
+                    const int t = 32 * m + l / 2;
+                    load_to_lds(r_v, s_v[NXT] + m * 1024, (int)((uint32_t)(t * row_v) + (uint32_t)(16 * (l & 1))));
+                }
+            } else if (hs == 1) {
+                if (j < nch) {
+                    load_to_lds(make_rsrc(ws + L.sc + vh_of(j) * G::SC_BYTES, G::SC_BYTES), s_sc[NXT], 16 * l);
+                } else {
+                    s_sc[NXT][C + l] = 0.f;
+                    if (l == 0) s_sc[NXT][3 * C] = 1.f;
+                }
+            }
+        };
+        dma_rows(k, 0, s_k[0]);
+        __builtin_amdgcn_s_waitcnt(0);
+        barrier_lds_only();  // window -1
+        stage(parity_t<1>{}, -1);
+        __builtin_amdgcn_s_waitcnt(0);  // this window's loads have landed in LDS
+#pragma unroll 1
+        for (int64_t c = 0; c < nwin; c += 2) {
+            barrier_lds_only();
+            stage(parity_t<0>{}, c);
+            __builtin_amdgcn_s_waitcnt(0);
+            barrier_lds_only();
+            stage(parity_t<1>{}, c + 1);
+            __builtin_amdgcn_s_waitcnt(0);
+        }
+        barrier_lds_only();  // the last window
+    }
+}
+
 template <int D, int C, typename TIn>
 hipError_t launch_chunked_t(const Call& cl, int parts)
 {
@@ -2069,6 +2527,10 @@ hipError_t launch_chunked_t(const Call& cl, int parts)
         hipLaunchKernelGGL((chunk_scan_kernel<D, C, TIn>), dim3((unsigned)scan_blocks),
                            dim3(ScanGeo<D, C, TIn>::THREADS), 0, cl.stream, q, k, v, ws, L,
                            cl.state_in, cl.out, cl.state_out, cl.t, cl.h_qk, cl.h_v, scan_blocks);
+    } else if constexpr (C == 64 && D == 128 && !F32IN) {
+        hipLaunchKernelGGL(chunk64_scan_kernel, dim3((unsigned)scan_blocks), dim3(512), 0, cl.stream,
+                           q, k, v, ws, L, cl.state_in, cl.out, cl.state_out, cl.t, cl.h_qk,
+                           cl.h_v, scan_blocks);
     } else {
         hipLaunchKernelGGL((chunk_scan_wide_kernel<D, C, TIn>), dim3((unsigned)scan_blocks), dim3(256), 0,
                            cl.stream, q, k, v, ws, L, cl.state_in, cl.out, cl.state_out, cl.t,
