@@ -21,6 +21,7 @@ __all__ = [
     "bind_prefill_chunked", "bind_prefill_scan", "bind_decode_step", "DecodeGraph",
     "gdn_prefill_segmented", "gdn_prefill_segmented_workspace_bytes", "gdn_prefill_scan_blockwise",
     "calib_mfma_bf16", "calib_stream_copy", "gdn_prefill_segmented_noalloc", "gdn_noalloc_scratch_bytes",
+    "debug_fill_lds",
 ]
 
 GDN_F32, GDN_BF16 = 0, 1
@@ -78,6 +79,7 @@ def _load():
         "gdn_noalloc_scratch_bytes": (sz, []),
         "gdn_calib_stream_copy": (ctypes.c_int, [P, P, ctypes.c_int64, ctypes.c_int32, P]),
         "gdn_prefill_segmented_noalloc": (ctypes.c_int, [D, ctypes.c_int64] + [P] * 9),
+        "gdn_debug_fill_lds": (ctypes.c_int, [ctypes.c_uint32, ctypes.c_int32, P, P]),
     }
     for name, (res, args) in sig.items():
         f = getattr(lib, name)
@@ -252,6 +254,18 @@ def calib_stream_copy(src, dst, blocks=1024, stream=None):
         raise ValueError("src and dst must be contiguous device tensors of the same byte size")
     _check(_load().gdn_calib_stream_copy(_ptr(src), _ptr(dst), nbytes, int(blocks),
                                          _stream(src.device, stream)), "gdn_calib_stream_copy")
+
+
+def debug_fill_lds(sink, pattern=0x7FC00000, blocks=1024, stream=None):
+    """Fill the LDS of every CU with a 32-bit pattern (testing only; default a quiet NaN),
+    so that a kernel launched next on the same stream that reads LDS it never wrote sees
+    that pattern. `sink`: an int32 device tensor of at least one element, written only if
+    the fill failed."""
+    _check_tensor("sink", sink, (sink.numel(),), torch.int32, sink.device)
+    if sink.numel() < 1:
+        raise ValueError("sink: need at least one element")
+    _check(_load().gdn_debug_fill_lds(int(pattern) & 0xFFFFFFFF, int(blocks), _ptr(sink),
+                                      _stream(sink.device, stream)), "gdn_debug_fill_lds")
 
 
 def gdn_decode_step(q, k, v, g, beta, state_in=None, *, l2_eps=1e-6, out=None,

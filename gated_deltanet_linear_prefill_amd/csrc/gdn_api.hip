@@ -713,4 +713,13 @@ gdn_status gdn_calib_stream_copy(const void* src, void* dst, int64_t bytes, int3
     return finish(launch_stream_copy(src, dst, bytes / 16, blocks, static_cast<hipStream_t>(stream)));
 }
 
+gdn_status gdn_debug_fill_lds(uint32_t pattern, int32_t blocks, uint32_t* sink, void* stream)
+{
+    if (!sink) return GDN_ERR_NULL;
+    if (blocks <= 0 || blocks > kMaxCalibBlocks) return GDN_ERR_SHAPE;
+    if (!aligned(sink, 4)) return GDN_ERR_ALIGN;
+    (void)hipGetLastError();
+    return finish(launch_lds_fill(pattern, blocks, sink, static_cast<hipStream_t>(stream)));
+}
+
 }  // extern "C"

@@ -3,7 +3,10 @@
 //  * a loop of dense bf16 MFMAs, for the achievable matrix rate that the chunked kernels'
 //    MFMA use is reported against;
 //  * a streaming device copy, for the achievable HBM rate (read + write) that the decode
-//    step, which reads and writes every state element once, is reported against.
+//    step, which reads and writes every state element once, is reported against;
+//  * an LDS fill (diagnostic): workgroups that take a CU's whole LDS and fill it with one
+//    32-bit pattern, so that a kernel launched after it that reads LDS it never wrote sees
+//    that pattern (a NaN, say) rather than whatever the previous kernel left there.
 //
 // Each wave keeps four independent 32x32x16 accumulators, so consecutive MFMAs never wait
 // for each other, and writes one sum per lane at the end so that nothing is optimised away.
@@ -57,7 +60,25 @@ __global__ void __launch_bounds__(256) stream_copy_kernel(const float4* __restri
         dst[i] = src[i];
 }
 
+// 160 KB of LDS per workgroup: the whole of a CU's LDS, so one workgroup per CU at a time.
+constexpr int kFillLdsBytes = 160 * 1024;
+
+__global__ void __launch_bounds__(256) lds_fill_kernel(uint32_t pattern, uint32_t* __restrict__ sink)
+{
+    __shared__ __align__(16) uint32_t s_fill[kFillLdsBytes / 4];
+    for (int i = threadIdx.x; i < kFillLdsBytes / 4; i += 256) s_fill[i] = pattern;
+    __syncthreads();
+    // one read back, so that the stores are kept
+    if (threadIdx.x == 0 && s_fill[(blockIdx.x * 977u) % (kFillLdsBytes / 4)] != pattern) sink[0] = 1u;
+}
+
 }  // namespace
+
+hipError_t launch_lds_fill(uint32_t pattern, int32_t blocks, uint32_t* sink, hipStream_t stream)
+{
+    hipLaunchKernelGGL(lds_fill_kernel, dim3((unsigned)blocks), dim3(256), 0, stream, pattern, sink);
+    return hipGetLastError();
+}
 
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t n16, int32_t blocks,
                               hipStream_t stream)

@@ -312,6 +312,15 @@ __device__ __forceinline__ void tri_tile(int t, int& rt, int& ct)
     ct = t - rt * (rt + 1) / 2;
 }
 
+// A workgroup barrier that waits only for this wave's LDS operations: the other waves see
+// its LDS writes, while its global loads and stores may still be in flight. (__syncthreads()
+// also waits for every outstanding global store and for loads that write LDS directly; the
+// kernels wait for those explicitly where a result depends on them.)
+__device__ __forceinline__ void barrier_lds_only()
+{
+    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
 // =============================================================================== prep
 // Fragment index fi of a compact lower-triangular operand -> (row tile rt, k tile kt).
 __device__ __forceinline__ void tri_frag(int fi, int& rt, int& kt)
@@ -322,7 +331,9 @@ __device__ __forceinline__ void tri_frag(int fi, int& rt, int& kt)
 }
 
 // Four waves per SIMD (registers for four resident workgroups per CU): the kernel is bound by
-// latency, and the register allocation fits without spills.
+// latency, and the register allocation fits without spills. Phases are separated by barriers
+// that wait for LDS only: nothing in the workgroup reads back the workspace it stores, so a
+// phase never waits for the previous phase's stores to complete.
 template <int D, int C, typename TIn>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ g,
@@ -337,25 +348,30 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     constexpr int KS = DP + 8;    // LDS row stride of the K / Q pieces (bf16)
     constexpr int CS = CP + 4;    // LDS row stride of the CP x CP fp32 matrices
     // The V heads of the QK head are taken NHP at a time, NWH waves each: for chunks of up to
-    // 32 tokens two heads side by side (the diagonal solve needs one wave, the other writes
-    // Ptil meanwhile), longer chunks one head with all four waves.
-    constexpr int NWH = C <= 32 ? 2 : 4;           // waves per V head
+    // 64 tokens two heads side by side (the diagonal solve needs one wave, the other writes
+    // Ptil meanwhile), 128-token chunks one head with all four waves. For 64-token chunks T
+    // is formed in place of A (INPLACE), so that both heads' matrices fit the LDS that four
+    // resident workgroups per CU leave.
+    constexpr int NWH = C <= 64 ? 2 : 4;           // waves per V head
     constexpr int NHP = 4 / NWH;                   // V heads per pass
+    constexpr bool INPLACE = C == 64;
     constexpr size_t KQ_LDS = (size_t)2 * NS * CP * KS * 2;
-    constexpr size_t AT_LDS = (size_t)NHP * 2 * CP * CS * 4;
+    constexpr size_t AT_LDS = (size_t)NHP * (INPLACE ? 1 : 2) * CP * CS * 4;
     constexpr size_t U_LDS = KQ_LDS > AT_LDS ? KQ_LDS : AT_LDS;
-    // Waves of a head that solve its diagonal blocks (one lane per column); the others write
-    // Ptil meanwhile (all of the head's waves when the diagonal blocks take them all).
+    // The Gram tiles are shared by the V heads of a pass: every wave forms its share of them
+    // once and writes A and Ptil for all NHP heads from it. The first NBW waves of each head
+    // slot solve the diagonal blocks of T (one lane per column) while the others write Ptil,
+    // so the Ptil fragments go to those others first (rank prk).
+    constexpr int NFW = (NTRI + 3) / 4;  // Ptil fragments per wave
     constexpr int NBW = (NB * 16 + 63) / 64;
-    constexpr int PW0 = NBW < NWH ? NBW : 0;      // first Ptil wave of a head
-    constexpr int NPW = NWH - PW0;                // Ptil waves per head
-    constexpr int NFW = (NTRI + NPW - 1) / NPW;   // Ptil fragments per Ptil wave
+    constexpr int NNS = NHP * (NWH - NBW);  // waves that do not solve
 
     // The K and Q chunks (first phases) and the A / T matrices (later phases) share one
     // buffer; the Gram matrices live in registers in between.
     __shared__ __align__(16) char s_buf[U_LDS];
     __shared__ float s_rk[CP], s_rq[CP];
-    __shared__ float s_gam[NHP][CP], s_beta[NHP][CP], s_sv[NHP][CP];
+    __shared__ float s_gam[NHP][CP], s_beta[NHP][CP];
+    __shared__ float s_sv[G::WITH_H ? NHP : 1][G::WITH_H ? CP : 1];  // s for H (chunks <= 32)
     __shared__ float s_x[4][16][17];  // per-wave 16x16 scratch
     auto s_kq = [&](int which, int part, int r, int f) -> __bf16& {
         return reinterpret_cast<__bf16*>(s_buf)[(((size_t)which * NS + part) * CP + r) * KS + f];
@@ -371,13 +387,18 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     const int w = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform: scalar branches
     const int pm = w / NWH, wl = w % NWH;  // the head slot of this wave, its index there
     const int pt = tid - 64 * NWH * pm;    // thread index within the head slot
+    const int prk = wl >= NBW ? pm * (NWH - NBW) + wl - NBW : NNS + pm * NBW + wl;
     const int grp = h_v / h_qk;
     const int64_t tok0 = seq * T + c0;  // flattened token index of the chunk's first token
-    float(*s_a)[CS] = reinterpret_cast<float(*)[CS]>(s_buf + (size_t)pm * 2 * CP * CS * 4);
-    float(*s_t)[CS] = reinterpret_cast<float(*)[CS]>(s_buf + ((size_t)pm * 2 + 1) * CP * CS * 4);
-    // V head of slot pm in the pass starting at head g0 (a slot past the QK head's V heads
+    float(*s_a)[CS] = reinterpret_cast<float(*)[CS]>(s_buf + (size_t)pm * (INPLACE ? 1 : 2) * CP * CS * 4);
+    float(*s_t)[CS] = INPLACE ? s_a : reinterpret_cast<float(*)[CS]>(s_buf + ((size_t)pm * 2 + 1) * CP * CS * 4);
+    // V head of slot p in the pass starting at head g0 (a slot past the QK head's V heads
     // repeats the pass's first head: the same values are computed and written twice)
-    auto head_of = [&](int g0) { return hq * grp + (g0 + pm < grp ? g0 + pm : g0); };
+    auto head_at = [&](int g0, int p) { return hq * grp + (g0 + p < grp ? g0 + p : g0); };
+    auto head_of = [&](int g0) { return head_at(g0, pm); };
+    auto a_of = [&](int p) {
+        return reinterpret_cast<float(*)[CS]>(s_buf + (size_t)p * (INPLACE ? 1 : 2) * CP * CS * 4);
+    };
 
     // Gate and write strength of one V head for this chunk (the first wave of each head
     // slot; E tokens per lane), loaded one pass ahead of their use.
@@ -474,7 +495,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             }
         }
     }
-    __syncthreads();
+    barrier_lds_only();
 
     // ---- phase 2: Gram matrices from the raw inputs, kept in registers for every V head
     //      of this QK head.
@@ -484,7 +505,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     //    lane holds in the two tiles are the eight k slots (permuted token order) of the
     //    B fragment of Ptil^T the scan kernel multiplies U^T with.
     constexpr int NTL = RT * (RT + 1) / 2;
-    constexpr int NTW = (NTL + NWH - 1) / NWH;  // K K^T tiles per wave (each head slot has all)
+    constexpr int NTW = (NTL + 3) / 4;  // K K^T tiles per wave
     constexpr int NPG = NS == 1 ? 1 : 3; // split passes of a Gram product
     // Gram tile: rows of chunk `wa` (0 = K, 1 = Q) tile ta against rows of chunk `wb` tile tb.
     auto gram = [&](int wa, int ta, int wb, int tb) {
@@ -510,7 +531,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 #pragma unroll
     for (int i = 0; i < NTW; ++i) {
         gk[i] = floatx4{0.f, 0.f, 0.f, 0.f};
-        const int ti = wl + NWH * i;
+        const int ti = w + 4 * i;
         if (ti < NTL) {
             int rt, ct;
             tri_tile(ti, rt, ct);
@@ -521,8 +542,8 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 #pragma unroll
     for (int i = 0; i < NFW; ++i) {
         gp[i][0] = gp[i][1] = floatx4{0.f, 0.f, 0.f, 0.f};
-        const int fi = wl - PW0 + NPW * i;
-        if (wl >= PW0 && fi < NTRI) {
+        const int fi = prk + 4 * i;
+        if (fi < NTRI) {
             int rt, kt;
             tri_frag(fi, rt, kt);
             gp[i][0] = gram(0, 2 * kt, 1, rt);
@@ -568,7 +589,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             for (int kt = 0; kt < KTC; ++kt) pair_to_frag(gt[2 * kt], gt[2 * kt + 1], gnb[i][kt][0], gnb[i][kt][1]);
         }
     }
-    __syncthreads();  // the K / Q buffer becomes A / T below
+    barrier_lds_only();  // the K / Q buffer becomes A / T below
 
     for (int g0 = 0; g0 < grp; g0 += NHP) {
         const int hv = head_of(g0);
@@ -600,7 +621,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             }
             if (g0 + NHP < grp) load_gb(head_of(g0 + NHP));
         }
-        __syncthreads();
+        barrier_lds_only();
 
         // ---- per-token scalars a = Gamma r_k, s = r_k exp(gamma_C - gamma), o = Gamma r_q
         //      and Gamma_C (padded tokens carry r_k = r_q = 0, so their scalars are zero)
@@ -614,32 +635,39 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
                 scp[i] = Gi * s_rk[i];
                 scp[CP + i] = si;
                 scp[2 * CP + i] = Gi * s_rq[i];
-                s_sv[pm][i] = si;  // for H below
+                if constexpr (G::WITH_H) s_sv[pm][i] = si;  // for H below
             }
             if (pt == 0) scp[3 * CP] = expf(gam_c);
         }
 
         // ---- phase 4: A = strictly lower (beta_r exp(gamma_r - gamma_s) r_k,r r_k,s k_r . k_s)
+        //      for every V head of the pass
 #pragma unroll
         for (int i = 0; i < NTW; ++i) {
-            const int ti = wl + NWH * i;
+            const int ti = w + 4 * i;
             if (ti < NTL) {
                 int rt, ct;
                 tri_tile(ti, rt, ct);
 #pragma unroll
-                for (int e = 0; e < 4; ++e) {
-                    const int r = 16 * rt + 4 * lg + e, s = 16 * ct + lr;
-                    float a = 0.f;
-                    if (s < r) a = s_beta[pm][r] * __expf(s_gam[pm][r] - s_gam[pm][s]) * s_rk[r] * s_rk[s] * gk[i][e];
-                    s_a[r][s] = a;
+                for (int p = 0; p < NHP; ++p) {
+                    float(*s_ap)[CS] = a_of(p);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const int r = 16 * rt + 4 * lg + e, s = 16 * ct + lr;
+                        float a = 0.f;
+                        if (s < r) a = s_beta[p][r] * __expf(s_gam[p][r] - s_gam[p][s]) * s_rk[r] * s_rk[s] * gk[i][e];
+                        s_ap[r][s] = a;
+                    }
                 }
             }
         }
-        __syncthreads();
+        barrier_lds_only();
 
         // ---- phase 5: diagonal 16x16 blocks of T by forward substitution, one lane per
-        //      column: T[r][s] = delta_rs - sum_{m<r} A[r][m] T[m][s]. The other waves
-        //      write Ptil^T meanwhile.
+        //      column: T[r][s] = delta_rs - sum_{m<r} A[r][m] T[m][s]; then (the other waves
+        //      at once) Ptil^T of every V head of the pass as B fragments (rt, kt), hi and lo:
+        //      slot 4 h + e holds Ptil[16 rt + lr][16 (2 kt + h) + 4 lg + e], which is zero
+        //      above the diagonal.
         if (pt < NB * 16) {
             const int b = pt >> 4, s = pt & 15;
             float t[16];
@@ -653,59 +681,86 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 #pragma unroll
             for (int r = 0; r < 16; ++r) s_t[16 * b + r][16 * b + s] = t[r];
         }
-        // Ptil^T B fragment (rt, kt), hi and lo: slot 4 h + e holds
-        // Ptil[16 rt + lr][16 (2 kt + h) + 4 lg + e], which is zero above the diagonal.
-        if (wl >= PW0) {
-            char* pt_base = ws + L.pt + (size_t)vh * G::TRI_BYTES;
 #pragma unroll
-            for (int i = 0; i < NFW; ++i) {
-                const int fi = wl - PW0 + NPW * i;
-                if (fi >= NTRI) continue;
-                int rt, kt;
-                tri_frag(fi, rt, kt);
-                const int r = 16 * rt + lr;
+        for (int i = 0; i < NFW; ++i) {
+            const int fi = prk + 4 * i;
+            if (fi >= NTRI) continue;
+            int rt, kt;
+            tri_frag(fi, rt, kt);
+            const int r = 16 * rt + lr;
+#pragma unroll
+            for (int p = 0; p < NHP; ++p) {
+                const int64_t vhp = (seq * nch + c) * h_v + head_at(g0, p);
+                char* pt_base = ws + L.pt + (size_t)vhp * G::TRI_BYTES;
                 float val[8];
 #pragma unroll
                 for (int h = 0; h < 2; ++h)
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int s = 32 * kt + 16 * h + 4 * lg + e;
-                        float p = 0.f;
-                        if (s <= r) p = __expf(s_gam[pm][r] - s_gam[pm][s]) * s_rq[r] * s_rk[s] * gp[i][h][e];
-                        val[4 * h + e] = p;
+                        float pv = 0.f;
+                        if (s <= r) pv = __expf(s_gam[p][r] - s_gam[p][s]) * s_rq[r] * s_rk[s] * gp[i][h][e];
+                        val[4 * h + e] = pv;
                     }
                 uint32_t hi[4], lo[4];
 #pragma unroll
-                for (int p = 0; p < 4; ++p) split2(val[2 * p], val[2 * p + 1], &hi[p], &lo[p]);
+                for (int q2 = 0; q2 < 4; ++q2) split2(val[2 * q2], val[2 * q2 + 1], &hi[q2], &lo[q2]);
                 *reinterpret_cast<u32x4*>(pt_base + (size_t)(2 * fi) * 1024 + l * 16) = u32x4{hi[0], hi[1], hi[2], hi[3]};
                 *reinterpret_cast<u32x4*>(pt_base + (size_t)(2 * fi + 1) * 1024 + l * 16) = u32x4{lo[0], lo[1], lo[2], lo[3]};
             }
         }
-        __syncthreads();
+        barrier_lds_only();
 
         // ---- phase 6: off-diagonal blocks, block row by block row:
         //      T_ij = -T_ii (sum_{m=j}^{i-1} A_im T_mj)   (fp32 MFMA)
-        for (int i = 1; i < NB; ++i) {
-            for (int j = wl; j < i; j += NWH) {
-                floatx4 x = {0.f, 0.f, 0.f, 0.f};
-                for (int m = j; m < i; ++m) {
-#pragma unroll
-                    for (int kk = 0; kk < 4; ++kk)
-                        x = mfma_f32(s_a[16 * i + lr][16 * m + 4 * kk + lg],
-                                     s_t[16 * m + 4 * kk + lg][16 * j + lr], x);
-                }
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s_x[w][4 * lg + e][lr] = x[e];
-                lds_fence();
-                floatx4 y = {0.f, 0.f, 0.f, 0.f};
+        auto offdiag = [&](int i, int j) {
+            floatx4 x = {0.f, 0.f, 0.f, 0.f};
+            for (int m = j; m < i; ++m) {
 #pragma unroll
                 for (int kk = 0; kk < 4; ++kk)
-                    y = mfma_f32(s_t[16 * i + lr][16 * i + 4 * kk + lg], s_x[w][4 * kk + lg][lr], y);
-#pragma unroll
-                for (int e = 0; e < 4; ++e) s_t[16 * i + 4 * lg + e][16 * j + lr] = -y[e];
-                lds_fence();
+                    x = mfma_f32(s_a[16 * i + lr][16 * m + 4 * kk + lg],
+                                 s_t[16 * m + 4 * kk + lg][16 * j + lr], x);
             }
-            __syncthreads();
+#pragma unroll
+            for (int e = 0; e < 4; ++e) s_x[w][4 * lg + e][lr] = x[e];
+            lds_fence();
+            floatx4 y = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+            for (int kk = 0; kk < 4; ++kk)
+                y = mfma_f32(s_t[16 * i + lr][16 * i + 4 * kk + lg], s_x[w][4 * kk + lg][lr], y);
+            return y;
+        };
+        if constexpr (INPLACE) {
+            // T_ij replaces A_ij, which the other blocks of row i still read: every wave forms
+            // its blocks of the row first, and writes them after a barrier.
+            constexpr int NJ = (NB + NWH - 1) / NWH;
+#pragma unroll 1
+            for (int i = 1; i < NB; ++i) {
+                floatx4 yv[NJ];
+#pragma unroll
+                for (int jj = 0; jj < NJ; ++jj)
+                    if (wl + NWH * jj < i) yv[jj] = offdiag(i, wl + NWH * jj);
+                barrier_lds_only();
+#pragma unroll
+                for (int jj = 0; jj < NJ; ++jj) {
+                    const int j = wl + NWH * jj;
+                    if (j < i) {
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) s_t[16 * i + 4 * lg + e][16 * j + lr] = -yv[jj][e];
+                    }
+                }
+                barrier_lds_only();
+            }
+        } else {
+            for (int i = 1; i < NB; ++i) {
+                for (int j = wl; j < i; j += NWH) {
+                    const floatx4 y = offdiag(i, j);
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) s_t[16 * i + 4 * lg + e][16 * j + lr] = -y[e];
+                    lds_fence();
+                }
+                barrier_lds_only();
+            }
         }
 
         // ---- T' = T diag(beta) as compact hi/lo A-operand tiles with the permuted token
@@ -774,7 +829,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
                 }
             }
         }
-        __syncthreads();  // s_a, s_t and the gate prefix sums are rewritten for the next V head
+        barrier_lds_only();  // s_a, s_t and the gate prefix sums are rewritten for the next V head
     }
 }
 
@@ -883,13 +938,6 @@ __device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, void* lds,
     __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
 }
 
-// A workgroup barrier that waits only for this wave's LDS operations. (__syncthreads()
-// would also wait for every load that writes LDS directly; the staging helpers wait for
-// those explicitly, two windows after issue.)
-__device__ __forceinline__ void barrier_lds_only()
-{
-    asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
-}
 
 // Calls f(std::integral_constant<int, i>) for the wave-uniform index i in [I, N), so that the
 // callee is specialised for each index.
@@ -2069,8 +2117,9 @@ chunk_scan_wide_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, con
 // over the workgroups that read them), so that the staging loads hit L2.
 // Windows are separated by workgroup barriers, one per chunk: window -1 forms the state's
 // first partial products; windows 0 .. nwin - 1 the chunks, where nwin is the chunk count
-// rounded up to even (the extra window, when there is one, has s = 0 and Gamma_C = 1 staged,
-// so that it leaves the state unchanged: M <- 1 * M + K^T 0); a last window the last outputs.
+// rounded up to even (the extra window, when there is one, has a = s = 0 and Gamma_C = 1
+// staged, so that it leaves the state unchanged: M <- 1 * M + K^T 0); a last window the last
+// outputs.
 // Staged data of chunks past the sequence is the last chunk's again (or zero scalars), in
 // slots whose products nobody reads. The rings start cleared, so rows past a short last
 // chunk (never written: their loads fall outside the buffer range) hold finite values, which
@@ -2457,7 +2506,9 @@ chunk64_scan_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
         // window c stages what window c + 1 reads: K rows of chunk c + 2 (into the slot of
         // chunk c, whose reads ended in window c - 1), and the Q rows, T' pieces, V block
         // and scalars of chunk c + 1. Chunks past the sequence: the last chunk's rows and
-        // pieces again, and scalars s = 0, Gamma_C = 1 (an update that changes nothing).
+        // pieces again, and scalars a = s = 0, Gamma_C = 1 (an update that changes nothing;
+        // every scalar the chain reads is written, since 0 times a stale non-finite value
+        // would not be zero).
         auto stage = [&](auto par_c, int64_t c) {
             constexpr int PAR = decltype(par_c)::value;  // c & 1
             constexpr int NXT = PAR ^ 1;                 // (c + 1) & 1
@@ -2482,6 +2533,7 @@ chunk64_scan_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
                 if (j < nch) {
                     load_to_lds(make_rsrc(ws + L.sc + vh_of(j) * G::SC_BYTES, G::SC_BYTES), s_sc[NXT], 16 * l);
                 } else {
+                    s_sc[NXT][l] = 0.f;
                     s_sc[NXT][C + l] = 0.f;
                     if (l == 0) s_sc[NXT][3 * C] = 1.f;
                 }

@@ -34,6 +34,7 @@ constexpr int kChunkPrep = 1, kChunkScan = 2;
 hipError_t launch_chunked(const Call& c, int chunk, int parts = kChunkPrep | kChunkScan);
 hipError_t launch_state_passthrough(const Call& c);  // t == 0: state_out = state_in or 0
 hipError_t launch_mfma_loop(int64_t iters, int32_t blocks, float* sink, hipStream_t stream);
+hipError_t launch_lds_fill(uint32_t pattern, int32_t blocks, uint32_t* sink, hipStream_t stream);
 hipError_t launch_stream_copy(const void* src, void* dst, int64_t n16, int32_t blocks,
                               hipStream_t stream);
 

@@ -323,6 +323,17 @@ gdn_status gdn_calib_mfma_bf16(int64_t iters, int32_t blocks, float* sink, void*
 gdn_status gdn_calib_stream_copy(const void* src, void* dst, int64_t bytes, int32_t blocks,
                                  void* stream);
 
+/*
+ * Diagnostic (testing only): `blocks` workgroups, each holding the whole 160 KB of a CU's
+ * LDS, fill it with the 32-bit `pattern` on `stream`. Launched with a few workgroups per
+ * CU right before a kernel, it leaves that pattern wherever the kernel reads LDS it has not
+ * written (with a NaN pattern, such a read shows up as a non-finite result). `sink` is
+ * device memory of one uint32_t that the kernel writes only if the fill failed; its contents
+ * are otherwise left as they are. GDN_ERR_NULL for a NULL sink, GDN_ERR_SHAPE unless
+ * 0 < blocks <= 2^20, GDN_ERR_ALIGN for a sink not 4-byte aligned.
+ */
+gdn_status gdn_debug_fill_lds(uint32_t pattern, int32_t blocks, uint32_t* sink, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

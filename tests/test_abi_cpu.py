@@ -425,3 +425,13 @@ def test_calib_stream_copy_validation(lib):
     assert f(a, b, 1024, (1 << 20) + 1, None) == SHAPE
     assert f(P(0x7F0000000008), b, 1024, 16, None) == ALIGN
     assert f(a, P(0x7F0000000200), 1024, 16, None) == ALIAS
+
+
+def test_debug_fill_lds_validation(lib):
+    """Argument checks of the LDS fill diagnostic (no launch on any error)."""
+    P = ctypes.c_void_p
+    f = lib.gdn_debug_fill_lds
+    assert f(0x7FC00000, 16, None, None) == NULL
+    assert f(0x7FC00000, 0, P(0x7F0000000000), None) == SHAPE
+    assert f(0x7FC00000, (1 << 20) + 1, P(0x7F0000000000), None) == SHAPE
+    assert f(0x7FC00000, 16, P(0x7F0000000002), None) == ALIGN
