@@ -3,8 +3,9 @@
 
 One step is the whole hot path once:
   * prefill: a 4096-token prompt through 30 GDN layers, one library prefill call per layer
-    (the method gdn_prefill_choose picks: the chunked kernels at this length), each layer
-    on its own synthetic inputs (16 QK heads, 32 V heads, d_k = d_v = 128, bf16 q/k/v,
+    (the method gdn_prefill_choose picks: the chunked kernels with 64-token chunks at this
+    length), each layer on its own synthetic inputs (16 QK heads, 32 V heads,
+    d_k = d_v = 128, bf16 q/k/v,
     fp32 gate and write strength, zero initial state), states written to a 30-layer stack;
   * decode: one token through the same 30 layers (one stacked gdn_decode_step, n = 30),
     continuing from the states the prefill produced, updated in place.
@@ -586,7 +587,9 @@ def main():
         "prefill_workspace_bytes": ws.numel(),
         "roofline": {"bound": "hbm", "achieved": achieved, "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": achieved / HBM_PEAK_GBS, "traffic": traffic,
-                     "kernel": "gdn_prefill_chunked call (chunk_prep_kernel + chunk_scan_kernel)",
+                     "kernel": ("gdn_prefill_chunked call (chunk_prep_kernel + "
+                                + ("chunk64_scan_kernel)" if chunk == 64 else "chunk_scan_kernel)")
+                                if chunk else "gdn_prefill_scan call"),
                      "algorithmic_bytes_per_call": prefill_bytes()},
         "matrix": matrix_fields(chunk, mean_call_s, extra),
     }

@@ -6,8 +6,12 @@ workload shapes": whether the token-by-token scan or the re-blocked (chunked) ev
 faster depends on the dimensions, the workload and the hardware, so the choice is measured
 rather than assumed. The sweep times one prefill call of the 16 QK / 32 V head, d = 128
 layer (bf16 q/k/v, fp32 gate and write strength, zero initial state) at each length, for the
-scan and every chunk size, in interleaved rounds, and keeps the median per method. Inputs are
-synthetic (normal q/k/v, write strength sigmoid(normal), gate log sigmoid(normal + 2)).
+scan and every chunk size, in interleaved rounds, and keeps the median per method. As in a
+layer stack, each call reads its own inputs and writes its own outputs: a round runs the
+calls of several input sets back to back (enough sets that they do not all fit in the
+GPU's caches, for lengths where that is possible) between two events, and a call's time is
+the round's time over the call count. Inputs are synthetic (normal q/k/v, write strength
+sigmoid(normal), gate log sigmoid(normal + 2)).
 
     python -m gated_deltanet_linear_prefill_amd.crossover            # print the sweep
     python -m gated_deltanet_linear_prefill_amd.crossover --write    # and rewrite the table
@@ -41,50 +45,68 @@ def make_inputs(t, seed):
     return q, k, v, g, beta
 
 
-def time_calls(fn, reps):
-    """Per-call times (us) of `reps` calls, each bracketed by its own events."""
-    out = []
-    for _ in range(reps):
-        s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        s.record()
-        fn()
-        e.record()
-        e.synchronize()
-        out.append(s.elapsed_time(e) * 1e3)
-    return out
+# Input sets per length: enough that their inputs and outputs together exceed this many
+# bytes (more than the device's last-level cache), within [MIN_SETS, MAX_SETS].
+ROTATE_BYTES = 1 << 30
+MIN_SETS, MAX_SETS = 2, 32
+
+
+def set_bytes(t):
+    return t * (2 * H_QK * D * 2 + H_V * D * 2 + 2 * H_V * 4 + H_V * D * 4) + H_V * D * D * 4
+
+
+def time_round(fns, repeat):
+    """Time (us) per call of `repeat` passes over the calls `fns`, launched back to back
+    between two events."""
+    s, e = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    s.record()
+    for _ in range(repeat):
+        for fn in fns:
+            fn()
+    e.record()
+    e.synchronize()
+    return s.elapsed_time(e) * 1e3 / (repeat * len(fns))
 
 
 def sweep(lengths, rounds):
     import gated_deltanet_linear_prefill_amd as gdn
     rows = []
     for t in lengths:
-        q, k, v, g, beta = make_inputs(t, seed=5000 + t)
-        out = torch.empty(1, t, H_V, D, device="cuda")
-        st = torch.empty(1, H_V, D, D, device="cuda")
+        nsets = max(MIN_SETS, min(MAX_SETS, -(-ROTATE_BYTES // set_bytes(t))))
+        sets = []
+        for i in range(nsets):
+            q, k, v, g, beta = make_inputs(t, seed=5000 + 97 * i + t)
+            out = torch.empty(1, t, H_V, D, device="cuda")
+            st = torch.empty(1, H_V, D, D, device="cuda")
+            sets.append((q, k, v, g, beta, out, st))
         methods = {}
         ws_scan = torch.empty(max(1, gdn.gdn_workspace_bytes(1, t, H_QK, H_V, D, chunk=0)),
                               device="cuda", dtype=torch.uint8)
-        methods["scan"] = lambda: gdn.gdn_prefill_scan(q, k, v, g, beta, None, out=out, state_out=st,
-                                                       workspace=ws_scan)
+        methods["scan"] = [gdn.bind_prefill_scan(q, k, v, g, beta, None, out, st, ws_scan)
+                           for q, k, v, g, beta, out, st in sets]
         for c in CHUNKS:
             ws = torch.empty(max(1, gdn.gdn_workspace_bytes(1, t, H_QK, H_V, D, chunk=c)),
                              device="cuda", dtype=torch.uint8)
-            methods[f"C{c}"] = (lambda c=c, ws=ws: gdn.gdn_prefill_chunked(
-                q, k, v, g, beta, None, chunk=c, out=out, state_out=st, workspace=ws))
-        for fn in methods.values():  # warm-up
-            fn()
-            fn()
+            methods[f"C{c}"] = [gdn.bind_prefill_chunked(q, k, v, g, beta, None, out, st, ws,
+                                                         chunk=c)
+                                for q, k, v, g, beta, out, st in sets]
+        for fns in methods.values():  # warm-up
+            for fn in fns:
+                fn()
         torch.cuda.synchronize()
+        # about 2 ms of calls per round and method (at least one pass over the sets)
+        probe = time_round(methods["C32"], 1)
+        repeat = max(1, int(2000.0 / (probe * nsets)))
         times = {name: [] for name in methods}
         for _ in range(rounds):  # rounds alternate between the methods
-            for name, fn in methods.items():
-                times[name] += time_calls(fn, 1)
+            for name, fns in methods.items():
+                times[name].append(time_round(fns, repeat))
         med = {name: statistics.median(v) for name, v in times.items()}
         best = min(med, key=med.get)
-        rows.append((t, med, best))
-        print(f"T={t:7d} " + " ".join(f"{n}={med[n]:9.1f}us" for n in methods) + f"  best {best}",
-              flush=True)
-        del q, k, v, g, beta, out, st, methods, ws_scan
+        rows.append((t, med, best, nsets))
+        print(f"T={t:7d} sets={nsets:2d} " + " ".join(f"{n}={med[n]:9.1f}us" for n in methods) +
+              f"  best {best}", flush=True)
+        del sets, methods, ws_scan
         torch.cuda.empty_cache()
     return rows
 
@@ -93,7 +115,7 @@ def table_entries(rows):
     """Breakpoints {min_t, chunk}: each measured length's winner holds from that length up
     to the next measured length where the winner differs."""
     entries = []
-    for t, _, best in rows:
+    for t, _, best, _ in rows:
         chunk = 0 if best == "scan" else int(best[1:])
         if not entries or entries[-1][1] != chunk:
             entries.append((0 if not entries else t, chunk))
@@ -126,14 +148,16 @@ def write_summary(path, rows, entries, device_name, rounds):
         "",
         "    python -m gated_deltanet_linear_prefill_amd.crossover " + " ".join(sys.argv[1:]),
         "",
-        f"Device: {device_name}. Median of {rounds} interleaved rounds, one prefill call per "
-        "measurement (HIP events around the call).",
+        f"Device: {device_name}. Median of {rounds} interleaved rounds; a round times the calls "
+        "of `sets` input sets (each with its own inputs and outputs, one shared workspace per "
+        "method) back to back between two HIP events, and a call's time is the round's time "
+        "over its call count.",
         "",
-        "| T | " + " | ".join(f"{n} us" for n in names) + " | best | best tokens/s |",
-        "|---|" + "---|" * (len(names) + 2),
+        "| T | sets | " + " | ".join(f"{n} us" for n in names) + " | best | best tokens/s |",
+        "|---|---|" + "---|" * (len(names) + 2),
     ]
-    for t, med, best in rows:
-        lines.append(f"| {t} | " + " | ".join(f"{med[n]:.1f}" for n in names) +
+    for t, med, best, nsets in rows:
+        lines.append(f"| {t} | {nsets} | " + " | ".join(f"{med[n]:.1f}" for n in names) +
                      f" | {best} | {t / (med[best] * 1e-6):.3e} |")
     lines += ["", "Dispatch table (csrc/gdn_crossover.inc; min_t -> chunk, 0 = scan): " +
               ", ".join(f"{t}->{c}" for t, c in entries), ""]
