@@ -41,3 +41,29 @@ def assert_parity(out, st, out_ref, st_ref, what="", out_tol=OUT_TOL, state_tol=
         assert np.all(np.isfinite(to64(out))), "non-finite output: " + msg
     assert eo <= out_tol and es <= state_tol, msg
     return eo, es
+
+
+# ---------------------------------------------------------------- error report
+# Full-size cases record their worst errors here; with GDN_PARITY_REPORT=<path> set, the
+# test session writes them as a markdown table at its end (tests/conftest.py).
+REPORT = []
+
+
+def record(config, method, compared, out_errs, state_errs, out_tol=OUT_TOL, state_tol=STATE_TOL):
+    """Keep the worst output and state errors of one (workload, method) comparison.
+    `compared` says what was compared (heads, steps, segments)."""
+    eo = float(np.max(out_errs)) if len(out_errs) else 0.0
+    es = float(np.max(state_errs)) if len(state_errs) else 0.0
+    REPORT.append(dict(config=config, method=method, compared=compared, out=eo, state=es,
+                       out_tol=out_tol, state_tol=state_tol))
+
+
+def write_report(path, header=""):
+    lines = ["# Parity at full size: GPU library against the fp64 oracle", "", header, "",
+             "| workload | method | compared | worst out max\\|err\\|/RMS | worst state rel-F | "
+             "tolerance (out / state) |", "|---|---|---|---|---|---|"]
+    for r in REPORT:
+        lines.append(f"| {r['config']} | {r['method']} | {r['compared']} | {r['out']:.3e} | "
+                     f"{r['state']:.3e} | {r['out_tol']:g} / {r['state_tol']:g} |")
+    with open(path, "w") as f:
+        f.write("\n".join(lines) + "\n")

@@ -1,8 +1,6 @@
-"""GPU parity: gdn_prefill_chunked (and the scan/chunk sweep grid) against the fp64 oracle.
-
-Large cases compare a sample of V heads: the oracle runs a problem built from the sampled
-heads' slices with one QK head per V head, which is the same computation bitwise (pinned by
-the oracle's head-mapping test).
+"""GPU parity: gdn_prefill_chunked against the fp64 oracle on small and ragged shapes, every
+chunk size, head dimension and input dtype (the workloads' full sizes are in
+test_gpu_fullsize.py).
 """
 import pytest
 import torch
@@ -11,11 +9,10 @@ import gated_deltanet_linear_prefill_amd as gdn
 import gdn_inputs
 import oracle
 from gdn_inputs import Shape
-from parity import assert_parity, out_error, state_error
+from parity import assert_parity, out_error
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
-FULL = dict(h_qk=16, h_v=32, d=128)
 
 
 def cpu(c):
@@ -25,24 +22,6 @@ def cpu(c):
 def run_oracle(c, eps=1e-6):
     h = cpu(c)
     return oracle.run(h["q"], h["k"], h["v"], h["g"], h["beta"], h["state_in"], l2_eps=eps)
-
-
-def head_slice(c, heads, grp):
-    """Inputs of the given V heads alone, as a problem with one QK head per V head (V head
-    i of the slice reads QK head i), on the CPU."""
-    hs = list(heads)
-    qk = [h // grp for h in hs]
-    s = {"q": c["q"][:, :, qk], "k": c["k"][:, :, qk], "v": c["v"][:, :, hs],
-         "g": c["g"][:, :, hs], "beta": c["beta"][:, :, hs],
-         "state_in": None if c["state_in"] is None else c["state_in"][:, hs]}
-    return {key: (None if val is None else val.contiguous().cpu()) for key, val in s.items()}
-
-
-def oracle_heads(c, heads, grp):
-    """{head: (out [n, t, 1, d], state [n, 1, d, d])} from one oracle run over the sample."""
-    s = head_slice(c, heads, grp)
-    o, st = oracle.run(s["q"], s["k"], s["v"], s["g"], s["beta"], s["state_in"])
-    return {h: (o[:, :, i:i + 1], st[:, i:i + 1]) for i, h in enumerate(heads)}
 
 
 # ------------------------------------------------------------------------ small cases
@@ -126,90 +105,3 @@ def test_chunked_retrieval_and_column_independence(chunk):
     out, st = gdn.gdn_prefill_chunked(**c, chunk=chunk)
     torch.cuda.synchronize()
     assert torch.count_nonzero(out[..., 77]) == 0 and torch.count_nonzero(st[..., 77]) == 0
-
-
-# ------------------------------------------------------------------------ full sizes
-def bench_chunk(shape):
-    """The method gdn_prefill picks for a shape (what the benchmark times); chunked here."""
-    chunk = gdn.gdn_prefill_choose(shape.t, shape.h_qk, shape.h_v, shape.d, shape.n, shape.dtype)
-    assert chunk > 0, chunk
-    return chunk
-
-
-@pytest.mark.parametrize("which", ["dispatch", "C=64"])
-def test_chunked_prefill_4k(which):
-    """The 4096-token prefill workload (16 QK / 32 V heads, d=128, bf16, S0=0) in the launch
-    configuration the benchmark times (the chunk gdn_prefill picks, 32 on MI355X) and at
-    chunk 64: every output and the final state of a sample of V heads against the oracle;
-    all heads against the direct scan."""
-    c = gdn_inputs.make_case(gdn_inputs.PREFILL_4K, seed=2, device=DEV)
-    chunk = bench_chunk(gdn_inputs.PREFILL_4K) if which == "dispatch" else 64
-    out, st = gdn.gdn_prefill_chunked(**c, chunk=chunk)
-    out_s, st_s = gdn.gdn_prefill_scan(**c)
-    torch.cuda.synchronize()
-    heads = [0, 5, 18, 31]
-    ref = oracle_heads(c, heads, 2)
-    for h in heads:
-        assert_parity(out[:, :, h], st[:, h], ref[h][0][:, :, 0], ref[h][1][:, 0], f"4k head {h}")
-    # every head: chunked and scan agree to the same bar
-    assert_parity(out, st, out_s, st_s, "4k chunked vs scan, all heads")
-
-
-def test_chunked_long_131072_segments():
-    """The long-prefill workload: T = 131072 as 32 segments of 4096 with the state carried
-    between calls, with the chunk gdn_prefill picks for a segment. Per-segment outputs and
-    the final state of sampled V heads against one single-pass oracle run."""
-    seg_t, nseg = gdn_inputs.LONG_SEGMENT.t, gdn_inputs.LONG_SEGMENTS
-    heads = [3, 28]
-    st = torch.zeros(1, 32, 128, 128, device=DEV)
-    host = {key: [] for key in ("q", "k", "v", "g", "beta")}
-    outs = []
-    chunk = bench_chunk(gdn_inputs.LONG_SEGMENT)
-    ws = torch.empty(gdn.gdn_workspace_bytes(1, seg_t, 16, 32, 128, chunk=chunk), device=DEV,
-                     dtype=torch.uint8)
-    out = torch.empty(1, seg_t, 32, 128, device=DEV)
-    for s in range(nseg):
-        c = gdn_inputs.make_case(gdn_inputs.LONG_SEGMENT, seed=4000 + s, device=DEV)
-        gdn.gdn_prefill_chunked(c["q"], c["k"], c["v"], c["g"], c["beta"], st, out=out,
-                                state_out=st, workspace=ws, chunk=chunk)
-        sl = head_slice(c, heads, 2)
-        for key in host:
-            host[key].append(sl[key])
-        outs.append(out[:, :, heads].cpu())
-    torch.cuda.synchronize()
-    assert torch.isfinite(st).all()
-    full = {key: torch.cat(val, dim=1) for key, val in host.items()}
-    o_ref, s_ref = oracle.run(full["q"], full["k"], full["v"], full["g"], full["beta"])
-    for i, h in enumerate(heads):
-        worst = 0.0
-        for s in range(nseg):
-            sl = slice(s * seg_t, (s + 1) * seg_t)
-            worst = max(worst, out_error(outs[s][:, :, i], o_ref[:, sl, i]))
-        es = state_error(st[:, h], s_ref[:, i])
-        print(f"long head {h}: worst segment out err {worst:.3e}, final state {es:.3e}")
-        assert worst <= 2e-3 and es <= 1e-3, (h, worst, es)
-
-
-@pytest.mark.parametrize("t", gdn_inputs.SWEEP_T)
-def test_sweep_grid_parity(t):
-    """The scan-versus-chunk sweep grid at one length: chunk 16, 32, 64 and 128, the direct
-    scan and the dispatching gdn_prefill against one oracle run of sampled heads; then the
-    retrieval inputs (g = 0, beta = 1) at the same length, where the same bar applies."""
-    shape = Shape(n=1, t=t, **FULL)
-    for retrieval in (False, True):
-        c = gdn_inputs.make_case(shape, seed=5000 + t, device=DEV, retrieval=retrieval)
-        heads = [7, 24]
-        ref = oracle_heads(c, heads, 2)
-        chunks = sorted({16, *gdn_inputs.SWEEP_CHUNKS})
-        runs = {f"C={cs}": gdn.gdn_prefill_chunked(**c, chunk=cs) for cs in chunks}
-        runs["scan"] = gdn.gdn_prefill_scan(**c)
-        runs["dispatch"] = gdn.gdn_prefill(**c)
-        torch.cuda.synchronize()
-        for name, (out, st) in runs.items():
-            assert torch.isfinite(out).all() and torch.isfinite(st).all(), name
-            for h in heads:
-                assert_parity(out[:, :, h], st[:, h], ref[h][0][:, :, 0], ref[h][1][:, 0],
-                              f"sweep t={t} {name} head {h} retrieval={retrieval}")
-            del out, st
-        del runs, c
-        torch.cuda.empty_cache()

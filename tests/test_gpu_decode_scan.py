@@ -4,7 +4,6 @@ Every case draws seeded synthetic inputs on the GPU (gdn_inputs), runs the HIP l
 through its C ABI, copies inputs and results to the host and compares them with the
 oracle at the tolerances in parity.py.
 """
-import numpy as np
 import pytest
 import torch
 
@@ -12,7 +11,7 @@ import gated_deltanet_linear_prefill_amd as gdn
 import gdn_inputs
 import oracle
 from gdn_inputs import Shape
-from parity import assert_parity, to64
+from parity import assert_parity
 
 pytestmark = pytest.mark.gpu
 DEV = "cuda"
@@ -26,13 +25,6 @@ def run_oracle(c, eps=1e-6, heads=None):
     h = cpu(c)
     return oracle.run(h["q"], h["k"], h["v"], h["g"], h["beta"], h["state_in"], l2_eps=eps,
                       heads=heads)
-
-
-def heads_of(out, st, heads, h_v):
-    """Select flattened (seq * h_v + head) heads from [n, t, h_v, d] and [n, h_v, d, d]."""
-    o = np.stack([to64(out)[hid // h_v, :, hid % h_v] for hid in heads])
-    s = np.stack([to64(st)[hid // h_v, hid % h_v] for hid in heads])
-    return o, s
 
 
 # ----------------------------------------------------------------------------- decode
@@ -78,45 +70,6 @@ def test_decode_tiny_as_64_steps():
     assert_parity(torch.cat(outs, dim=1), st, o_ref, s_ref, "decode tiny x64")
 
 
-def test_decode_30_layers_4096_steps():
-    """The stacked decode workload: 30 layers x 32 V heads x 128x128 fp32 state,
-    S0 ~ N(0, 0.02^2), 4096 consecutive steps with the state carried in place. The oracle
-    follows a sample of (layer, head) pairs; outputs of every step and the state every
-    512 steps are compared for them."""
-    L, steps, snap = 30, 4096, 512
-    per_step = Shape(n=L * steps, t=1, h_qk=16, h_v=32, d=128)
-    c = gdn_inputs.make_case(per_step, seed=3, device=DEV)
-    x = {key: c[key].view(steps, L, *c[key].shape[1:]) for key in ("q", "k", "v", "g", "beta")}
-    s0 = gdn_inputs.make_case(Shape(n=L, t=1, h_qk=16, h_v=32, d=128), seed=33, device=DEV,
-                              s0_std=0.02)["state_in"]
-    st = s0.clone()
-    outs = torch.empty(steps, L, 1, 32, 128, device=DEV)
-    snaps = []
-    for s in range(steps):
-        gdn.gdn_decode_step(x["q"][s], x["k"][s], x["v"][s], x["g"][s], x["beta"][s], st,
-                            out=outs[s], state_out=st)
-        if (s + 1) % snap == 0:
-            snaps.append(st.clone())
-    torch.cuda.synchronize()
-    assert torch.isfinite(outs).all() and torch.isfinite(st).all()
-    sample = [(0, 0), (7, 13), (15, 31), (29, 30)]  # (layer, V head)
-    for layer in sorted({l for l, _ in sample}):
-        hs = [h for l, h in sample if l == layer]
-        seq = {key: x[key][:, layer].reshape(1, steps, *x[key].shape[3:]).cpu()
-               for key in ("q", "k", "v", "g", "beta")}
-        state = s0[layer:layer + 1].cpu()
-        for seg in range(steps // snap):
-            sl = slice(seg * snap, (seg + 1) * snap)
-            o_ref, s_ref = oracle.run(seq["q"][:, sl], seq["k"][:, sl], seq["v"][:, sl],
-                                      seq["g"][:, sl], seq["beta"][:, sl], state, heads=hs)
-            for h in hs:
-                got_o = outs[sl, layer, 0, h].cpu()
-                got_s = snaps[seg][layer, h].cpu()
-                assert_parity(got_o, got_s, o_ref[0, :, h], s_ref[0, h],
-                              f"decode layer {layer} head {h} steps {sl}")
-            state = torch.from_numpy(s_ref)
-
-
 # ----------------------------------------------------------------------------- scan
 def test_scan_tiny():
     c = gdn_inputs.make_case(gdn_inputs.TINY, seed=1, device=DEV)
@@ -136,19 +89,6 @@ def test_scan_shapes(d, dtype, t):
     torch.cuda.synchronize()
     o_ref, s_ref = run_oracle(c)
     assert_parity(out, st, o_ref, s_ref, f"scan d={d} t={t} {dtype}")
-
-
-def test_scan_prefill_4k_sampled_heads():
-    """The 4096-token prefill workload (16 QK / 32 V heads, d=128, bf16, S0=0), every
-    output of a sample of V heads against the oracle."""
-    c = gdn_inputs.make_case(gdn_inputs.PREFILL_4K, seed=2, device=DEV)
-    out, st = gdn.gdn_prefill_scan(**c)
-    torch.cuda.synchronize()
-    heads = [0, 1, 17, 31]
-    o_ref, s_ref = run_oracle(c, heads=heads)
-    got = heads_of(out, st, heads, 32)
-    ref = heads_of(o_ref, s_ref, heads, 32)
-    assert_parity(got[0], got[1], ref[0], ref[1], "scan 4k")
 
 
 def test_scan_in_place_empty_and_deterministic():
