@@ -207,22 +207,6 @@ __device__ __forceinline__ void to_pieces(const floatx8& raw, bf16x8* piece)
     piece[1] = __builtin_bit_cast(bf16x8, u32x4{lo[0], lo[1], lo[2], lo[3]});
 }
 
-// Buffer resources: a base address and byte range in scalar registers, re-based once per
-// chunk with scalar adds, while each lane keeps fixed byte offsets. Lanes whose offset
-// falls outside the range read zero (and their stores are dropped), which handles the rows
-// past the end of a sequence and padded features without per-lane branches. The 0x00020000
-// word is the raw (untyped, unswizzled) descriptor format of the gfx9 family.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes)
-{
-    const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
-    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
-}
-
-// A byte offset beyond every buffer range used here (ranges stay below 2^30; the host
-// checks the chunk's q/k/v/out extents against that bound). Added to an in-range offset
-// (below 2^30) it stays below 2^32, so the hardware's unsigned offset does not wrap.
-constexpr uint32_t OOR = 0x60000000u;
-
 __device__ __forceinline__ bf16x8 buf_bf16x8(__amdgpu_buffer_rsrc_t r, int off)
 {
     return __builtin_bit_cast(bf16x8, __builtin_amdgcn_raw_buffer_load_b128(r, off, 0, 0));
@@ -417,6 +401,34 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     };
     if (wl == 0) load_gb(head_of(0));
 
+    // Gate prefix sums gamma and write strengths of the pass starting at V head g0 into
+    // LDS (the first wave of each head slot); the next pass's gates are loaded meanwhile.
+    auto gate_prefix = [&](int g0) {
+        if (wl != 0) return;
+        float run = 0.f, gs[E];
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            run += gv[e];
+            gs[e] = run;
+        }
+        float x = run;
+#pragma unroll
+        for (int off = 1; off < 64; off <<= 1) {
+            const float y = __shfl_up(x, off, 64);
+            if (l >= off) x += y;
+        }
+        const float excl = x - run;
+#pragma unroll
+        for (int e = 0; e < E; ++e) {
+            const int i = l * E + e;
+            if (i < CP) {
+                s_gam[pm][i] = gs[e] + excl;
+                s_beta[pm][i] = bv[e];
+            }
+        }
+        if (g0 + NHP < grp) load_gb(head_of(g0 + NHP));
+    };
+
     // The next chunk's key rows for H (see below), loaded now so that they arrive while the
     // chunk's own rows are loaded and normalised.
     constexpr int NIT = G::WITH_H ? (RT + NWH - 1) / NWH : 0;
@@ -440,7 +452,8 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 
     // ---- phase 0: inverse norms of the q and k rows; both chunks into LDS as bf16 pieces
     //      (rows past the chunk and padded features are zero). The loads of a batch of
-    //      rows are all issued before any of them is used.
+    //      rows are all issued before any of them is used. The first pass's gate prefix
+    //      sums are formed here too, while the rows arrive.
     {
         constexpr int EPL = D / 16;  // elements per lane, 16 lanes per row
         constexpr int NPASS = CP / 16;
@@ -495,6 +508,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             }
         }
     }
+    gate_prefix(0);
     barrier_lds_only();
 
     // ---- phase 2: Gram matrices from the raw inputs, kept in registers for every V head
@@ -595,33 +609,11 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         const int hv = head_of(g0);
         const int64_t vh = (seq * nch + c) * h_v + hv;
 
-        // ---- phase 3: gate prefix sums gamma (first wave of the slot), write strengths; the
-        //      next pass's gate and write strength are loaded meanwhile
-        if (wl == 0) {
-            float run = 0.f, gs[E];
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                run += gv[e];
-                gs[e] = run;
-            }
-            float x = run;
-#pragma unroll
-            for (int off = 1; off < 64; off <<= 1) {
-                const float y = __shfl_up(x, off, 64);
-                if (l >= off) x += y;
-            }
-            const float excl = x - run;
-#pragma unroll
-            for (int e = 0; e < E; ++e) {
-                const int i = l * E + e;
-                if (i < CP) {
-                    s_gam[pm][i] = gs[e] + excl;
-                    s_beta[pm][i] = bv[e];
-                }
-            }
-            if (g0 + NHP < grp) load_gb(head_of(g0 + NHP));
+        // ---- phase 3 (passes after the first; the first pass's ran in phase 0)
+        if (g0 > 0) {
+            gate_prefix(g0);
+            barrier_lds_only();
         }
-        barrier_lds_only();
 
         // ---- per-token scalars a = Gamma r_k, s = r_k exp(gamma_C - gamma), o = Gamma r_q
         //      and Gamma_C (padded tokens carry r_k = r_q = 0, so their scalars are zero)
@@ -933,10 +925,6 @@ __device__ __forceinline__ bf16x4 lds_read_tr16(const void* p)
 
 // A 16-byte-per-lane buffer load that writes LDS directly: lane l's bytes land at
 // lds + 16 l (established with an in-bounds probe of the instruction).
-__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, int off)
-{
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
-}
 
 
 // Calls f(std::integral_constant<int, i>) for the wave-uniform index i in [I, N), so that the

@@ -104,6 +104,35 @@ __device__ __forceinline__ float row16_sum(float x)
     return x;
 }
 
+// Buffer resources: a base address and byte range in scalar registers, re-based once per
+// chunk with scalar adds, while each lane keeps fixed byte offsets. Lanes whose offset
+// falls outside the range read zero (and their stores are dropped), which handles the rows
+// past the end of a sequence and padded features without per-lane branches. The 0x00020000
+// word is the raw (untyped, unswizzled) descriptor format of the gfx9 family.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, int64_t bytes)
+{
+    const int32_t n = bytes <= 0 ? 0 : (bytes >= 0x7fffffff ? 0x7fffffff : (int32_t)bytes);
+    return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, n, 0x00020000);
+}
+
+// A byte offset beyond every buffer range used here (ranges stay below 2^30; the host
+// checks the chunk's q/k/v/out extents against that bound). Added to an in-range offset
+// (below 2^30) it stays below 2^32, so the hardware's unsigned offset does not wrap.
+constexpr uint32_t OOR = 0x60000000u;
+
+// Loads that write LDS directly: each lane's 16 (load_to_lds) or 4 (load_to_lds4) bytes at
+// byte offset `off` of the buffer land in LDS at `lds` + 16 (or 4) * lane; `lds` is the same
+// for the whole wave. Lanes whose offset is out of range write zeros.
+__device__ __forceinline__ void load_to_lds(__amdgpu_buffer_rsrc_t r, void* lds, int off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 16, off, 0, 0, 0);
+}
+
+__device__ __forceinline__ void load_to_lds4(__amdgpu_buffer_rsrc_t r, void* lds, int off)
+{
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)lds, 4, off, 0, 0, 0);
+}
+
 template <int N, typename TIn>
 __device__ __forceinline__ void load_n(const TIn* p, float* x)
 {
