@@ -116,8 +116,8 @@ const char* gdn_status_str(int32_t status);
 
 /*
  * Workspace bytes a call needs: chunk in {16,32,64,128} for gdn_prefill_chunked, chunk 0
- * for gdn_prefill_scan. Returns 0 for invalid or unsupported dims (and for t == 0).
- * gdn_decode_step needs no workspace.
+ * for gdn_prefill_scan (always 0: the direct scan needs none). Returns 0 for invalid or
+ * unsupported dims (and for t == 0). gdn_decode_step needs no workspace.
  */
 size_t gdn_workspace_bytes(const gdn_dims* dims, int32_t chunk);
 
@@ -138,8 +138,9 @@ gdn_status gdn_prefill_chunked(const gdn_dims* dims, int32_t chunk, const void* 
 
 /*
  * Direct-scan prefill: tokens in order, the state held in registers for the whole call
- * and written back once ("Keep the recurrent state on-chip"). Needs
- * gdn_workspace_bytes(dims, 0) bytes of workspace.
+ * and written back once ("Keep the recurrent state on-chip"). The inputs are staged and
+ * normalised on chip, so it needs no workspace (gdn_workspace_bytes(dims, 0) is 0; the
+ * workspace arguments are ignored).
  */
 gdn_status gdn_prefill_scan(const gdn_dims* dims, const void* q, const void* k,
                             const void* v, const float* g, const float* beta,

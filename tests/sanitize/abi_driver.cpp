@@ -94,7 +94,6 @@ int main()
 
     // scan, blockwise scan, choice, decode
     expect("scan null state_out", gdn_prefill_scan(&b.d, vq, vk, vv, g, be, si, out, nullptr, ws, WS, nullptr), GDN_ERR_NULL);
-    expect("scan short workspace", gdn_prefill_scan(&b.d, vq, vk, vv, g, be, si, out, so, ws, 8, nullptr), GDN_ERR_WORKSPACE);
     expect("blockwise block 0", gdn_prefill_scan_blockwise(&b.d, 0, vq, vk, vv, g, be, si, out, so, ws, WS, nullptr), GDN_ERR_SHAPE);
     expect("blockwise alias", gdn_prefill_scan_blockwise(&b.d, 8, vq, vk, vv, g, be, si, P<float>(b.v), so, ws, WS, nullptr), GDN_ERR_ALIAS);
     expect("prefill null", gdn_prefill(&b.d, vq, vk, vv, g, be, si, out, so, nullptr, 0, nullptr), GDN_ERR_WORKSPACE);
@@ -107,11 +106,11 @@ int main()
     expect("decode t 2", gdn_decode_step(&two, P<void>(one.q), P<void>(one.k), P<void>(one.v), P<float>(one.g), P<float>(one.beta), P<float>(one.si), P<float>(one.out), P<float>(one.so), nullptr), GDN_ERR_SHAPE);
     expect("decode alias", gdn_decode_step(&one.d, P<void>(one.q), P<void>(one.k), P<void>(one.v), P<float>(one.g), P<float>(one.beta), P<float>(one.si), P<float>(one.si + 64), P<float>(one.so), nullptr), GDN_ERR_ALIAS);
 
-    // segmented
+    // segmented (64-token segments: the chunked path, which needs a workspace)
     expect("segmented seg 0", gdn_prefill_segmented(&b.d, 0, 0, vq, vk, vv, g, be, si, out, so, ws, WS, nullptr), GDN_ERR_SHAPE);
-    expect("segmented overlapped 2", gdn_prefill_segmented(&b.d, 16, 2, vq, vk, vv, g, be, si, out, so, ws, WS, nullptr), GDN_ERR_SHAPE);
-    expect("segmented short workspace", gdn_prefill_segmented(&b.d, 16, 1, vq, vk, vv, g, be, si, out, so, ws, 16, nullptr), GDN_ERR_WORKSPACE);
-    expect("segmented misaligned workspace", gdn_prefill_segmented(&b.d, 16, 1, vq, vk, vv, g, be, si, out, so, P<void>(b.ws + 8), WS, nullptr), GDN_ERR_ALIGN);
+    expect("segmented overlapped 2", gdn_prefill_segmented(&b.d, 64, 2, vq, vk, vv, g, be, si, out, so, ws, WS, nullptr), GDN_ERR_SHAPE);
+    expect("segmented short workspace", gdn_prefill_segmented(&b.d, 64, 1, vq, vk, vv, g, be, si, out, so, ws, 16, nullptr), GDN_ERR_WORKSPACE);
+    expect("segmented misaligned workspace", gdn_prefill_segmented(&b.d, 64, 1, vq, vk, vv, g, be, si, out, so, P<void>(b.ws + 8), WS, nullptr), GDN_ERR_ALIGN);
 
     // decode graph (checked before any recording)
     const void* qs[1] = {P<void>(one.q)};

@@ -172,13 +172,19 @@ def test_misaligned_workspace(lib):
     assert call_scan(lib, b, ws=b.p("ws", 4)) == ALIGN
 
 
-@pytest.mark.parametrize("call", CALLS, ids=["chunked", "scan"])
-def test_workspace_checks(lib, call):
+def test_workspace_checks(lib):
     b = Bufs()
-    need = lib.gdn_workspace_bytes(ctypes.byref(b.dims), 64 if call is call_chunked else 0)
+    need = lib.gdn_workspace_bytes(ctypes.byref(b.dims), 64)
     assert need > 0
-    assert call(lib, b, ws=None) == WS
-    assert call(lib, b, ws_bytes=need - 1) == WS
+    assert call_chunked(lib, b, ws=None) == WS
+    assert call_chunked(lib, b, ws_bytes=need - 1) == WS
+
+
+def test_scan_needs_no_workspace(lib):
+    """The direct scan stages and normalises its inputs in LDS: no workspace at any size."""
+    for t in (1, 2, 100, 4096, 131072):
+        dims = gdn.make_dims(2, t, 16, 32, 128)
+        assert lib.gdn_workspace_bytes(ctypes.byref(dims), 0) == 0
 
 
 @pytest.mark.parametrize("call", CALLS + [call_decode], ids=["chunked", "scan", "decode"])
@@ -195,9 +201,11 @@ def test_aliasing(lib, call):
 
 
 def test_workspace_alias(lib):
+    """A workspace that overlaps any buffer of the call (the direct scan takes none, so
+    its workspace arguments are not checked)."""
     b = Bufs()
     assert call_chunked(lib, b, ws=b.p("out")) == ALIAS
-    assert call_scan(lib, b, ws=b.p("state_in")) == ALIAS
+    assert call_chunked(lib, b, ws=b.p("state_in")) == ALIAS
     assert call_chunked(lib, b, ws=b.p("k")) == ALIAS
 
 
@@ -297,22 +305,24 @@ def call_segmented(lib, b, seg_t=16, dims=None, ws_bytes=64 * MB, overlapped=0, 
 
 def test_segmented_validation(lib):
     """The whole call is validated before any segment is issued (no HIP call here)."""
-    b = Bufs(t=64)
+    b = Bufs(t=256)
+    seg = 64  # segments dispatched to the chunked path, which needs a workspace
+    assert gdn.gdn_prefill_choose(seg, b.dims.h_qk, b.dims.h_v, b.dims.d_k, 1) > 0
     assert lib.gdn_prefill_segmented(None, 16, 0, *[None] * 9, 0, None) == NULL
     assert call_segmented(lib, b, seg_t=0) == SHAPE
     assert call_segmented(lib, b, seg_t=-5) == SHAPE
-    assert call_segmented(lib, b, overlapped=2) == SHAPE
-    assert call_segmented(lib, b, overlapped=-1) == SHAPE
-    need = lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(b.dims), 16, 1)
-    assert call_segmented(lib, b, overlapped=1, ws_bytes=need - 1) == WS
-    assert call_segmented(lib, b, overlapped=1, ws=b.p("ws", 8)) == ALIGN
-    assert call_segmented(lib, b, q=None) == NULL
-    assert call_segmented(lib, b, out=b.p("out", 4)) == ALIGN
-    assert call_segmented(lib, b, out=b.p("q")) == ALIAS
-    assert call_segmented(lib, b, ws=None) == WS
-    assert call_segmented(lib, b, ws_bytes=16) == WS
-    assert call_segmented(lib, b, ws=b.p("state_out")) == ALIAS
-    assert call_segmented(lib, b, dims=with_dims(b, d_k=40, d_v=40)) == UNSUP
+    assert call_segmented(lib, b, seg_t=seg, overlapped=2) == SHAPE
+    assert call_segmented(lib, b, seg_t=seg, overlapped=-1) == SHAPE
+    need = lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(b.dims), seg, 1)
+    assert call_segmented(lib, b, seg_t=seg, overlapped=1, ws_bytes=need - 1) == WS
+    assert call_segmented(lib, b, seg_t=seg, overlapped=1, ws=b.p("ws", 8)) == ALIGN
+    assert call_segmented(lib, b, seg_t=seg, q=None) == NULL
+    assert call_segmented(lib, b, seg_t=seg, out=b.p("out", 4)) == ALIGN
+    assert call_segmented(lib, b, seg_t=seg, out=b.p("q")) == ALIAS
+    assert call_segmented(lib, b, seg_t=seg, ws=None) == WS
+    assert call_segmented(lib, b, seg_t=seg, ws_bytes=16) == WS
+    assert call_segmented(lib, b, seg_t=seg, ws=b.p("state_out")) == ALIAS
+    assert call_segmented(lib, b, seg_t=seg, dims=with_dims(b, d_k=40, d_v=40)) == UNSUP
 
 
 def test_segmented_workspace_bytes(lib):
@@ -348,8 +358,6 @@ def test_scan_blockwise_validation(lib):
     assert call(block_t=0) == SHAPE
     assert call(block_t=-1) == SHAPE
     assert call(q=None) == NULL
-    assert call(ws=None) == WS
-    assert call(ws_bytes=16) == WS
     assert call(out=b.p("q")) == ALIAS
     assert call(out=b.p("out", 4)) == ALIGN
 
@@ -369,12 +377,17 @@ def test_calib_validation(lib):
 
 
 def test_single_token_prefill_needs_no_workspace(lib):
-    """gdn_prefill runs one token as the decode step, which needs no workspace; the
-    segmented workspace for one-token segments is therefore 0 as well."""
+    """gdn_prefill runs one token as the decode step and short prompts as the direct scan,
+    which need no workspace; the segmented workspace for one-token segments is therefore 0
+    as well. Lengths dispatched to the chunked path need one."""
     one = gdn.make_dims(2, 1, 16, 32, 128)
     assert lib.gdn_prefill_workspace_bytes(ctypes.byref(one)) == 0
     two = gdn.make_dims(2, 2, 16, 32, 128)
-    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(two)) > 0
+    assert gdn.gdn_prefill_choose(2, 16, 32, 128, 2) == 0
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(two)) == 0
+    long = gdn.make_dims(2, 4096, 16, 32, 128)
+    assert gdn.gdn_prefill_choose(4096, 16, 32, 128, 2) > 0
+    assert lib.gdn_prefill_workspace_bytes(ctypes.byref(long)) > 0
     seq = gdn.make_dims(1, 100, 16, 32, 128)
     assert lib.gdn_prefill_segmented_workspace_bytes(ctypes.byref(seq), 1, 0) == 0
 
