@@ -646,9 +646,10 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int r = 16 * rt + 4 * lg + e, s = 16 * ct + lr;
-                        float a = 0.f;
-                        if (s < r) a = s_beta[p][r] * __expf(s_gam[p][r] - s_gam[p][s]) * s_rk[r] * s_rk[s] * gk[i][e];
-                        s_ap[r][s] = a;
+                        // formed for every element and selected (above the diagonal the
+                        // decay may overflow; the select drops it)
+                        const float a = s_beta[p][r] * __expf(s_gam[p][r] - s_gam[p][s]) * s_rk[r] * s_rk[s] * gk[i][e];
+                        s_ap[r][s] = s < r ? a : 0.f;
                     }
                 }
             }
@@ -690,9 +691,8 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 #pragma unroll
                     for (int e = 0; e < 4; ++e) {
                         const int s = 32 * kt + 16 * h + 4 * lg + e;
-                        float pv = 0.f;
-                        if (s <= r) pv = __expf(s_gam[p][r] - s_gam[p][s]) * s_rq[r] * s_rk[s] * gp[i][h][e];
-                        val[4 * h + e] = pv;
+                        const float pv = __expf(s_gam[p][r] - s_gam[p][s]) * s_rq[r] * s_rk[s] * gp[i][h][e];
+                        val[4 * h + e] = s <= r ? pv : 0.f;
                     }
                 uint32_t hi[4], lo[4];
 #pragma unroll
@@ -767,7 +767,8 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 #pragma unroll
                 for (int j = 0; j < 8; ++j) {
                     const int s = tok_of(kt, lg, j);
-                    val[j] = s <= r ? s_t[r][s] * s_beta[pm][s] : 0.f;
+                    const float tv = s_t[r][s] * s_beta[pm][s];  // above the diagonal: dropped
+                    val[j] = s <= r ? tv : 0.f;
                 }
                 uint32_t hi[4], lo[4];
 #pragma unroll
