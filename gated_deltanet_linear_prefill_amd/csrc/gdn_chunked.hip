@@ -459,8 +459,50 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         constexpr int NPASS = CP / 16;
         constexpr int BATCH = NPASS < 4 ? NPASS : 4;
         const int sub = tid & 15;
+        // bf16 rows of 128 features: each thread's 8 features are one 16-byte load, copied to
+        // LDS as loaded (a bf16 input is its own hi piece); the norms square the widened
+        // values in the same order as the general path below.
+        constexpr bool RAW16 = std::is_same<TIn, uint16_t>::value && NS == 1 && D == DP && EPL == 8;
+        if constexpr (RAW16) {
 #pragma unroll
-        for (int p0 = 0; p0 < NPASS; p0 += BATCH) {
+            for (int p0 = 0; p0 < NPASS; p0 += BATCH) {
+                u32x4 qr[BATCH], kr[BATCH];
+#pragma unroll
+                for (int b = 0; b < BATCH; ++b) {
+                    const int r = 16 * (p0 + b) + (tid >> 4);
+                    const bool ok = r < Cr;
+                    const int64_t off = ((tok0 + (ok ? r : 0)) * h_qk + hq) * (int64_t)D + sub * EPL;
+                    qr[b] = *reinterpret_cast<const u32x4*>(q + off);
+                    kr[b] = *reinterpret_cast<const u32x4*>(k + off);
+                }
+#pragma unroll
+                for (int b = 0; b < BATCH; ++b) {
+                    const int r = 16 * (p0 + b) + (tid >> 4);
+                    const bool ok = r < Cr;
+                    float qq = 0.f, kk = 0.f;
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        const float q0 = __uint_as_float(qr[b][e] << 16), q1 = __uint_as_float(qr[b][e] & 0xffff0000u);
+                        const float k0 = __uint_as_float(kr[b][e] << 16), k1 = __uint_as_float(kr[b][e] & 0xffff0000u);
+                        qq += q0 * q0;
+                        qq += q1 * q1;
+                        kk += k0 * k0;
+                        kk += k1 * k1;
+                    }
+                    qq = row16_sum(qq);
+                    kk = row16_sum(kk);
+                    if (sub == 0) {
+                        s_rq[r] = ok ? 1.0f / sqrtf(qq + eps) : 0.f;
+                        s_rk[r] = ok ? 1.0f / sqrtf(kk + eps) : 0.f;
+                    }
+                    const u32x4 z = {0u, 0u, 0u, 0u};
+                    *reinterpret_cast<u32x4*>(&s_kq(0, 0, r, sub * EPL)) = ok ? kr[b] : z;
+                    *reinterpret_cast<u32x4*>(&s_kq(1, 0, r, sub * EPL)) = ok ? qr[b] : z;
+                }
+            }
+        }
+#pragma unroll
+        for (int p0 = 0; p0 < (RAW16 ? 0 : NPASS); p0 += BATCH) {
             float qv[BATCH][EPL], kv[BATCH][EPL];
 #pragma unroll
             for (int b = 0; b < BATCH; ++b) {
