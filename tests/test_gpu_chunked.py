@@ -63,6 +63,22 @@ def test_chunked_tails(t, chunk):
     assert_parity(out, st, o_ref, s_ref, f"chunked tail t={t} C={chunk}")
 
 
+@pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
+@pytest.mark.parametrize("t,chunk", [(16, 16), (31, 16), (20, 32), (32, 32)])
+def test_chunked_single_chunk(t, chunk, dtype):
+    """Prompts of one chunk (a full one and a short one at C = 16 and 32): the pipelined
+    scan runs its first and last windows on the same chunk."""
+    shape = Shape(n=1, t=t, h_qk=2, h_v=4, d=128, dtype=dtype)
+    c = gdn_inputs.make_case(shape, seed=450 + t + chunk, device=DEV, s0_std=0.1)
+    out, st = gdn.gdn_prefill_chunked(**c, chunk=chunk)
+    torch.cuda.synchronize()
+    o_ref, s_ref = run_oracle(c)
+    assert_parity(out, st, o_ref, s_ref, f"chunked single chunk t={t} C={chunk} {dtype}")
+    out2, st2 = gdn.gdn_prefill(**c)
+    torch.cuda.synchronize()
+    assert_parity(out2, st2, o_ref, s_ref, f"dispatched t={t} {dtype}")
+
+
 def test_chunked_head_groups():
     """h_v / h_qk = 1 and 4 (the mapping V head h -> QK head h // group)."""
     for h_qk, h_v in ((4, 4), (2, 8)):
