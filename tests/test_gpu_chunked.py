@@ -63,6 +63,19 @@ def test_chunked_tails(t, chunk):
     assert_parity(out, st, o_ref, s_ref, f"chunked tail t={t} C={chunk}")
 
 
+@pytest.mark.parametrize("n,t", [(1, 150), (2, 300), (2, 192)])
+def test_chunked64_odd_chunk_counts(n, t):
+    """The 64-token kernel (d = 128, bf16) with an odd number of chunks greater than one
+    (3, 5 and 3 full ones): its two-window loop ends in a padding window that must leave
+    each sequence's state unchanged."""
+    shape = Shape(n=n, t=t, h_qk=2, h_v=4, d=128)
+    c = gdn_inputs.make_case(shape, seed=460 + t + n, device=DEV, s0_std=0.1)
+    out, st = gdn.gdn_prefill_chunked(**c, chunk=64)
+    torch.cuda.synchronize()
+    o_ref, s_ref = run_oracle(c)
+    assert_parity(out, st, o_ref, s_ref, f"chunked C=64 n={n} t={t}")
+
+
 @pytest.mark.parametrize("dtype", [torch.bfloat16, torch.float32], ids=["bf16", "f32"])
 @pytest.mark.parametrize("t,chunk", [(16, 16), (31, 16), (20, 32), (32, 32)])
 def test_chunked_single_chunk(t, chunk, dtype):
