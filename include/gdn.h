@@ -151,11 +151,11 @@ gdn_status gdn_prefill_scan(const gdn_dims* dims, const void* q, const void* k,
  * The residency ablation of the direct scan ("Keep the recurrent state on-chip": with the
  * state not kept resident, a blockwise scan moves the whole state through device memory
  * over and over; the pages count the bytes per layer for a 2K-token prompt). Same
- * arithmetic as gdn_prefill_scan, and the same bits: q/k are normalised once, then the scan
- * kernel runs once per block of block_t tokens of each sequence, reading the state at the
- * start of the block (state_in for the first block, else state_out) and writing it to
- * state_out at the end, so each block moves 2 x h_v x d_k x d_v x 4 bytes of state per
- * sequence. n x ceil(t / block_t) scan launches on `stream`. Workspace and errors as for
+ * arithmetic as gdn_prefill_scan, and the same bits: the scan kernel runs once per block of
+ * block_t tokens of each sequence (normalising that block's q/k rows on chip), reading the
+ * state at the start of the block (state_in for the first block, else state_out) and
+ * writing it to state_out at the end, so each block moves 2 x h_v x d_k x d_v x 4 bytes of
+ * state per sequence. n x ceil(t / block_t) scan launches on `stream`. Workspace and errors as for
  * gdn_prefill_scan; GDN_ERR_SHAPE for block_t <= 0. For measurement, not for speed.
  */
 gdn_status gdn_prefill_scan_blockwise(const gdn_dims* dims, int64_t block_t, const void* q,
