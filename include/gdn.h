@@ -155,8 +155,9 @@ gdn_status gdn_prefill_scan(const gdn_dims* dims, const void* q, const void* k,
  * block_t tokens of each sequence (normalising that block's q/k rows on chip), reading the
  * state at the start of the block (state_in for the first block, else state_out) and
  * writing it to state_out at the end, so each block moves 2 x h_v x d_k x d_v x 4 bytes of
- * state per sequence. n x ceil(t / block_t) scan launches on `stream`. Workspace and errors as for
- * gdn_prefill_scan; GDN_ERR_SHAPE for block_t <= 0. For measurement, not for speed.
+ * state per sequence. n x ceil(t / block_t) scan launches on `stream`. Workspace and
+ * errors as for gdn_prefill_scan; GDN_ERR_SHAPE for block_t <= 0. For measurement, not for
+ * speed.
  */
 gdn_status gdn_prefill_scan_blockwise(const gdn_dims* dims, int64_t block_t, const void* q,
                                       const void* k, const void* v, const float* g,
