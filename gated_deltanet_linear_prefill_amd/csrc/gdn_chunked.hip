@@ -2311,8 +2311,15 @@ chunk64_scan_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
             const int nq_mine = (2 * HALF - iq + nbq - 1) / nbq;
             const int nv_mine = (NWS + HALF - cb + NCB - 1) / NCB;
             // the second chain wave touches lane 0's line only (its loop issues the same
-            // loads as the first's, see below, but need not repeat its requests)
-            const int li = (l < nq_mine + nv_mine && hh == 0) ? l : 0;
+            // loads as the first's, see below, but need not repeat its requests). The lines
+            // of T', Ptil and the scalars are touched only when the call's workspace exceeds
+            // 64 MiB: a smaller one, which the preparation has just written, is still in the
+            // 256 MB MALL, and touching it only costs vector-memory issue (measured: 4K
+            // tokens, 51 MB of workspace, 1.8 us faster per layer without those touches; 8K,
+            // 102 MB, equal; 16K, 204 MB, 11% slower without).
+            const bool touch_ws = L.total > ((size_t)64 << 20);
+            const bool wsline = l >= nq_mine && cb + NCB * (l - nq_mine) < NWS;
+            const int li = (l < nq_mine + nv_mine && hh == 0 && (touch_ws || !wsline)) ? l : 0;
             const bool isq = li < nq_mine;
             const int lq = iq + nbq * li, rq = lq < HALF ? lq : lq - HALF;
             const uint64_t q0 = pick(lq < HALF, (uint64_t)k, (uint64_t)q) +
