@@ -53,6 +53,8 @@
 // (__expf); its relative error, a few 1e-6 at these arguments, is far below that precision.
 #include <type_traits>
 
+#include <atomic>
+
 #include "gdn_internal.hpp"
 
 namespace gdn {
@@ -322,8 +324,18 @@ template <int D, int C, typename TIn>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ g,
                   const float* __restrict__ beta, char* __restrict__ ws, ChunkWs L, int64_t T,
-                  int h_qk, int h_v, float eps)
+                  int h_qk, int h_v, float eps, int stagger_wgs, int stagger_units)
 {
+    // Staggered start (stagger_units > 0: the whole grid resident at once, several workgroups
+    // per CU). Every workgroup loads its q/k rows first and all would otherwise share the
+    // memory bandwidth equally, so that none could start computing before nearly all rows
+    // had arrived. Group i (workgroups i * stagger_wgs .. (i + 1) * stagger_wgs - 1, one per
+    // CU) waits about the time one group's rows take to stream in, times i, so that earlier
+    // groups compute while later groups' rows arrive.
+    if (stagger_units > 0) {
+        const int grp = (int)(blockIdx.x / (unsigned)stagger_wgs);
+        for (int i = (grp * stagger_units) / 8; i > 0; --i) __builtin_amdgcn_s_sleep(8);
+    }
     constexpr bool F32IN = std::is_same<TIn, float>::value;
     using G = Geo<D, C, F32IN>;
     constexpr int DP = G::DP, CP = G::CP, RT = G::RT, KTD = G::KTD, KTC = G::KTC;
@@ -2595,6 +2607,26 @@ chunk64_scan_kernel(const uint16_t* __restrict__ q, const uint16_t* __restrict__
     }
 }
 
+// Compute units of the current device, looked up once per device (0 if the query fails).
+int device_cu_count()
+{
+    static std::atomic<int> cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) {
+        (void)hipGetLastError();
+        return 0;
+    }
+    int n = cached[dev].load(std::memory_order_relaxed);
+    if (n == 0) {
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) {
+            (void)hipGetLastError();
+            return 0;
+        }
+        cached[dev].store(n, std::memory_order_relaxed);
+    }
+    return n;
+}
+
 template <int D, int C, typename TIn>
 hipError_t launch_chunked_t(const Call& cl, int parts)
 {
@@ -2606,8 +2638,23 @@ hipError_t launch_chunked_t(const Call& cl, int parts)
     const TIn* v = static_cast<const TIn*>(cl.v);
     const int64_t prep_blocks = cl.n * L.nch * cl.h_qk;
     if (parts & kChunkPrep) {
+        // The staggered start of chunk_prep_kernel, measured for 64-token chunks of bf16 rows
+        // of 128 features (four workgroups resident per CU): 1,024 workgroups at 4K tokens,
+        // 25.0 -> 24.0 us with about 1.5-2 us per group (0.5 us per group: no change; 3 us:
+        // slower). Only when the whole grid is resident at once and spans several groups.
+        int stagger_wgs = 1, stagger_units = 0;
+        if constexpr (C == 64 && D == 128 && !F32IN) {
+            const int cus = device_cu_count();
+            if (cus > 0 && prep_blocks > cus && prep_blocks <= 4 * (int64_t)cus) {
+                stagger_wgs = cus;
+                // one group's q/k rows (cus x 2 x C x D x 2 bytes) at about 5 TB/s, in
+                // s_sleep units of 64 clocks at about 2.1 GHz
+                stagger_units = (int)((double)cus * 2 * C * D * sizeof(TIn) / 5.0e12 * 2.1e9 / 64.0);
+            }
+        }
         hipLaunchKernelGGL((chunk_prep_kernel<D, C, TIn>), dim3((unsigned)prep_blocks), dim3(256), 0,
-                           cl.stream, q, k, cl.g, cl.beta, ws, L, cl.t, cl.h_qk, cl.h_v, cl.eps);
+                           cl.stream, q, k, cl.g, cl.beta, ws, L, cl.t, cl.h_qk, cl.h_v, cl.eps,
+                           stagger_wgs, stagger_units);
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
