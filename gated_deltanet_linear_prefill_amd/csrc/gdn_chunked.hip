@@ -320,6 +320,12 @@ __device__ __forceinline__ void tri_frag(int fi, int& rt, int& kt)
 // latency, and the register allocation fits without spills. Phases are separated by barriers
 // that wait for LDS only: nothing in the workgroup reads back the workspace it stores, so a
 // phase never waits for the previous phase's stores to complete.
+// Largest spread of a head's gate prefix sums over one chunk for which the prep kernel forms
+// the pairwise decays as products of two exponentials: each factor then stays within
+// [e^-60, e^60] (times an inverse norm of at most 1 / sqrt(eps)), far from fp32 overflow and
+// underflow, while a chunk of 64 tokens at the workloads' gates spans about 8.
+constexpr float SEP_SPAN = 60.f;
+
 template <int D, int C, typename TIn>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ g,
@@ -368,7 +374,22 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     __shared__ float s_rk[CP], s_rq[CP];
     __shared__ float s_gam[NHP][CP], s_beta[NHP][CP];
     __shared__ float s_sv[G::WITH_H ? NHP : 1][G::WITH_H ? CP : 1];  // s for H (chunks <= 32)
-    __shared__ float s_x[4][16][17];  // per-wave 16x16 scratch
+    __shared__ float s_x[4][16][17];  // per-wave 16x16 scratch (phase 6)
+    __shared__ int s_sep[NHP];        // 1: the head's decays are formed as products (below)
+    // Decay tables of the pass (phases 4 and 5), in the phase-6 scratch. In a tile pair
+    // (row tile R, column tile S <= R) the anchor b = 16 R lies between every column token s
+    // and row token r >= b, so exp(gamma_r - gamma_s) = exp(gamma_r - gamma_b) exp(gamma_b -
+    // gamma_s). Per head slot: rho_k[r] = beta_r r_k,r exp(gamma_r - gamma_b(r)) and
+    // rho_q[r] = r_q,r exp(gamma_r - gamma_b(r)) (CP each), then kappa[R][s] = r_k,s
+    // exp(gamma_16R - gamma_s) for s < 16 R + 16 (packed by R: offset 8 R (R + 1)). An element
+    // of A is then rho_k[r] kappa[R][s] (k_r . k_s) and one of Ptil rho_q[r] kappa[R][s]
+    // (q_r . k_s). Used when the head's gamma spans at most SEP_SPAN over the chunk, so that no
+    // factor overflows or underflows where the product does not.
+    constexpr int DSTR = 2 * CP + 8 * RT * (RT + 1);
+    static_assert(NHP * DSTR + 16 <= 4 * 16 * 17, "decay tables (+16 floats read past the last "
+                  "one, dropped by the selects) fit the phase-6 scratch");
+    static_assert(64 * NWH >= CP, "one thread per token of a head slot");
+    float* const s_dec = &s_x[0][0][0];
     auto s_kq = [&](int which, int part, int r, int f) -> __bf16& {
         return reinterpret_cast<__bf16*>(s_buf)[(((size_t)which * NS + part) * CP + r) * KS + f];
     };
@@ -430,6 +451,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             if (l >= off) x += y;
         }
         const float excl = x - run;
+        bool nonpos = true;
 #pragma unroll
         for (int e = 0; e < E; ++e) {
             const int i = l * E + e;
@@ -437,8 +459,43 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
                 s_gam[pm][i] = gs[e] + excl;
                 s_beta[pm][i] = bv[e];
             }
+            nonpos = nonpos && gv[e] <= 0.f;  // false for NaN
         }
+        // With no positive gate gamma falls from g_0 (lane 0) to the total (lane 63), so that
+        // difference is its spread over the chunk (NaN or infinite for such gates: no product
+        // form then).
+        const bool mono = __ballot(!nonpos) == 0;
+        const float spread = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gs[0] + excl))) -
+                             __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
+        if (l == 0) s_sep[pm] = mono && spread <= SEP_SPAN ? 1 : 0;
         if (g0 + NHP < grp) load_gb(head_of(g0 + NHP));
+    };
+
+    // The decay tables of this head slot's head in the first pass (gamma, beta and the
+    // inverse norms in LDS); every thread of the slot forms rho for one token and kappa for
+    // every R of its residue class.
+    auto build_dec = [&]() {
+        float* d = s_dec + pm * DSTR;
+        if (pt < CP) {
+            const float e = __expf(s_gam[pm][pt] - s_gam[pm][pt & ~15]);
+            d[pt] = s_beta[pm][pt] * s_rk[pt] * e;
+            d[CP + pt] = s_rq[pt] * e;
+        }
+        constexpr int SL = 64 * NWH / CP;
+        const int sv = pt % CP, rg = pt / CP;
+#pragma unroll
+        for (int j = 0; j < (RT + SL - 1) / SL; ++j) {
+            const int R = rg + SL * j;
+            if (R < RT && sv < 16 * R + 16)
+                d[2 * CP + 8 * R * (R + 1) + sv] = s_rk[sv] * __expf(s_gam[pm][16 * R] - s_gam[pm][sv]);
+        }
+    };
+    // Whether every head of the pass takes the product form (wave-uniform).
+    auto sep_pass = [&]() {
+        int all = 1;
+#pragma unroll
+        for (int p = 0; p < NHP; ++p) all &= s_sep[p];
+        return __builtin_amdgcn_readfirstlane(all) != 0;
     };
 
     // The next chunk's key rows for H (see below), loaded now so that they arrive while the
@@ -487,6 +544,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
                     qr[b] = *reinterpret_cast<const u32x4*>(q + off);
                     kr[b] = *reinterpret_cast<const u32x4*>(k + off);
                 }
+                float sq[BATCH], sk[BATCH];
 #pragma unroll
                 for (int b = 0; b < BATCH; ++b) {
                     const int r = 16 * (p0 + b) + (tid >> 4);
@@ -501,15 +559,28 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
                         kk += k0 * k0;
                         kk += k1 * k1;
                     }
-                    qq = row16_sum(qq);
-                    kk = row16_sum(kk);
-                    if (sub == 0) {
-                        s_rq[r] = ok ? 1.0f / sqrtf(qq + eps) : 0.f;
-                        s_rk[r] = ok ? 1.0f / sqrtf(kk + eps) : 0.f;
-                    }
+                    sq[b] = row16_sum(qq);
+                    sk[b] = row16_sum(kk);
                     const u32x4 z = {0u, 0u, 0u, 0u};
                     *reinterpret_cast<u32x4*>(&s_kq(0, 0, r, sub * EPL)) = ok ? kr[b] : z;
                     *reinterpret_cast<u32x4*>(&s_kq(1, 0, r, sub * EPL)) = ok ? qr[b] : z;
+                }
+                // The 16 lanes of a row group hold the same 2 x BATCH sums: lane sub < 2 BATCH
+                // forms inverse norm number sub (q rows first, then k rows), one per lane.
+                static_assert(2 * BATCH <= 16, "one inverse norm per lane of a row group");
+                const int bs = sub % BATCH;
+                float xq = sq[0], xk = sk[0];
+#pragma unroll
+                for (int b = 1; b < BATCH; ++b) {
+                    xq = bs == b ? sq[b] : xq;
+                    xk = bs == b ? sk[b] : xk;
+                }
+                const float rinv = 1.0f / sqrtf((sub < BATCH ? xq : xk) + eps);
+                if (sub < 2 * BATCH) {
+                    const int r = 16 * (p0 + bs) + (tid >> 4);
+                    const float val = r < Cr ? rinv : 0.f;
+                    if (sub < BATCH) s_rq[r] = val;
+                    else s_rk[r] = val;
                 }
             }
         }
@@ -572,6 +643,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     //    accumulator rows are tokens s of K, columns tokens r of Q, so the four values a
     //    lane holds in the two tiles are the eight k slots (permuted token order) of the
     //    B fragment of Ptil^T the scan kernel multiplies U^T with.
+    build_dec();  // first pass; visible after the barrier that ends phase 2
     constexpr int NTL = RT * (RT + 1) / 2;
     constexpr int NTW = (NTL + 3) / 4;  // K K^T tiles per wave
     constexpr int NPG = NS == 1 ? 1 : 3; // split passes of a Gram product
@@ -668,6 +740,9 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
             gate_prefix(g0);
             barrier_lds_only();
         }
+        // the tables are built for the first pass only (in phase 2); later passes, for more
+        // than NHP V heads per QK head, form every decay as one exponential
+        const bool sep = g0 == 0 && sep_pass();
 
         // ---- per-token scalars a = Gamma r_k, s = r_k exp(gamma_C - gamma), o = Gamma r_q
         //      and Gamma_C (padded tokens carry r_k = r_q = 0, so their scalars are zero)
@@ -688,22 +763,46 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
 
         // ---- phase 4: A = strictly lower (beta_r exp(gamma_r - gamma_s) r_k,r r_k,s k_r . k_s)
         //      for every V head of the pass
+        if (sep) {
 #pragma unroll
-        for (int i = 0; i < NTW; ++i) {
-            const int ti = w + 4 * i;
-            if (ti < NTL) {
-                int rt, ct;
-                tri_tile(ti, rt, ct);
+            for (int i = 0; i < NTW; ++i) {
+                const int ti = w + 4 * i;
+                if (ti < NTL) {
+                    int rt, ct;
+                    tri_tile(ti, rt, ct);
 #pragma unroll
-                for (int p = 0; p < NHP; ++p) {
-                    float(*s_ap)[CS] = a_of(p);
+                    for (int p = 0; p < NHP; ++p) {
+                        float(*s_ap)[CS] = a_of(p);
+                        const float* d = s_dec + p * DSTR;
+                        const int s = 16 * ct + lr;
+                        const float kap = d[2 * CP + 8 * rt * (rt + 1) + s];
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int r = 16 * rt + 4 * lg + e, s = 16 * ct + lr;
-                        // formed for every element and selected (above the diagonal the
-                        // decay may overflow; the select drops it)
-                        const float a = s_beta[p][r] * __expf(s_gam[p][r] - s_gam[p][s]) * s_rk[r] * s_rk[s] * gk[i][e];
-                        s_ap[r][s] = s < r ? a : 0.f;
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 16 * rt + 4 * lg + e;
+                            const float a = d[r] * kap * gk[i][e];
+                            s_ap[r][s] = s < r ? a : 0.f;
+                        }
+                    }
+                }
+            }
+        } else {
+#pragma unroll
+            for (int i = 0; i < NTW; ++i) {
+                const int ti = w + 4 * i;
+                if (ti < NTL) {
+                    int rt, ct;
+                    tri_tile(ti, rt, ct);
+#pragma unroll
+                    for (int p = 0; p < NHP; ++p) {
+                        float(*s_ap)[CS] = a_of(p);
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int r = 16 * rt + 4 * lg + e, s = 16 * ct + lr;
+                            // formed for every element and selected (above the diagonal the
+                            // decay may overflow; the select drops it)
+                            const float a = s_beta[p][r] * __expf(s_gam[p][r] - s_gam[p][s]) * s_rk[r] * s_rk[s] * gk[i][e];
+                            s_ap[r][s] = s < r ? a : 0.f;
+                        }
                     }
                 }
             }
@@ -740,14 +839,29 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
                 const int64_t vhp = (seq * nch + c) * h_v + head_at(g0, p);
                 char* pt_base = ws + L.pt + (size_t)vhp * G::TRI_BYTES;
                 float val[8];
+                if (sep) {
+                    const float* d = s_dec + p * DSTR;
+                    const float rho = d[CP + r];
 #pragma unroll
-                for (int h = 0; h < 2; ++h)
+                    for (int h = 0; h < 2; ++h)
 #pragma unroll
-                    for (int e = 0; e < 4; ++e) {
-                        const int s = 32 * kt + 16 * h + 4 * lg + e;
-                        const float pv = __expf(s_gam[p][r] - s_gam[p][s]) * s_rq[r] * s_rk[s] * gp[i][h][e];
-                        val[4 * h + e] = s <= r ? pv : 0.f;
-                    }
+                        for (int e = 0; e < 4; ++e) {
+                            // past the row tile (zero Gram tiles) kappa is read from the next
+                            // R's entries or the slack after the tables; the select drops it
+                            const int s = 32 * kt + 16 * h + 4 * lg + e;
+                            const float pv = rho * d[2 * CP + 8 * rt * (rt + 1) + s] * gp[i][h][e];
+                            val[4 * h + e] = s <= r ? pv : 0.f;
+                        }
+                } else {
+#pragma unroll
+                    for (int h = 0; h < 2; ++h)
+#pragma unroll
+                        for (int e = 0; e < 4; ++e) {
+                            const int s = 32 * kt + 16 * h + 4 * lg + e;
+                            const float pv = __expf(s_gam[p][r] - s_gam[p][s]) * s_rq[r] * s_rk[s] * gp[i][h][e];
+                            val[4 * h + e] = s <= r ? pv : 0.f;
+                        }
+                }
                 uint32_t hi[4], lo[4];
 #pragma unroll
                 for (int q2 = 0; q2 < 4; ++q2) split2(val[2 * q2], val[2 * q2 + 1], &hi[q2], &lo[q2]);
