@@ -94,3 +94,27 @@ def test_extreme_input_scales(method):
     assert torch.isfinite(out).all() and torch.isfinite(st).all()
     o_ref, s_ref = ref(c)
     assert_parity(out, st, o_ref, s_ref, f"{method} input scales")
+
+
+@pytest.mark.parametrize("kind", ["spread_59", "spread_61", "some_positive"])
+@pytest.mark.parametrize("chunk", [16, 32, 64, 128])
+def test_decay_product_threshold(kind, chunk):
+    """The chunked form takes the pairwise decays of a chunk as products of two exponentials
+    when no gate is positive and the gate sum over the chunk's tokens after the first spans at
+    most 60, and one exponential per element otherwise. Gates just inside (59) and just
+    outside (61) that bound, and gates of both signs, against the oracle, over two full
+    chunks and a ragged one."""
+    shape = Shape(n=1, t=2 * chunk + 5, h_qk=2, h_v=4, d=128)
+    c = gdn_inputs.make_case(shape, seed=1600 + chunk + len(kind), device=DEV, s0_std=0.05)
+    gen = torch.Generator(device="cpu").manual_seed(1610 + chunk)
+    if kind == "some_positive":
+        g = torch.rand(c["g"].shape, generator=gen, dtype=torch.float64) * 0.25 - 0.2
+    else:
+        span = 59.0 if kind == "spread_59" else 61.0
+        g = torch.full(c["g"].shape, -span / (chunk - 1), dtype=torch.float64)
+    c["g"] = g.to(torch.float32).to(DEV)
+    out, st = gdn.gdn_prefill_chunked(**c, chunk=chunk)
+    torch.cuda.synchronize()
+    assert torch.isfinite(out).all() and torch.isfinite(st).all()
+    o_ref, s_ref = ref(c)
+    assert_parity(out, st, o_ref, s_ref, f"C={chunk} {kind}")
