@@ -329,7 +329,7 @@ __device__ __forceinline__ void tri_frag(int fi, int& rt, int& kt)
 // underflow, while a chunk of 64 tokens at the workloads' gates spans about 8.
 constexpr float SEP_SPAN = 60.f;
 
-template <int D, int C, typename TIn>
+template <int D, int C, typename TIn, bool PH = false>
 __global__ void __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(4)))
 chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const float* __restrict__ g,
                   const float* __restrict__ beta, char* __restrict__ ws, ChunkWs L, int64_t T,
@@ -356,10 +356,14 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     // 64 tokens two heads side by side (the diagonal solve needs one wave, the other writes
     // Ptil meanwhile), 128-token chunks one head with all four waves. For 64-token chunks T
     // is formed in place of A (INPLACE), so that both heads' matrices fit the LDS that four
-    // resident workgroups per CU leave.
-    constexpr int NWH = C <= 64 ? 2 : 4;           // waves per V head
+    // resident workgroups per CU leave. PH (per head): one workgroup per (sequence, chunk, V
+    // head) with all four waves on its head, each forming the QK head's Gram tiles again;
+    // for grids that leave CUs idle, where a workgroup's latency rather than the chip's
+    // throughput sets the time.
+    static_assert(!PH || C == 64, "the per-head form is built for 64-token chunks");
+    constexpr int NWH = PH || C > 64 ? 4 : 2;      // waves per V head
     constexpr int NHP = 4 / NWH;                   // V heads per pass
-    constexpr bool INPLACE = C == 64;
+    constexpr bool INPLACE = C == 64 && !PH;
     constexpr size_t KQ_LDS = (size_t)2 * NS * CP * KS * 2;
     constexpr size_t AT_LDS = (size_t)NHP * (INPLACE ? 1 : 2) * CP * CS * 4;
     constexpr size_t U_LDS = KQ_LDS > AT_LDS ? KQ_LDS : AT_LDS;
@@ -398,9 +402,11 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     };
 
     const int64_t nch = L.nch;
-    const int hq = (int)(blockIdx.x % h_qk);
-    const int64_t sc_idx = blockIdx.x / h_qk;
+    const int unit = PH ? h_v : h_qk;  // workgroups per (sequence, chunk)
+    const int hx = (int)(blockIdx.x % unit);
+    const int64_t sc_idx = blockIdx.x / unit;
     const int64_t c = sc_idx % nch, seq = sc_idx / nch;
+    const int hq = PH ? hx / (h_v / h_qk) : hx;
     const int64_t c0 = c * C;
     const int Cr = (int)((T - c0) < C ? (T - c0) : C);
     const int tid = threadIdx.x, l = tid & 63, lr = l & 15, lg = l >> 4;
@@ -409,12 +415,13 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     const int pt = tid - 64 * NWH * pm;    // thread index within the head slot
     const int prk = wl >= NBW ? pm * (NWH - NBW) + wl - NBW : NNS + pm * NBW + wl;
     const int grp = h_v / h_qk;
+    const int npass = PH ? 1 : grp;  // V heads this workgroup takes, NHP per pass
     const int64_t tok0 = seq * T + c0;  // flattened token index of the chunk's first token
     float(*s_a)[CS] = reinterpret_cast<float(*)[CS]>(s_buf + (size_t)pm * (INPLACE ? 1 : 2) * CP * CS * 4);
     float(*s_t)[CS] = INPLACE ? s_a : reinterpret_cast<float(*)[CS]>(s_buf + ((size_t)pm * 2 + 1) * CP * CS * 4);
     // V head of slot p in the pass starting at head g0 (a slot past the QK head's V heads
     // repeats the pass's first head: the same values are computed and written twice)
-    auto head_at = [&](int g0, int p) { return hq * grp + (g0 + p < grp ? g0 + p : g0); };
+    auto head_at = [&](int g0, int p) { return PH ? hx : hq * grp + (g0 + p < grp ? g0 + p : g0); };
     auto head_of = [&](int g0) { return head_at(g0, pm); };
     auto a_of = [&](int p) {
         return reinterpret_cast<float(*)[CS]>(s_buf + (size_t)p * (INPLACE ? 1 : 2) * CP * CS * 4);
@@ -471,7 +478,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
         const float spread = __int_as_float(__builtin_amdgcn_readfirstlane(__float_as_int(gs[0] + excl))) -
                              __int_as_float(__builtin_amdgcn_readlane(__float_as_int(x), 63));
         if (l == 0) s_sep[pm] = mono && spread <= SEP_SPAN ? 1 : 0;
-        if (g0 + NHP < grp) load_gb(head_of(g0 + NHP));
+        if (g0 + NHP < npass) load_gb(head_of(g0 + NHP));
     };
 
     // The decay tables of this head slot's head in the first pass (gamma, beta and the
@@ -734,7 +741,7 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     }
     barrier_lds_only();  // the K / Q buffer becomes A / T below
 
-    for (int g0 = 0; g0 < grp; g0 += NHP) {
+    for (int g0 = 0; g0 < npass; g0 += NHP) {
         const int hv = head_of(g0);
         const int64_t vh = (seq * nch + c) * h_v + hv;
 
@@ -2760,18 +2767,34 @@ hipError_t launch_chunked_t(const Call& cl, int parts)
         // 25.0 -> 24.0 us with about 1.5-2 us per group (0.5 us per group: no change; 3 us:
         // slower). Only when the whole grid is resident at once and spans several groups.
         int stagger_wgs = 1, stagger_units = 0;
+        bool per_head = false;
         if constexpr (C == 64 && D == 128 && !F32IN) {
             const int cus = device_cu_count();
-            if (cus > 0 && prep_blocks > cus && prep_blocks <= 4 * (int64_t)cus) {
+            // A workgroup per V head (all four waves on it) where that duplicates nothing (one
+            // V head per QK head) or where the grid would leave CUs idle, so that one
+            // workgroup's latency rather than the chip's throughput sets the time.
+            per_head = cus > 0 && (cl.h_v == cl.h_qk || prep_blocks <= cus);
+            // (the stagger, measured for four resident workgroups per CU, only on that grid)
+            const bool same_grid = !per_head || cl.h_v == cl.h_qk;
+            if (same_grid && cus > 0 && prep_blocks > cus && prep_blocks <= 4 * (int64_t)cus) {
                 stagger_wgs = cus;
                 // one group's q/k rows (cus x 2 x C x D x 2 bytes) at about 5 TB/s, in
                 // s_sleep units of 64 clocks at about 2.1 GHz
                 stagger_units = (int)((double)cus * 2 * C * D * sizeof(TIn) / 5.0e12 * 2.1e9 / 64.0);
             }
         }
-        hipLaunchKernelGGL((chunk_prep_kernel<D, C, TIn>), dim3((unsigned)prep_blocks), dim3(256), 0,
-                           cl.stream, q, k, cl.g, cl.beta, ws, L, cl.t, cl.h_qk, cl.h_v, cl.eps,
-                           stagger_wgs, stagger_units);
+        if constexpr (C == 64 && D == 128 && !F32IN) {
+            if (per_head) {
+                hipLaunchKernelGGL((chunk_prep_kernel<D, C, TIn, true>), dim3((unsigned)(cl.n * L.nch * cl.h_v)),
+                                   dim3(256), 0, cl.stream, q, k, cl.g, cl.beta, ws, L, cl.t, cl.h_qk,
+                                   cl.h_v, cl.eps, stagger_wgs, stagger_units);
+            }
+        }
+        if (!per_head) {
+            hipLaunchKernelGGL((chunk_prep_kernel<D, C, TIn>), dim3((unsigned)prep_blocks), dim3(256), 0,
+                               cl.stream, q, k, cl.g, cl.beta, ws, L, cl.t, cl.h_qk, cl.h_v, cl.eps,
+                               stagger_wgs, stagger_units);
+        }
         hipError_t e = hipGetLastError();
         if (e != hipSuccess) return e;
     }
