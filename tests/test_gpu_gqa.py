@@ -50,3 +50,15 @@ def test_scan_decode_blockwise_gqa(h_qk, h_v):
     o1, s1 = gdn.gdn_decode_step(**d1)
     torch.cuda.synchronize()
     assert_parity(o1, s1, o1_ref, s1_ref, f"decode h_qk={h_qk} h_v={h_v}")
+
+
+def test_chunked64_one_v_head_per_qk_head_staggered():
+    """One V head per QK head at 4096 tokens (16 heads, 1,024 (chunk, head) items): the
+    64-token preparation then runs one workgroup per V head with the staggered start; every
+    head's outputs and state against the oracle."""
+    c = gdn_inputs.make_case(Shape(n=1, t=4096, h_qk=16, h_v=16, d=128), seed=1150, device=DEV,
+                             s0_std=0.02)
+    out, st = gdn.gdn_prefill_chunked(**c, chunk=64)
+    torch.cuda.synchronize()
+    o_ref, s_ref = ref(c)
+    assert_parity(out, st, o_ref, s_ref, "chunked C=64 h_qk=h_v=16 t=4096")
