@@ -390,8 +390,9 @@ chunk_prep_kernel(const TIn* __restrict__ q, const TIn* __restrict__ k, const fl
     // rho_q[r] = r_q,r exp(gamma_r - gamma_b(r)) (CP each), then kappa[R][s] = r_k,s
     // exp(gamma_16R - gamma_s) for s < 16 R + 16 (packed by R: offset 8 R (R + 1)). An element
     // of A is then rho_k[r] kappa[R][s] (k_r . k_s) and one of Ptil rho_q[r] kappa[R][s]
-    // (q_r . k_s). Used when the head's gamma spans at most SEP_SPAN over the chunk, so that no
-    // factor overflows or underflows where the product does not.
+    // (q_r . k_s). Used in the first pass when no gate of its heads is positive and each
+    // head's gamma spans at most SEP_SPAN over the chunk, so that no factor overflows or
+    // underflows where the product does not.
     constexpr int DSTR = 2 * CP + 8 * RT * (RT + 1);
     static_assert(NHP * DSTR + 16 <= 4 * 16 * 17, "decay tables (+16 floats read past the last "
                   "one, dropped by the selects) fit the phase-6 scratch");
