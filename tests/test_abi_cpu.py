@@ -235,6 +235,17 @@ def test_prefill_choose(lib):
     for t in (1, 7, 64, 256, 4096, 131072):
         c = gdn.gdn_prefill_choose(t)
         assert c in (0, 16, 32, 64, 128)
+    # The pick follows the measured table (the last entry whose min_t <= t), at and around
+    # every boundary the table lists.
+    inc = open(os.path.join(ROOT, "gated_deltanet_linear_prefill_amd", "csrc", "gdn_crossover.inc")).read()
+    table = [(int(a), int(b)) for a, b in re.findall(r"\{(\d+), (\d+)\}", inc)]
+    assert table and table[0][0] == 0 and [m for m, _ in table] == sorted(m for m, _ in table)
+
+    def pick(t):
+        return [ch for m, ch in table if m <= t][-1]
+
+    for t in sorted({1, 2, 131072} | {m + dt for m, _ in table for dt in (-1, 0, 1) if m + dt >= 1}):
+        assert gdn.gdn_prefill_choose(t) == pick(t), t
     res = ctypes.c_int32()
     assert lib.gdn_prefill_choose(None, ctypes.byref(res)) == NULL
     b = Bufs()
